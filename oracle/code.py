@@ -1,0 +1,73 @@
+"""The computed code: 16-bit trellis state -> fp16 weight (test infrastructure).
+
+Follows the three-instruction code of [TQ] Part nine (and its self-check
+answer seven): (1) one step of a 32-bit linear congruential generator, a
+single multiply-add of the state; (2) treat the 32 bits as two 16-bit halves,
+keep each half's sign bit and low bits with a mask and XOR in a constant that
+pins the exponent, giving two half-precision values with random signs and
+bounded magnitude; (3) add the two halves with one half-precision add.
+Step (2) is the mantissa-splice trick of [TQ] Part three.
+
+The pages print no constants for this code. Reading (listed in the design doc):
+the multiplier is the blog's 0x9E3779B9 ([DD] Section 3 code) cut to its top
+24 bits, 0x9E3779, so the multiply-add is one full-rate instruction on the
+target, as [TQ] Part nine requires of step (1); the addend is the blog's
+0x7F4A7C15; the mask 0x8FFF8FFF keeps each half's sign, the two low exponent
+bits and the 10 fraction bits; the XOR constant 0x30003000 forces exponent
+field 0b011xx, so each half lies in +-[1/8, 2). The sum is rounded to
+binary16 with ties to even.
+
+Pins (tests/test_oracle_code.py): hand-derived values for chosen states
+(tests/golden/code_hand_values.txt); NumPy's independent float16 rounding on
+all 65,536 states; structural invariants the pages state (bounded halves,
+random balanced signs, near-Gaussian sum); no NaN / infinity / subnormal.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import fp16
+
+MUL = 0x009E3779          # LCG multiplier (24 bits)
+ADD = 0x7F4A7C15          # LCG addend
+MASK = 0x8FFF8FFF         # keep sign + low 2 exponent bits + 10 fraction bits of each half
+XOR = 0x30003000          # pins each half's exponent field to 0b011xx
+
+_M32 = (1 << 32) - 1
+
+
+def lcg(states) -> np.ndarray:
+    """Step (1): h = (MUL * S + ADD) mod 2^32, exact in int64 (product < 2^40)."""
+    s = np.asarray(states, dtype=np.int64)
+    return (s * MUL + ADD) & _M32
+
+
+def mask_xor(h) -> np.ndarray:
+    """Step (2): u = (h AND MASK) XOR XOR."""
+    return (np.asarray(h, dtype=np.int64) & MASK) ^ XOR
+
+
+def halves(u):
+    """Low and high 16-bit halves of u as binary16 bit patterns."""
+    u = np.asarray(u, dtype=np.int64)
+    return (u & 0xFFFF).astype(np.uint16), ((u >> 16) & 0xFFFF).astype(np.uint16)
+
+
+def weight_bits(states) -> np.ndarray:
+    """Step (3): fp16 bits of RNE(value(lo) + value(hi)).
+
+    The exact sum is formed in float64 (both halves are multiples of 2^-13
+    below 2 in magnitude, so the float64 sum is exact) and then rounded once.
+    """
+    lo, hi = halves(mask_xor(lcg(states)))
+    return fp16.round_rne(fp16.value(lo) + fp16.value(hi))
+
+
+def weight_values(states) -> np.ndarray:
+    """Decoded weights as exact float64 values."""
+    return fp16.value(weight_bits(states))
+
+
+def table() -> np.ndarray:
+    """The whole code: fp16 bits for all 65,536 states."""
+    return weight_bits(np.arange(1 << 16))

@@ -1,0 +1,112 @@
+"""The trellis-coded matrix-vector product, in float64 (test infrastructure).
+
+What the path computes ([DD] Section 2 equations; [TQ] Parts eight, nine,
+eleven; [FG] "out_scales always"):
+
+    W^[o, i] = code(S_t) of tile (o // 16, i // 16), t = 16 (o % 16) + (i % 16)
+    x~ = blockdiag(H_128) diag(s_in) x
+    y~ = diag(g) W^ x~                          (g: per-output fp16 scale)
+    y  = diag(s_out) blockdiag(H_128) y~
+
+Reading (listed in the design doc): the per-output scale g acts in the rotated
+domain, on y~ before the output transform.
+
+Two routes are provided and pinned against each other: the factored route
+(transform x, multiply, transform back) and the dense route, which forms
+W_eff = diag(s_out) H diag(g) W^ H diag(s_in) and multiplies once. The
+batched and grouped forms run the single-vector routine row by row and expert
+by expert. Further pins: the all-zero stream has a closed-form output, a
+naive triple loop agrees on a small layer, unit impulses read out columns.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import code, fp16, hadamard, trellis
+
+
+def decode_layer(layer, tile_rows=None) -> np.ndarray:
+    """fp16 bit patterns of the decoded weights, [m, n] (or only the listed tile rows)."""
+    states = trellis.layer_states(layer.codes, layer.m, layer.n, layer.k_bits, tile_rows)
+    return code.weight_bits(trellis.states_to_matrix(states)).astype(np.uint16)
+
+
+def weight_matrix(layer, tile_rows=None) -> np.ndarray:
+    """Decoded weights W^ as exact float64 values."""
+    return fp16.value(decode_layer(layer, tile_rows))
+
+
+def scales(layer) -> np.ndarray:
+    return fp16.value(layer.scales)
+
+
+def gemv_with_weights(layer, W: np.ndarray, x_bits: np.ndarray) -> np.ndarray:
+    """Factored route for one activation vector, given the decoded weights."""
+    x = fp16.value(x_bits)
+    xt = hadamard.rht_forward(x, layer.sign_in)
+    yt = scales(layer) * (W @ xt)
+    return hadamard.rht_inverse(yt, layer.sign_out)
+
+
+def gemv(layer, x_bits: np.ndarray) -> np.ndarray:
+    """y = W x for one fp16 activation vector x (given as bit patterns), float64 [m]."""
+    return gemv_with_weights(layer, weight_matrix(layer), x_bits)
+
+
+def effective_matrix(layer, W: np.ndarray = None) -> np.ndarray:
+    """Dense route: W_eff = diag(s_out) blockdiag(H) diag(g) W^ blockdiag(H) diag(s_in)."""
+    if W is None:
+        W = weight_matrix(layer)
+    Hm = hadamard.blockdiag_matrix(layer.m)
+    Hn = hadamard.blockdiag_matrix(layer.n)
+    s_out = hadamard.signs(layer.sign_out, layer.m)
+    s_in = hadamard.signs(layer.sign_in, layer.n)
+    return (s_out[:, None] * Hm) @ (scales(layer)[:, None] * W) @ (Hn * s_in[None, :])
+
+
+def gemv_dense(layer, x_bits: np.ndarray) -> np.ndarray:
+    return effective_matrix(layer) @ fp16.value(x_bits)
+
+
+def gemv_rows(layer, x_bits: np.ndarray, rows) -> np.ndarray:
+    """y at the listed output indices only, decoding just the 128-row blocks they fall in."""
+    rows = np.asarray(rows)
+    x = fp16.value(x_bits)
+    xt = hadamard.rht_forward(x, layer.sign_in)
+    g = scales(layer)
+    out = np.empty(len(rows))
+    for blk in np.unique(rows // hadamard.BLOCK):
+        tr = np.arange(blk * 8, blk * 8 + 8)                      # 8 tile rows = 128 outputs
+        W = weight_matrix(layer, tr)
+        o = slice(blk * hadamard.BLOCK, (blk + 1) * hadamard.BLOCK)
+        yt = g[o] * (W @ xt)
+        s = hadamard.signs(layer.sign_out, layer.m)[o]
+        yb = s * hadamard.apply_blocks(yt)
+        sel = rows // hadamard.BLOCK == blk
+        out[sel] = yb[rows[sel] % hadamard.BLOCK]
+    return out
+
+
+def gemm(layer, X_bits: np.ndarray, W: np.ndarray = None) -> np.ndarray:
+    """Batched form, row by row with the single-vector routine. X [M, n] -> Y [M, m]."""
+    if W is None:
+        W = weight_matrix(layer)
+    return np.stack([gemv_with_weights(layer, W, X_bits[i]) for i in range(X_bits.shape[0])])
+
+
+def gemm_rows(layer, X_bits: np.ndarray, rows) -> np.ndarray:
+    """Batched form at sampled output indices. X [M, n] -> [M, len(rows)]."""
+    return np.stack([gemv_rows(layer, X_bits[i], rows) for i in range(X_bits.shape[0])])
+
+
+def grouped(layers, sel, X_bits: np.ndarray, shared_x: bool) -> list:
+    """Grouped form: for each selected layer index, one GEMV (expert by expert).
+
+    shared_x: every selected layer reads the same vector X_bits [n]; otherwise
+    X_bits[e] is the input of the e-th selection.
+    """
+    out = []
+    for e, li in enumerate(sel):
+        x = X_bits if shared_x else X_bits[e]
+        out.append(gemv(layers[int(li)], x))
+    return out

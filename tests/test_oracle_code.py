@@ -1,0 +1,82 @@
+"""Pins for the oracle's computed code and its binary16 helpers (no GPU)."""
+from fractions import Fraction
+
+import numpy as np
+
+from conftest import golden_rows
+from oracle import code, fp16
+
+
+def test_hand_values():
+    """Every intermediate of the three-instruction code against hand-derived values."""
+    for state, h, u, lo, hi, num, den, w in golden_rows("code_hand_values.txt"):
+        s = np.array([int(state, 16)])
+        assert int(code.lcg(s)[0]) == int(h, 16)
+        assert int(code.mask_xor(code.lcg(s))[0]) == int(u, 16)
+        l, hh = code.halves(code.mask_xor(code.lcg(s)))
+        assert int(l[0]) == int(lo, 16) and int(hh[0]) == int(hi, 16)
+        total = fp16.value(l) + fp16.value(hh)
+        assert Fraction(float(total[0])) == Fraction(int(num), int(den))
+        assert int(code.weight_bits(s)[0]) == int(w, 16)
+
+
+def test_mask_and_xor_are_disjoint():
+    """XOR into masked-off bits equals OR: the pages' mask-then-XOR is one bit-insert."""
+    assert code.MASK & code.XOR == 0
+    assert code.MUL < 1 << 24
+
+
+def test_table_rounding_matches_numpy_cast():
+    """The oracle's own round-to-nearest-even against NumPy's float64->float16 cast, all states."""
+    lo, hi = code.halves(code.mask_xor(code.lcg(np.arange(1 << 16))))
+    exact = fp16.value(lo) + fp16.value(hi)
+    assert (fp16.round_rne(exact) == exact.astype(np.float16).view(np.uint16)).all()
+    assert (code.table() == exact.astype(np.float16).view(np.uint16)).all()
+
+
+def test_fp16_value_matches_numpy_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ours = fp16.value(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    assert (ours[fin] == ref[fin]).all()
+    assert (np.isnan(ours) == np.isnan(ref)).all()
+
+
+def test_round_rne_edge_cases():
+    cases = [(0.0, 0x0000), (-0.0, 0x8000), (1.0, 0x3C00), (65504.0, 0x7BFF), (65520.0, 0x7C00),
+             (65519.99, 0x7BFF), (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000), (3 * 2.0 ** -25, 0x0002),
+             (2.0 ** -14, 0x0400), (1.0 + 2.0 ** -11, 0x3C00), (1.0 + 3 * 2.0 ** -11, 0x3C02),
+             (-2.8427734375, 0xC1B0)]
+    for v, b in cases:
+        assert int(fp16.round_rne(np.array([v]))[0]) == b, v
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(100000) * rng.choice([1e-6, 1e-3, 1, 1e3], 100000)
+    assert (fp16.round_rne(v) == v.astype(np.float16).view(np.uint16)).all()
+
+
+def test_halves_are_bounded_signed_and_exponent_pinned():
+    """Each half keeps its sign, has exponent field 0b011xx (|half| in [1/8, 2)); no NaN/Inf/subnormal."""
+    u = code.mask_xor(code.lcg(np.arange(1 << 16)))
+    for half in code.halves(u):
+        e = (half.astype(np.int64) >> 10) & 0x1F
+        assert set(np.unique(e)) <= {12, 13, 14, 15}
+        v = np.abs(fp16.value(half))
+        assert v.min() >= 0.125 and v.max() < 2.0
+    lo, hi = code.halves(u)
+    # the multiplier is odd, so S -> low 16 bits of h is a bijection: the low half's sign is exactly balanced
+    assert ((lo >> 15) == 1).sum() == 1 << 15
+    assert abs(((hi >> 15) == 1).mean() - 0.5) < 0.01
+
+
+def test_sum_is_near_gaussian_and_finite():
+    """The sum of the two halves is close to a Gaussian (lecture, Part nine)."""
+    w = fp16.value(code.table())
+    assert np.isfinite(w).all()
+    e = (code.table().astype(np.int64) >> 10) & 0x1F
+    assert not ((e == 0) & ((code.table() & 0x3FF) != 0)).any()    # no subnormals
+    assert abs(w.mean()) < 0.01
+    assert 1.1 < w.std() < 1.4
+    kurt = ((w - w.mean()) ** 4).mean() / w.var() ** 2
+    assert 2.5 < kurt < 3.5
+    assert np.abs(w).max() < 4.0
