@@ -1,0 +1,184 @@
+/*
+ * trellis_gemv.h -- C ABI of the MI355X (gfx950) trellis-coded GEMV library.
+ *
+ * A linear layer y = W x is stored the QTIP / EXL3 way:
+ *   - W is rotated on both sides by randomized 128-point Hadamard blocks
+ *     ("ExLlamaV3 & EXL3 Deep Dive", Section 2, the two incoherence
+ *     equations; "Trellis Quantization" lecture, Part eleven: EXL3 rotates
+ *     blocks of 128 along each axis);
+ *   - the rotated matrix is cut into 16x16 tiles, each one tail-biting
+ *     bitshift-trellis sequence of 256 weights at K bits per weight, a 16-bit
+ *     state window sliding K bits per weight (lecture, Part eight; Deep Dive,
+ *     Section 3, transition equation);
+ *   - each weight is rebuilt from its state by a computed code: a 32-bit
+ *     multiply-add, a mask/XOR to two fp16 halves, their fp16 sum (lecture,
+ *     Part nine, three-instruction code);
+ *   - a per-output fp16 scale ("out_scales", LLM Cal EXL3 field guide).
+ *
+ * At run time the library computes
+ *     x~ = blockdiag(H) diag(s_in) x,   y~ = diag(g) W^ x~,   y = diag(s_out) blockdiag(H) y~
+ * with H the normalised 128x128 Sylvester-Hadamard matrix, entirely in HIP
+ * kernels on the caller's stream.
+ *
+ * Storage format (code_id 0):
+ *   codes   : uint32, (m/16)*(n/16) tiles in tile-row-major order (tile (R,C) is
+ *             tile R*(n/16)+C), 8*K words per tile. Stream bit p of a tile is bit
+ *             31-(p%32) of word p/32. Weight (16R+r, 16C+c) is sequence step
+ *             t = 16r+c; its state is the 16 stream bits starting at bit K*t,
+ *             taken cyclically (tail-biting), first bit most significant.
+ *   code    : h = (0x9E3779*S + 0x7F4A7C15) mod 2^32; u = (h & 0x8FFF8FFF) ^ 0x30003000;
+ *             w = fp16_rne(half(u[15:0]) + half(u[31:16])).
+ *   scales  : m fp16 bit patterns (g).
+ *   sign_in : ceil(n/32) uint32 words; bit i%32 of word i/32 set means s_in[i] = -1.
+ *   sign_out: ceil(m/32) uint32 words, same convention.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* or documented "device" are device pointers (hipMalloc
+ *     or any allocator of device memory); the tg_layer struct itself is read on
+ *     the host. The caller owns every buffer; the library never allocates,
+ *     frees, or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; the library never synchronises.
+ *   - Every argument is validated on the host before anything is enqueued; on
+ *     error a negative tg_status is returned and nothing is enqueued. A failed
+ *     launch returns TG_ERR_LAUNCH. No exception crosses the ABI.
+ *   - Outputs must not alias inputs or the workspace.
+ *   - Results are bitwise deterministic for identical inputs and launch
+ *     configuration.
+ *   - Calls that share a workspace must not run concurrently.
+ */
+#ifndef TRELLIS_GEMV_H
+#define TRELLIS_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_ABI_VERSION 1
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_ERR_NULL = -1,       /* a required pointer is NULL                               */
+  TG_ERR_SHAPE = -2,      /* m, n not positive multiples of 128, or M / rows out of range */
+  TG_ERR_KBITS = -3,      /* k_bits outside 1..8                                      */
+  TG_ERR_ALIGN = -4,      /* a pointer is not aligned as documented                   */
+  TG_ERR_WORKSPACE = -5,  /* workspace missing or smaller than tg_workspace_size()     */
+  TG_ERR_CODE_ID = -6,    /* unsupported code_id                                      */
+  TG_ERR_LAUNCH = -7,     /* the HIP runtime rejected a kernel launch                 */
+  TG_ERR_ARG = -8         /* any other invalid argument (stride, flags, index range)   */
+} tg_status;
+
+/* Layer flags. */
+#define TG_FLAG_ROUND_WEIGHTS 1  /* GEMV paths round each weight to fp16 before the product
+                                    (the default adds the two fp16 halves inside the fp32
+                                    product, which is exact up to fp32 rounding). */
+
+/* One trellis-coded linear layer: out_features m, in_features n. Read on the host. */
+typedef struct tg_layer {
+  int32_t m;                 /* out_features, multiple of 128                              */
+  int32_t n;                 /* in_features, multiple of 128                               */
+  int32_t k_bits;            /* bits per weight K, 1..8 (lecture, Part eleven)              */
+  int32_t code_id;           /* 0 = the three-instruction code above                        */
+  int32_t flags;             /* TG_FLAG_*                                                  */
+  int32_t reserved;          /* must be 0                                                  */
+  const uint32_t *codes;     /* device, (m/16)*(n/16)*8*K words, 16-byte aligned            */
+  const uint16_t *scales;    /* device, m fp16 patterns, 2-byte aligned                     */
+  const uint32_t *sign_in;   /* device, ceil(n/32) words                                   */
+  const uint32_t *sign_out;  /* device, ceil(m/32) words                                   */
+} tg_layer;
+
+/* ABI version of the loaded library (TG_ABI_VERSION it was built with). */
+int32_t tg_abi_version(void);
+
+/* Human-readable name of a status code. Never NULL. */
+const char *tg_status_str(int32_t status);
+
+/*
+ * Workspace bytes needed by trellis_gemv (M == 1) or trellis_gemm_small
+ * (1 <= M <= 64) for this layer, or 0 if the layer / M is invalid.
+ * The workspace holds split-K partial sums and per-output-block arrival
+ * counters. It must be zero-filled before its first use; every completed call
+ * leaves it zero-filled again, so it can be reused by later calls on the same
+ * stream. 256-byte alignment is required.
+ */
+size_t tg_workspace_size(const tg_layer *layer, int32_t M);
+
+/*
+ * Batch-1 trellis-coded GEMV: y = W x (the hot path; lecture, Parts eight,
+ * nine and eleven; Deep Dive, Section 2).
+ *   x  : device, n fp16 patterns.
+ *   y  : device, m fp32 outputs, 4-byte aligned.
+ *   ws : device workspace of ws_bytes >= tg_workspace_size(layer, 1).
+ */
+int32_t trellis_gemv(const tg_layer *layer, const uint16_t *x, float *y,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Small-batch trellis-coded GEMM on the matrix cores: Y[r] = W X[r] for
+ * r < M, 1 <= M <= 64. Each decoded 16x16 tile feeds an fp32-accumulating
+ * MFMA (lecture, Part eight: the 16x16 tile matches the matrix-multiply tile;
+ * Part eleven: decoding happens in registers feeding the matrix units).
+ *   X   : device, M rows of n fp16 patterns, row stride ldx >= n elements.
+ *   Y   : device, M rows of m fp32, row stride ldy >= m elements.
+ *   ws  : device workspace of ws_bytes >= tg_workspace_size(layer, M).
+ */
+int32_t trellis_gemm_small(const tg_layer *layer, int32_t M,
+                           const uint16_t *X, int64_t ldx, float *Y, int64_t ldy,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Randomized Hadamard transform on 128-blocks of `rows` rows of n values
+ * (Deep Dive, Section 2; lecture, Part eleven):
+ *   inverse == 0: out = blockdiag(H) diag(s) in      (input side)
+ *   inverse != 0: out = diag(s) blockdiag(H) in      (output side)
+ *   in    : device, rows*n fp16 patterns, contiguous rows.
+ *   out   : device, rows*n fp32, contiguous rows.
+ *   signs : device, ceil(n/32) words.
+ * n must be a positive multiple of 128; 1 <= rows <= 65535.
+ */
+int32_t rht_apply(int32_t n, int32_t rows, const uint16_t *in, float *out,
+                  const uint32_t *signs, int32_t inverse, void *stream);
+
+/*
+ * Grouped batch-1 GEMVs over layers selected at run time on the device (the
+ * mixture-of-experts case: per token a few experts out of many, each tensor
+ * with its own K; Deep Dive, Section 4 and lecture, Part eleven on per-tensor
+ * bit widths).
+ *   layers    : host array of n_layers descriptors (validated on the host).
+ *   d_layers  : device array holding the same n_layers descriptors.
+ *   d_sel     : device, n_sel int32 indices into the layer array (each < n_layers).
+ *   X         : device fp16 inputs; selection e reads X + e*x_stride
+ *               (x_stride == 0: all selections share one input vector).
+ *   Y         : device fp32 outputs; selection e writes Y + e*y_stride.
+ *   ws        : device workspace, ws_bytes >= tg_grouped_workspace_size(...).
+ * Every layer's n must fit the input stride (n <= x_stride when x_stride != 0)
+ * and m <= y_stride. Indices in d_sel outside [0, n_layers) make the affected
+ * selection write nothing.
+ */
+int32_t trellis_gemv_grouped(const tg_layer *layers, const tg_layer *d_layers, int32_t n_layers,
+                             const int32_t *d_sel, int32_t n_sel,
+                             const uint16_t *X, int64_t x_stride, float *Y, int64_t y_stride,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for trellis_gemv_grouped over these layers and n_sel selections (0 if invalid). */
+size_t tg_grouped_workspace_size(const tg_layer *layers, int32_t n_layers, int32_t n_sel);
+
+/*
+ * Decode the whole layer to fp16 weights (test / export hook): w_out[o*n + i]
+ * = W^[o, i] as fp16 patterns, bit-exact with the code's definition. Only
+ * codes and shape are used; m, n need only be positive multiples of 16.
+ *   w_out : device, m*n uint16.
+ */
+int32_t trellis_decode(const tg_layer *layer, uint16_t *w_out, void *stream);
+
+/* The whole code as a table: out[S] = fp16 pattern of the weight for state S, S < 65536. */
+int32_t tg_code_table(int32_t code_id, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRELLIS_GEMV_H */

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header declares, and rejects bad
+arguments on the host before anything is enqueued (so these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from trellis_coded_gemv_amd import binding as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "trellis_gemv.h")
+
+# fake device addresses: never dereferenced, every call below fails validation first
+A16 = 0x10000
+A4 = 0x20004
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def _layer(**kw):
+    d = dict(m=256, n=512, k_bits=2, code_id=0, flags=0, reserved=0, codes=A16, scales=A16, sign_in=A16,
+             sign_out=A16)
+    d.update(kw)
+    return tg.TgLayer(**d)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = tg.lib()
+    declared = _declared_functions()
+    assert set(declared) == set(tg.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.tg_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(tg.TgLayer) == 56
+    assert tg.TgLayer.codes.offset == 24 and tg.TgLayer.sign_out.offset == 48
+
+
+def test_status_strings():
+    L = tg.lib()
+    for code in range(-8, 1):
+        assert L.tg_status_str(code).decode().startswith(tg.STATUS[code])
+    assert L.tg_status_str(-99) == b"unknown tg_status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_bits=0), -3), (dict(k_bits=9), -3), (dict(m=100), -2), (dict(n=0), -2), (dict(m=-128), -2),
+    (dict(code_id=1), -6), (dict(flags=4), -8), (dict(reserved=1), -8), (dict(codes=0), -1),
+    (dict(sign_out=0), -1), (dict(codes=A16 + 8), -4), (dict(scales=A16 + 1), -4), (dict(sign_in=A4 + 2), -4)])
+def test_gemv_layer_validation(kw, status):
+    d = _layer(**kw)
+    assert tg.lib().trellis_gemv(ctypes.byref(d), A16, A16, A16, 1 << 30, None) == status
+
+
+def test_gemv_argument_validation():
+    L = tg.lib()
+    d = _layer()
+    assert L.trellis_gemv(None, A16, A16, A16, 1 << 30, None) == -1
+    assert L.trellis_gemv(ctypes.byref(d), 0, A16, A16, 1 << 30, None) == -1
+    assert L.trellis_gemv(ctypes.byref(d), A16, A16 + 2, A16, 1 << 30, None) == -4
+    need = L.tg_workspace_size(ctypes.byref(d), 1)
+    assert need > 0
+    assert L.trellis_gemv(ctypes.byref(d), A16, A16, 0, need, None) == -5
+    assert L.trellis_gemv(ctypes.byref(d), A16, A16, A16, 255, None) == -5
+    assert L.trellis_gemv(ctypes.byref(d), A16, A16, A16 + 16, need, None) == -4
+
+
+def test_workspace_size_queries():
+    L = tg.lib()
+    d = _layer()
+    assert L.tg_workspace_size(None, 1) == 0
+    assert L.tg_workspace_size(ctypes.byref(d), 0) == 0
+    assert L.tg_workspace_size(ctypes.byref(d), 65) == 0
+    assert L.tg_workspace_size(ctypes.byref(_layer(k_bits=9)), 1) == 0
+    for M in (1, 2, 16, 17, 64):
+        assert L.tg_workspace_size(ctypes.byref(d), M) % 256 == 0
+
+
+def test_gemm_small_validation():
+    L = tg.lib()
+    d = _layer()
+    ws = 1 << 34
+    assert L.trellis_gemm_small(ctypes.byref(d), 0, A16, 512, A16, 256, A16, ws, None) == -2
+    assert L.trellis_gemm_small(ctypes.byref(d), 65, A16, 512, A16, 256, A16, ws, None) == -2
+    assert L.trellis_gemm_small(ctypes.byref(d), 4, A16, 511, A16, 256, A16, ws, None) == -8
+    assert L.trellis_gemm_small(ctypes.byref(d), 4, A16, 512, A16, 255, A16, ws, None) == -8
+    assert L.trellis_gemm_small(ctypes.byref(d), 4, 0, 512, A16, 256, A16, ws, None) == -1
+    assert L.trellis_gemm_small(ctypes.byref(d), 4, A16, 512, A16, 256, A16, 16, None) == -5
+
+
+def test_rht_validation():
+    L = tg.lib()
+    assert L.rht_apply(100, 1, A16, A16, A16, 0, None) == -2
+    assert L.rht_apply(128, 0, A16, A16, A16, 0, None) == -2
+    assert L.rht_apply(128, 70000, A16, A16, A16, 0, None) == -2
+    assert L.rht_apply(128, 1, 0, A16, A16, 0, None) == -1
+    assert L.rht_apply(128, 1, A16, A16 + 2, A16, 0, None) == -4
+
+
+def test_decode_and_table_validation():
+    L = tg.lib()
+    assert L.trellis_decode(None, A16, None) == -1
+    assert L.trellis_decode(ctypes.byref(_layer(m=24)), A16, None) == -2
+    assert L.trellis_decode(ctypes.byref(_layer(k_bits=0)), A16, None) == -3
+    assert L.trellis_decode(ctypes.byref(_layer()), 0, None) == -1
+    assert L.tg_code_table(3, A16, None) == -6
+    assert L.tg_code_table(0, 0, None) == -1
+
+
+def test_grouped_validation():
+    L = tg.lib()
+    arr = (tg.TgLayer * 2)(_layer(), _layer(m=128, k_bits=3))
+    assert L.tg_grouped_workspace_size(arr, 2, 4) > 0
+    assert L.tg_grouped_workspace_size(arr, 0, 4) == 0
+    bad = (tg.TgLayer * 2)(_layer(), _layer(k_bits=11))
+    ws = 1 << 34
+    assert L.trellis_gemv_grouped(bad, A16, 2, A16, 4, A16, 0, A16, 256, A16, ws, None) == -3
+    mixed = (tg.TgLayer * 2)(_layer(), _layer(flags=1))
+    assert L.trellis_gemv_grouped(mixed, A16, 2, A16, 4, A16, 0, A16, 256, A16, ws, None) == -8
+    assert L.trellis_gemv_grouped(arr, 0, 2, A16, 4, A16, 0, A16, 256, A16, ws, None) == -1
+    assert L.trellis_gemv_grouped(arr, A16, 2, A16, 4, A16, 100, A16, 256, A16, ws, None) == -8
+    assert L.trellis_gemv_grouped(arr, A16, 2, A16, 4, A16, 0, A16, 255, A16, ws, None) == -8
+    assert L.trellis_gemv_grouped(arr, A16, 2, A16, 4, A16, 0, A16, 256, A16, 64, None) == -5

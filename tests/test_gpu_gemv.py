@@ -1,0 +1,124 @@
+"""GPU parity: batch-1 trellis GEMV and the randomized Hadamard transform against the oracle."""
+import os
+
+import numpy as np
+import pytest
+
+from gpu_common import REL_TOL, device, rel_err, sample_rows, say
+from oracle import gemv as ogemv
+from oracle import hadamard as ohad
+from trellis_coded_gemv_amd import binding as tg
+from trellis_coded_gemv_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gemv(arr, x_bits, dev, flags=0, ws=None):
+    torch = pytest.importorskip("torch")
+    L = tg.DeviceLayer(arr, dev, flags=flags)
+    x = tg.fp16_tensor(x_bits, dev)
+    y = tg.trellis_gemv(L, x, ws=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("inverse", [False, True])
+@pytest.mark.parametrize("n,rows", [(128, 1), (384, 3), (14336, 2)])
+def test_rht_apply(n, rows, inverse):
+    dev = device()
+    rng = np.random.default_rng(n + rows)
+    x = rng.standard_normal((rows, n)).astype(np.float16)
+    sw = rng.integers(0, 1 << 32, n // 32, dtype=np.uint32)
+    import torch
+    say("rht", n, rows, inverse)
+    out = tg.rht_apply(torch.from_numpy(x).to(dev), torch.from_numpy(sw.view(np.int32)).to(dev), inverse)
+    xv = x.astype(np.float64)
+    ref = ohad.rht_inverse(xv, sw) if inverse else ohad.rht_forward(xv, sw)
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("flags", [0, tg.TG_FLAG_ROUND_WEIGHTS])
+@pytest.mark.parametrize("k", range(1, 9))
+@pytest.mark.parametrize("m,n", [(128, 128), (256, 384), (384, 256), (128, 1152)])
+def test_gemv_small_shapes(k, m, n, flags):
+    dev = device()
+    arr = inputs.make_layer(m, n, k, 2000 + k, tensor=m * 7 + n)
+    x = inputs.make_x(n, 2000 + k, tensor=m * 7 + n)
+    say("gemv", m, n, k, flags)
+    y = _run_gemv(arr, x, dev, flags)
+    assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
+
+
+def test_gemv_config1_full():
+    dev = device()
+    wl = inputs.CFG1
+    m, n, k = wl.tensors["linear"]
+    arr = inputs.make_layer(m, n, k, wl.seed)
+    x = inputs.make_x(n, wl.seed)
+    say("gemv cfg1")
+    for flags in (0, tg.TG_FLAG_ROUND_WEIGHTS):
+        y = _run_gemv(arr, x, dev, flags)
+        err = rel_err(y, ogemv.gemv(arr, x))
+        say("cfg1 flags", flags, "rel err", err)
+        assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("cfg,tensor", [(2, "down"), (3, "q"), (3, "k"), (3, "v"), (3, "o"), (3, "gate"),
+                                        (3, "up"), (3, "down")])
+def test_gemv_config_sampled(cfg, tensor):
+    """Full-size workload tensors in the launch configuration the bench times; oracle on sampled outputs."""
+    dev = device()
+    wl = inputs.WORKLOADS[cfg]
+    m, n, k = wl.tensors[tensor]
+    idx = list(wl.tensors).index(tensor)
+    arr = inputs.make_layer(m, n, k, wl.seed, tensor=idx)
+    x = inputs.make_x(n, wl.seed, tensor=idx)
+    say("gemv config", cfg, tensor, m, n, k)
+    y = _run_gemv(arr, x, dev)
+    assert np.isfinite(y).all()
+    rows = sample_rows(m, seed=idx)
+    err = rel_err(y[rows], ogemv.gemv_rows(arr, x, rows))
+    say("rel err", err)
+    assert err <= REL_TOL
+
+
+def test_gemv_deterministic_and_workspace_reuse():
+    dev = device()
+    import torch
+    arr = inputs.make_layer(1024, 4096, 3, 77)
+    x = inputs.make_x(4096, 77)
+    L = tg.DeviceLayer(arr, dev)
+    ws = tg.workspace(L, 1, dev)
+    xt = tg.fp16_tensor(x, dev)
+    say("determinism")
+    y1 = tg.trellis_gemv(L, xt, ws=ws).clone()
+    y2 = tg.trellis_gemv(L, xt, ws=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert (ws[: 1024 // 128 * 4] == 0).all()         # arrival counters are left at zero
+    rows = sample_rows(1024)
+    assert rel_err(y1.cpu().numpy()[rows], ogemv.gemv_rows(arr, x, rows)) <= REL_TOL
+
+
+@pytest.mark.parametrize("splits", ["1", "3", "7", "32"])
+def test_gemv_split_counts(splits, monkeypatch):
+    """Every split count (forced through the tuning override) gives the same answer within tolerance."""
+    dev = device()
+    monkeypatch.setenv("TG_SPLITK", splits)
+    arr = inputs.make_layer(256, 4096, 2, 88)
+    x = inputs.make_x(4096, 88)
+    say("splits", splits)
+    y = _run_gemv(arr, x, dev)
+    assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
+
+
+def test_gemv_edge_values():
+    """Zero input gives zero output; an all-zero stream matches the oracle's closed-form case."""
+    dev = device()
+    arr = inputs.make_layer(256, 256, 2, 99)
+    y = _run_gemv(arr, np.zeros(256, np.uint16), dev)
+    assert (y == 0).all()
+    arr.codes = np.zeros_like(arr.codes)
+    x = inputs.make_x(256, 99)
+    y = _run_gemv(arr, x, dev)
+    assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL

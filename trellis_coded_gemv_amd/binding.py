@@ -1,0 +1,231 @@
+"""ctypes binding of libtrellis_gemv.so -- argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; PyTorch is
+used only to own device memory and to supply the current HIP stream. The
+functions mirror the C ABI of include/trellis_gemv.h name for name. If the
+library is missing or fails to load, every entry point raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrellis_gemv.so")
+
+TG_FLAG_ROUND_WEIGHTS = 1
+
+STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS", -4: "TG_ERR_ALIGN",
+          -5: "TG_ERR_WORKSPACE", -6: "TG_ERR_CODE_ID", -7: "TG_ERR_LAUNCH", -8: "TG_ERR_ARG"}
+
+# every symbol the header declares
+EXPORTS = ("tg_abi_version", "tg_status_str", "tg_workspace_size", "trellis_gemv", "trellis_gemm_small",
+           "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table")
+
+
+class TgLayer(ctypes.Structure):
+    """Mirror of tg_layer."""
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("k_bits", ctypes.c_int32),
+                ("code_id", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("sign_in", ctypes.c_void_p), ("sign_out", ctypes.c_void_p)]
+
+
+class TgError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_status_str(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m trellis_coded_gemv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    LP = ctypes.POINTER(TgLayer)
+    sig = {
+        "tg_abi_version": (I32, []),
+        "tg_status_str": (ctypes.c_char_p, [I32]),
+        "tg_workspace_size": (SZ, [LP, I32]),
+        "trellis_gemv": (I32, [LP, P, P, P, SZ, P]),
+        "trellis_gemm_small": (I32, [LP, I32, P, I64, P, I64, P, SZ, P]),
+        "rht_apply": (I32, [I32, I32, P, P, P, I32, P]),
+        "trellis_gemv_grouped": (I32, [LP, P, I32, P, I32, P, I64, P, I64, P, SZ, P]),
+        "tg_grouped_workspace_size": (SZ, [LP, I32, I32]),
+        "trellis_decode": (I32, [LP, P, P]),
+        "tg_code_table": (I32, [I32, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _status_str(status: int) -> str:
+    try:
+        return lib().tg_status_str(status).decode()
+    except Exception:  # noqa: BLE001 - message only
+        return "?"
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise TgError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class DeviceLayer:
+    """A layer's arrays in device memory plus its tg_layer descriptor."""
+
+    def __init__(self, arrays, device="cuda", flags: int = 0):
+        torch = _torch()
+        self.m, self.n, self.k_bits = int(arrays.m), int(arrays.n), int(arrays.k_bits)
+        self.code_id, self.flags = int(getattr(arrays, "code_id", 0)), int(flags)
+        self.codes = torch.from_numpy(np.ascontiguousarray(arrays.codes).view(np.int32)).to(device)
+        self.scales = torch.from_numpy(np.ascontiguousarray(arrays.scales).view(np.int16)).to(device)
+        self.sign_in = torch.from_numpy(np.ascontiguousarray(arrays.sign_in).view(np.int32)).to(device)
+        self.sign_out = torch.from_numpy(np.ascontiguousarray(arrays.sign_out).view(np.int32)).to(device)
+
+    def desc(self) -> TgLayer:
+        return TgLayer(self.m, self.n, self.k_bits, self.code_id, self.flags, 0,
+                       self.codes.data_ptr(), self.scales.data_ptr(),
+                       self.sign_in.data_ptr(), self.sign_out.data_ptr())
+
+    @property
+    def code_bytes(self) -> int:
+        return self.codes.numel() * 4
+
+
+def fp16_tensor(bits: np.ndarray, device="cuda"):
+    """Host uint16 fp16 patterns -> device float16 tensor (same bits)."""
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.float16)).to(device)
+
+
+def workspace_size(layer: DeviceLayer, M: int = 1) -> int:
+    d = layer.desc()
+    return int(lib().tg_workspace_size(ctypes.byref(d), M))
+
+
+def workspace(layer: DeviceLayer, M: int = 1, device="cuda"):
+    """Zero-filled workspace for trellis_gemv (M == 1) / trellis_gemm_small."""
+    size = workspace_size(layer, M)
+    if size == 0:
+        raise TgError(-8, "tg_workspace_size")
+    return _torch().zeros(size, dtype=_torch().uint8, device=device)
+
+
+def trellis_gemv(layer: DeviceLayer, x, y=None, ws=None, stream=None):
+    """y = W x for fp16 x [n] on the device; returns fp32 y [m]."""
+    torch = _torch()
+    if y is None:
+        y = torch.empty(layer.m, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(layer, 1, x.device)
+    d = layer.desc()
+    _check(lib().trellis_gemv(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+           "trellis_gemv")
+    return y
+
+
+def trellis_gemm_small(layer: DeviceLayer, X, Y=None, ws=None, stream=None):
+    """Y[r] = W X[r] for fp16 X [M, n] (row stride X.stride(0)); returns fp32 Y [M, m]."""
+    torch = _torch()
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty(M, layer.m, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = workspace(layer, M, X.device)
+    d = layer.desc()
+    ldx = X.stride(0) if M > 1 else X.shape[1]      # a single row's stride is meaningless (may be 0)
+    ldy = Y.stride(0) if M > 1 else Y.shape[1]
+    _check(lib().trellis_gemm_small(ctypes.byref(d), M, _ptr(X), ldx, _ptr(Y), ldy,
+                                    _ptr(ws), ws.numel(), _stream(stream)), "trellis_gemm_small")
+    return Y
+
+
+def rht_apply(x, signs, inverse: bool = False, out=None, stream=None):
+    """Randomized Hadamard transform on 128-blocks of fp16 rows x [rows, n] -> fp32."""
+    torch = _torch()
+    x2 = x.reshape(-1, x.shape[-1])
+    if out is None:
+        out = torch.empty(x2.shape, dtype=torch.float32, device=x.device)
+    _check(lib().rht_apply(x2.shape[1], x2.shape[0], _ptr(x2), _ptr(out), _ptr(signs), int(bool(inverse)),
+                           _stream(stream)), "rht_apply")
+    return out.reshape(x.shape)
+
+
+class LayerTable:
+    """Host and device copies of an array of tg_layer descriptors (for the grouped path)."""
+
+    def __init__(self, layers: Sequence[DeviceLayer], device="cuda"):
+        torch = _torch()
+        self.layers = list(layers)
+        self.host = (TgLayer * len(self.layers))(*[l.desc() for l in self.layers])
+        raw = np.frombuffer(bytes(self.host), dtype=np.uint8)
+        self.device = torch.from_numpy(raw.copy()).to(device)
+
+    def __len__(self):
+        return len(self.layers)
+
+
+def grouped_workspace(table: LayerTable, n_sel: int, device="cuda"):
+    size = int(lib().tg_grouped_workspace_size(table.host, len(table), n_sel))
+    if size == 0:
+        raise TgError(-8, "tg_grouped_workspace_size")
+    return _torch().zeros(size, dtype=_torch().uint8, device=device)
+
+
+def trellis_gemv_grouped(table: LayerTable, sel, X, x_stride: int, Y, y_stride: int, ws=None, stream=None):
+    """For each e < len(sel): Y[e*y_stride : ...][:m] = W_{sel[e]} X[e*x_stride : ...] (x_stride 0 = shared x)."""
+    n_sel = int(sel.numel())
+    if ws is None:
+        ws = grouped_workspace(table, n_sel, X.device)
+    _check(lib().trellis_gemv_grouped(table.host, _ptr(table.device), len(table), _ptr(sel), n_sel,
+                                      _ptr(X), x_stride, _ptr(Y), y_stride, _ptr(ws), ws.numel(), _stream(stream)),
+           "trellis_gemv_grouped")
+    return Y
+
+
+def trellis_decode(layer: DeviceLayer, out=None, stream=None):
+    """All decoded weights as fp16 patterns, int16 tensor [m, n]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(layer.m, layer.n, dtype=torch.int16, device=layer.codes.device)
+    d = layer.desc()
+    _check(lib().trellis_decode(ctypes.byref(d), _ptr(out), _stream(stream)), "trellis_decode")
+    return out
+
+
+def code_table(device="cuda", stream=None):
+    torch = _torch()
+    out = torch.empty(1 << 16, dtype=torch.int16, device=device)
+    _check(lib().tg_code_table(0, _ptr(out), _stream(stream)), "tg_code_table")
+    return out

@@ -1,0 +1,285 @@
+// C ABI of the trellis-coded GEMV library: argument validation, workspace
+// sizing, split selection and kernel launches. Nothing here touches the GPU
+// before every argument has been checked.
+#include <stddef.h>
+#include <stdlib.h>
+
+#include "trellis_gemv.h"
+#include "tg_internal.hpp"
+
+#define TG_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace tg;
+
+constexpr size_t kAlign = 256;
+
+static_assert(sizeof(tg_layer) == sizeof(LayerDev), "device layer table mirrors tg_layer");
+static_assert(offsetof(tg_layer, codes) == offsetof(LayerDev, codes), "device layer table mirrors tg_layer");
+static_assert(offsetof(tg_layer, sign_out) == offsetof(LayerDev, sign_out), "device layer table mirrors tg_layer");
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
+
+int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+
+int32_t check_layer(const tg_layer* L) {
+  if (!L) return TG_ERR_NULL;
+  if (L->code_id != 0) return TG_ERR_CODE_ID;
+  if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
+  if (L->m <= 0 || L->n <= 0 || (L->m % kBlock) != 0 || (L->n % kBlock) != 0) return TG_ERR_SHAPE;
+  if (L->m > (1 << 22) || L->n > (1 << 22)) return TG_ERR_SHAPE;
+  if ((L->flags & ~TG_FLAG_ROUND_WEIGHTS) != 0 || L->reserved != 0) return TG_ERR_ARG;
+  if (!L->codes || !L->scales || !L->sign_in || !L->sign_out) return TG_ERR_NULL;
+  if (misaligned(L->codes, 16) || misaligned(L->scales, 2) || misaligned(L->sign_in, 4) ||
+      misaligned(L->sign_out, 4))
+    return TG_ERR_ALIGN;
+  return TG_OK;
+}
+
+// Number of input chunks (split-K) for a batch-1 GEMV: enough workgroups to
+// fill 256 CUs several times over, at least one whole 16-tile step per wave,
+// and a chunk that fits the LDS budget. TG_SPLITK overrides (tuning aid).
+int gemv_splits(int m, int n) {
+  const int ob = m / kBlock, nb = n / kBlock;
+  int s = env_int("TG_SPLITK");
+  if (s <= 0) {
+    const int target_wg = 1024;
+    s = (target_wg + ob - 1) / ob;
+    s = s < (nb / 2 > 0 ? nb / 2 : 1) ? s : (nb / 2 > 0 ? nb / 2 : 1);
+  }
+  const int min_s = (nb + kMaxChunkBlocks - 1) / kMaxChunkBlocks;
+  if (s < min_s) s = min_s;
+  if (s > nb) s = nb;
+  if (s < 1) s = 1;
+  return s;
+}
+
+// Splits of the small-batch path: the fp32 partials cost 8*S*M*m bytes of
+// traffic against m*n*K/8 code bytes, so keep S small; sub-chunks are 128
+// (M <= 32) or 64 inputs.
+int gemm_splits(int m, int n, int M, int k_bits) {
+  const int ob = m / kBlock;
+  const int mpad = (M + 15) / 16 * 16;
+  const int nsub = n / (mpad <= 32 ? 128 : 64);
+  int s = env_int("TG_SPLITK_MFMA");
+  if (s <= 0) {
+    s = (512 + ob - 1) / ob;
+    const int cap = (int)((int64_t)n * k_bits / (1024 * M));   // partial traffic <= 1/16 of the code bytes
+    if (s > cap) s = cap;
+  }
+  if (s > nsub) s = nsub;
+  if (s < 1) s = 1;
+  return s;
+}
+
+struct GemvWs {
+  size_t counters, partials, total;
+};
+
+GemvWs gemv_ws(int m, int splits) {
+  GemvWs w;
+  w.counters = 0;
+  w.partials = round_up((size_t)(m / kBlock) * 4, kAlign);
+  w.total = w.partials + (splits > 1 ? round_up((size_t)splits * m * 4, kAlign) : 0);
+  return w;
+}
+
+struct GemmWs {
+  size_t counters, xt, partials, total;
+};
+
+GemmWs gemm_ws(int m, int n, int M, int splits) {
+  GemmWs w;
+  const int mpad = (M + 15) / 16 * 16;
+  w.counters = 0;
+  w.xt = round_up((size_t)(m / kBlock) * 4, kAlign);
+  w.partials = w.xt + round_up((size_t)mpad * n * 4, kAlign);
+  w.total = w.partials + (splits > 1 ? round_up((size_t)splits * M * m * 4, kAlign) : 0);
+  return w;
+}
+
+struct GroupedWs {
+  int max_m, max_n, splits;
+  size_t counters, partials, total;
+};
+
+int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel, GroupedWs* g) {
+  if (!layers) return TG_ERR_NULL;
+  if (n_layers <= 0 || n_sel <= 0 || n_sel > 65536) return TG_ERR_ARG;
+  int max_m = 0, max_n = 0, flags = layers[0].flags;
+  for (int i = 0; i < n_layers; ++i) {
+    const int32_t st = check_layer(&layers[i]);
+    if (st != TG_OK) return st;
+    if (layers[i].flags != flags) return TG_ERR_ARG;
+    if (layers[i].m > max_m) max_m = layers[i].m;
+    if (layers[i].n > max_n) max_n = layers[i].n;
+  }
+  const int max_ob = max_m / kBlock, max_nb = max_n / kBlock;
+  int s = env_int("TG_SPLITK");
+  if (s <= 0) {
+    s = (1024 + n_sel * max_ob - 1) / (n_sel * max_ob);
+    const int cap = max_nb / 2 > 0 ? max_nb / 2 : 1;
+    if (s > cap) s = cap;
+  }
+  const int min_s = (max_nb + kMaxChunkBlocks - 1) / kMaxChunkBlocks;
+  if (s < min_s) s = min_s;
+  if (s > max_nb) s = max_nb;
+  if (s < 1) s = 1;
+  g->max_m = max_m;
+  g->max_n = max_n;
+  g->splits = s;
+  g->counters = 0;
+  g->partials = round_up((size_t)n_sel * max_ob * 4, kAlign);
+  g->total = g->partials + round_up((size_t)n_sel * s * max_m * 4, kAlign);
+  return TG_OK;
+}
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH; }
+
+}  // namespace
+
+TG_API int32_t tg_abi_version(void) { return TG_ABI_VERSION; }
+
+TG_API const char* tg_status_str(int32_t status) {
+  switch (status) {
+    case TG_OK: return "TG_OK";
+    case TG_ERR_NULL: return "TG_ERR_NULL: a required pointer is NULL";
+    case TG_ERR_SHAPE: return "TG_ERR_SHAPE: shape or row count out of range";
+    case TG_ERR_KBITS: return "TG_ERR_KBITS: k_bits must be 1..8";
+    case TG_ERR_ALIGN: return "TG_ERR_ALIGN: pointer misaligned";
+    case TG_ERR_WORKSPACE: return "TG_ERR_WORKSPACE: workspace missing or too small";
+    case TG_ERR_CODE_ID: return "TG_ERR_CODE_ID: unsupported code_id";
+    case TG_ERR_LAUNCH: return "TG_ERR_LAUNCH: kernel launch failed";
+    case TG_ERR_ARG: return "TG_ERR_ARG: invalid argument";
+    default: return "unknown tg_status";
+  }
+}
+
+TG_API size_t tg_workspace_size(const tg_layer* L, int32_t M) {
+  if (check_layer(L) != TG_OK || M < 1 || M > 64) return 0;
+  const size_t g = gemm_ws(L->m, L->n, M, gemm_splits(L->m, L->n, M, L->k_bits)).total;
+  if (M > 1) return g;
+  const size_t v = gemv_ws(L->m, gemv_splits(L->m, L->n)).total;
+  return v > g ? v : g;
+}
+
+TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void* ws, size_t ws_bytes,
+                            void* stream) {
+  int32_t st = check_layer(L);
+  if (st != TG_OK) return st;
+  if (!x || !y) return TG_ERR_NULL;
+  if (misaligned(x, 2) || misaligned(y, 4)) return TG_ERR_ALIGN;
+  const int splits = gemv_splits(L->m, L->n);
+  const GemvWs w = gemv_ws(L->m, splits);
+  if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
+  if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
+  GemvArgs a;
+  a.codes = L->codes;
+  a.scales = L->scales;
+  a.sign_in = L->sign_in;
+  a.sign_out = L->sign_out;
+  a.x = x;
+  a.y = y;
+  a.counters = reinterpret_cast<uint32_t*>((char*)ws + w.counters);
+  a.partials = reinterpret_cast<float*>((char*)ws + w.partials);
+  a.m = L->m;
+  a.n = L->n;
+  a.splits = splits;
+  return launch_status(launch_gemv(a, L->k_bits, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
+}
+
+TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* X, int64_t ldx, float* Y,
+                                  int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != TG_OK) return st;
+  if (M < 1 || M > 64) return TG_ERR_SHAPE;
+  if (!X || !Y) return TG_ERR_NULL;
+  if (ldx < L->n || ldy < L->m) return TG_ERR_ARG;
+  if (misaligned(X, 2) || misaligned(Y, 4)) return TG_ERR_ALIGN;
+  const int splits = gemm_splits(L->m, L->n, M, L->k_bits);
+  const GemmWs w = gemm_ws(L->m, L->n, M, splits);
+  if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
+  if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
+  GemmArgs a;
+  a.codes = L->codes;
+  a.scales = L->scales;
+  a.sign_out = L->sign_out;
+  a.xt = reinterpret_cast<const uint32_t*>((char*)ws + w.xt);
+  a.y = Y;
+  a.ldy = ldy;
+  a.counters = reinterpret_cast<uint32_t*>((char*)ws + w.counters);
+  a.partials = reinterpret_cast<float*>((char*)ws + w.partials);
+  a.m = L->m;
+  a.n = L->n;
+  a.M = M;
+  a.mpad = (M + 15) / 16 * 16;
+  a.splits = splits;
+  return launch_status(launch_gemm_small(a, X, ldx, L->sign_in, L->k_bits, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0,
+                                         (hipStream_t)stream));
+}
+
+TG_API int32_t rht_apply(int32_t n, int32_t rows, const uint16_t* in, float* out, const uint32_t* signs,
+                         int32_t inverse, void* stream) {
+  if (n <= 0 || n % kBlock != 0 || n > (1 << 22) || rows < 1 || rows > 65535) return TG_ERR_SHAPE;
+  if (!in || !out || !signs) return TG_ERR_NULL;
+  if (misaligned(in, 2) || misaligned(out, 4) || misaligned(signs, 4)) return TG_ERR_ALIGN;
+  return launch_status(launch_rht(n, rows, in, out, signs, inverse != 0, (hipStream_t)stream));
+}
+
+TG_API size_t tg_grouped_workspace_size(const tg_layer* layers, int32_t n_layers, int32_t n_sel) {
+  GroupedWs g;
+  if (grouped_geometry(layers, n_layers, n_sel, &g) != TG_OK) return 0;
+  return g.total;
+}
+
+TG_API int32_t trellis_gemv_grouped(const tg_layer* layers, const tg_layer* d_layers, int32_t n_layers,
+                                    const int32_t* d_sel, int32_t n_sel, const uint16_t* X, int64_t x_stride,
+                                    float* Y, int64_t y_stride, void* ws, size_t ws_bytes, void* stream) {
+  GroupedWs g;
+  int32_t st = grouped_geometry(layers, n_layers, n_sel, &g);
+  if (st != TG_OK) return st;
+  if (!d_layers || !d_sel || !X || !Y) return TG_ERR_NULL;
+  if (misaligned(d_layers, 8) || misaligned(d_sel, 4) || misaligned(X, 2) || misaligned(Y, 4)) return TG_ERR_ALIGN;
+  if (x_stride < 0 || (x_stride != 0 && x_stride < g.max_n) || y_stride < g.max_m) return TG_ERR_ARG;
+  if (!ws || ws_bytes < g.total) return TG_ERR_WORKSPACE;
+  if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
+  GroupedArgs a;
+  a.layers = reinterpret_cast<const LayerDev*>(d_layers);
+  a.sel = d_sel;
+  a.n_layers = n_layers;
+  a.n_sel = n_sel;
+  a.x = X;
+  a.x_stride = x_stride;
+  a.y = Y;
+  a.y_stride = y_stride;
+  a.counters = reinterpret_cast<uint32_t*>((char*)ws + g.counters);
+  a.partials = reinterpret_cast<float*>((char*)ws + g.partials);
+  a.max_m = g.max_m;
+  a.splits = g.splits;
+  a.round_weights = (layers[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0;
+  return launch_status(launch_grouped(a, g.max_m / kBlock, g.max_n, (hipStream_t)stream));
+}
+
+TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) {
+  if (!L) return TG_ERR_NULL;
+  if (L->code_id != 0) return TG_ERR_CODE_ID;
+  if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
+  if (L->m <= 0 || L->n <= 0 || L->m % kTile != 0 || L->n % kTile != 0 || L->m > (1 << 22) || L->n > (1 << 22))
+    return TG_ERR_SHAPE;
+  if (!L->codes || !w_out) return TG_ERR_NULL;
+  if (misaligned(L->codes, 4) || misaligned(w_out, 2)) return TG_ERR_ALIGN;
+  return launch_status(launch_decode(L->codes, w_out, L->m, L->n, L->k_bits, (hipStream_t)stream));
+}
+
+TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
+  if (code_id != 0) return TG_ERR_CODE_ID;
+  if (!out) return TG_ERR_NULL;
+  if (misaligned(out, 2)) return TG_ERR_ALIGN;
+  return launch_status(launch_code_table(out, (hipStream_t)stream));
+}

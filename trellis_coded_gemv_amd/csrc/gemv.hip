@@ -1,0 +1,285 @@
+// Batch-1 trellis-coded GEMV for gfx950 (VALU decode + v_dot2 accumulate).
+//
+// Computes y = diag(s_out) H (g * (W^ (H diag(s_in) x))) for one activation
+// vector ("ExLlamaV3 & EXL3 Deep Dive", Section 2; "Trellis Quantization"
+// lecture, Parts eight, nine and eleven).
+//
+// Work decomposition. A workgroup of 8 waves owns one 128-output block (8
+// tile rows, one wave per tile row) and one contiguous chunk of 128-blocks of
+// the input ("split"). In one step a wave covers 16 tiles of its tile row:
+// lane l takes tile slot l/4 and rows 4*(l%4)..+3 of that tile, i.e. 64
+// consecutive sequence steps = 2K consecutive code words. Lanes therefore load
+// 8K contiguous bytes each and the wave one contiguous 1024K-byte run of the
+// tile row: fully coalesced 64/128-bit streaming loads. The 16-K bits of
+// overlap past a lane's last window come from the first word of the next lane
+// of the quad; the last lane of a quad takes the quad's first word, which is
+// exactly the tail-biting wrap of the tile (DPP quad_perm [1,2,3,0]).
+//
+// Per weight the VALU work is: one v_bfe_u32 window extract (plus one
+// v_alignbit per 32 stream bits for windows that straddle words), one
+// v_mad_u32_u24, one v_and_or_b32, one v_dot2c_f32_f16. The two fp16 halves
+// of the code enter the dot product against the pair (x~, x~), so the weight
+// lo+hi is used exactly inside the fp32 product; TG_FLAG_ROUND_WEIGHTS
+// instead rounds lo+hi to fp16 first (one v_add_f16 more per weight).
+//
+// Prologue: each workgroup transforms its input chunk (signs by XOR on the
+// fp16 sign bit, 128-point FWHT in registers with lane shuffles, 1/sqrt(128))
+// into LDS as fp16 pairs. Epilogue: lane -> wave reduction by lane shuffles,
+// then either a direct output transform (1 split) or fp32 split-K partials in
+// the workspace; the last-arriving workgroup of a block sums them in a fixed
+// order and applies scale, output FWHT and signs. No waiting on other
+// workgroups anywhere: every workgroup runs to completion independently.
+#include "tg_device.hpp"
+#include "tg_internal.hpp"
+
+namespace tg {
+
+// Prefetch depth in steps (each step is 8K bytes per lane).
+template <int K>
+constexpr int gemv_pf() { return K <= 2 ? 4 : (K <= 4 ? 3 : 2); }
+
+// Load this lane's 2K words (8K bytes) of the current step.
+template <int K>
+__device__ __forceinline__ void load_lane_words(const uint32_t* __restrict__ p, uint32_t (&w)[2 * K]) {
+  if constexpr (K % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
+      w[4 * i + 0] = v[0];
+      w[4 * i + 1] = v[1];
+      w[4 * i + 2] = v[2];
+      w[4 * i + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + i);
+      w[2 * i + 0] = v[0];
+      w[2 * i + 1] = v[1];
+    }
+  }
+}
+
+// Decode the lane's 64 weights (4 rows x 16 columns of one tile) and
+// accumulate their dot products with x~ of that tile column.
+//   w   : the lane's 2K stream words (stream bits 0 .. 64K-1 of the lane, MSB first)
+//   nb  : first word of the next lane in the tile (wrapping at the tile's end)
+//   xx  : 16 pairs (x~_c, x~_c) for the tile's 16 input columns
+template <int K, bool ROUND>
+__device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xx)[16],
+                                              float (&acc)[4], const CodeRegs& cr) {
+  constexpr int NW = 2 * K;
+  auto word = [&](int j) -> uint32_t { return j < NW ? w[j] : nb; };
+#pragma unroll
+  for (int tl = 0; tl < 64; ++tl) {
+    const int p = K * tl;            // window start, bits from the lane's first stream bit
+    const int j = p >> 5, q = p & 31;
+    uint32_t s;
+    if (q <= 16) {
+      s = ubfe(word(j), 16 - q, 16);
+    } else {
+      s = ubfe(alignbit(word(j), word(j + 1), 16), 32 - q, 16);
+    }
+    const uint32_t u = code_halves(s, cr);
+    if constexpr (ROUND) {
+      const uint32_t wr = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
+      acc[tl >> 4] = dot2(wr, xx[tl & 15], acc[tl >> 4]);
+    } else {
+      acc[tl >> 4] = dot2(u, xx[tl & 15], acc[tl >> 4]);
+    }
+  }
+}
+
+template <int K, bool ROUND, int PF>
+__device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int split, uint32_t* lds) {
+  constexpr int NW = 2 * K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb128 = a.n >> 7;
+  const int blk0 = (int)((int64_t)split * nb128 / a.splits);
+  const int blk1 = (int)((int64_t)(split + 1) * nb128 / a.splits);
+  const int cb = blk1 - blk0;             // 128-blocks in this chunk
+  const int ntiles = cb * 8;              // tiles of the chunk in one tile row
+  const int nsteps = (cb + 1) >> 1;       // 16 tiles per step
+  const int jslot = lane >> 2;
+  const int R = ob * 8 + wave;
+  const uint32_t* __restrict__ rowp =
+      a.codes + ((size_t)R * (size_t)(a.n >> 4) + (size_t)blk0 * 8) * (size_t)(8 * K) + (size_t)lane * NW;
+
+  uint32_t* xx_lds = lds;                                        // [2*nsteps blocks][128] pairs
+  float* ybuf = reinterpret_cast<float*>(lds + nsteps * 256);    // [128]
+  uint32_t* flag = lds + nsteps * 256 + 128;
+
+  // The first input block of this wave is fetched before the code prefetch:
+  // loads complete in order, so fetching it later would make the transform
+  // below wait for every prefetched code word as well.
+  const XBlock xfirst = load_x_block(a.x, a.sign_in, (blk0 + (wave < cb ? wave : cb - 1)) * kBlock, lane);
+  __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the prefetch below
+
+  // Prefetch ring. Every issue is unconditional (out-of-range steps and tiles
+  // read a dummy line at the start of the code array instead), so each path
+  // through the loop issues the same loads and the waits stay exact.
+  uint32_t buf[PF][NW];
+  const uint32_t* __restrict__ dummy = a.codes;
+  auto issue = [&](int st, uint32_t(&dst)[NW]) {
+    const bool ok = st < nsteps && st * 16 + jslot < ntiles;
+    load_lane_words<K>(ok ? rowp + (size_t)st * (128 * K) : dummy, dst);
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) issue(p, buf[p]);
+
+  // Prologue: x~ for the chunk, padded with zeros to whole steps.
+  for (int bb = wave; bb < 2 * nsteps; bb += kGemvWaves) {
+    uint32_t d0 = 0u, d1 = 0u;
+    if (bb < cb) {
+      const XBlock xb = bb == wave ? xfirst : load_x_block(a.x, a.sign_in, (blk0 + bb) * kBlock, lane);
+      rht_in_block_dup(xb, lane, d0, d1);
+    }
+    xx_lds[bb * kBlock + lane] = d0;
+    xx_lds[bb * kBlock + lane + 64] = d1;
+  }
+  __syncthreads();
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const CodeRegs cr;
+  for (int st0 = 0; st0 < nsteps; st0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int st = st0 + p;
+      uint32_t w[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) w[i] = buf[p][i];
+      issue(st + PF, buf[p]);
+      if (st < nsteps) {
+        uint32_t xv[16];
+        const u32x4* xs = reinterpret_cast<const u32x4*>(xx_lds + (st * 16 + jslot) * 16);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 t = xs[v];
+          xv[4 * v + 0] = t[0];
+          xv[4 * v + 1] = t[1];
+          xv[4 * v + 2] = t[2];
+          xv[4 * v + 3] = t[3];
+        }
+        const uint32_t nbw = quad_rotate_next(w[0]);
+        decode_dot_64<K, ROUND>(w, nbw, xv, acc, cr);
+      }
+    }
+  }
+
+  // Sum the 16 tile slots (lane bits 2..5); every lane ends with its rows' totals.
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+#pragma unroll
+    for (int mask = 4; mask <= 32; mask <<= 1) acc[g] += shfl_xor(acc[g], mask);
+  }
+  const int orow = wave * 16 + (lane & 3) * 4;   // output within the 128-block
+
+  if (a.splits == 1) {
+    if (lane < 4) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) ybuf[orow + g] = acc[g];
+    }
+    __syncthreads();
+    if (wave == 0) rht_out_block(ybuf[lane], ybuf[lane + 64], a.scales, a.sign_out, a.y, ob * kBlock, lane);
+    return;
+  }
+
+  if (lane < 4) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) store_partial(a.partials + (size_t)split * a.m + ob * kBlock + orow + g, acc[g]);
+  }
+  if (!arrive_is_last(&a.counters[ob], (uint32_t)a.splits, flag)) return;
+  if (wave == 0) {
+    float v0 = 0.f, v1 = 0.f;
+    const float* pp = a.partials + ob * kBlock;
+    for (int t = 0; t < a.splits; ++t) {
+      v0 += load_partial(pp + (size_t)t * a.m + lane);
+      v1 += load_partial(pp + (size_t)t * a.m + lane + 64);
+    }
+    rht_out_block(v0, v1, a.scales, a.sign_out, a.y, ob * kBlock, lane);
+    if (lane == 0) reset_counter(&a.counters[ob]);
+  }
+}
+
+// Blocks are issued round-robin over the 8 XCDs; remap so that the splits of
+// one output block, and the blocks reading the same input chunk, share an XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  return (nblk & 7) == 0 ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
+}
+
+template <int K, bool ROUND, int PF>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int ob = bid / a.splits;
+  gemv_workgroup<K, ROUND, PF>(a, ob, bid - ob * a.splits, lds);
+}
+
+template <bool ROUND>
+__global__ __launch_bounds__(kGemvThreads) void grouped_kernel(GroupedArgs g, int max_ob) {
+  extern __shared__ uint32_t lds[];
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_sel = max_ob * g.splits;
+  const int e = bid / per_sel;
+  const int rem = bid - e * per_sel;
+  const int ob = rem / g.splits, split = rem - ob * g.splits;
+  const int li = g.sel[e];
+  if (li < 0 || li >= g.n_layers) return;
+  const LayerDev L = g.layers[li];
+  if (ob >= (L.m >> 7)) return;
+  GemvArgs a;
+  a.codes = L.codes;
+  a.scales = L.scales;
+  a.sign_in = L.sign_in;
+  a.sign_out = L.sign_out;
+  a.x = g.x + (size_t)e * g.x_stride;
+  a.y = g.y + (size_t)e * g.y_stride;
+  a.partials = g.partials + (size_t)e * g.splits * g.max_m;
+  a.counters = g.counters + (size_t)e * (g.max_m >> 7);
+  a.m = L.m;
+  a.n = L.n;
+  a.splits = g.splits;
+  switch (L.k_bits) {
+    case 1: gemv_workgroup<1, ROUND, gemv_pf<1>()>(a, ob, split, lds); break;
+    case 2: gemv_workgroup<2, ROUND, gemv_pf<2>()>(a, ob, split, lds); break;
+    case 3: gemv_workgroup<3, ROUND, gemv_pf<3>()>(a, ob, split, lds); break;
+    case 4: gemv_workgroup<4, ROUND, gemv_pf<4>()>(a, ob, split, lds); break;
+    case 5: gemv_workgroup<5, ROUND, gemv_pf<5>()>(a, ob, split, lds); break;
+    case 6: gemv_workgroup<6, ROUND, gemv_pf<6>()>(a, ob, split, lds); break;
+    case 7: gemv_workgroup<7, ROUND, gemv_pf<7>()>(a, ob, split, lds); break;
+    default: gemv_workgroup<8, ROUND, gemv_pf<8>()>(a, ob, split, lds); break;
+  }
+}
+
+template <int K, bool ROUND>
+static hipError_t launch_k(const GemvArgs& a, hipStream_t s) {
+  constexpr int PF = gemv_pf<K>();
+  const int nb128 = a.n >> 7;
+  const int max_chunk = (nb128 + a.splits - 1) / a.splits;
+  const int grid = (a.m >> 7) * a.splits;
+  hipLaunchKernelGGL((gemv_kernel<K, ROUND, PF>), dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(max_chunk), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GemvArgs& a, int k_bits, bool round_weights, hipStream_t s) {
+#define TG_CASE(K) \
+  case K: return round_weights ? launch_k<K, true>(a, s) : launch_k<K, false>(a, s);
+  switch (k_bits) {
+    TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef TG_CASE
+}
+
+hipError_t launch_grouped(const GroupedArgs& g, int max_ob, int max_n, hipStream_t s) {
+  const int grid = g.n_sel * max_ob * g.splits;
+  if (grid == 0) return hipSuccess;
+  const int max_chunk = ((max_n >> 7) + g.splits - 1) / g.splits;
+  if (g.round_weights)
+    hipLaunchKernelGGL(grouped_kernel<true>, dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(max_chunk), s, g, max_ob);
+  else
+    hipLaunchKernelGGL(grouped_kernel<false>, dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(max_chunk), s, g, max_ob);
+  return hipGetLastError();
+}
+
+}  // namespace tg

@@ -1,0 +1,188 @@
+// Device-side building blocks shared by the trellis-coded GEMV kernels (gfx950).
+//
+// Window extraction follows the bitshift trellis of the "Trellis Quantization"
+// lecture, Part eight (weight t's 16-bit state starts at stream bit K*t, the
+// stream of a 16x16 tile is a circle) and the code follows its Part nine
+// (three-instruction code). Storage conventions are those of trellis_gemv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Code constants (code_id 0).
+constexpr uint32_t kMul = 0x009E3779u;   // 24-bit LCG multiplier: one full-rate v_mad_u32_u24
+constexpr uint32_t kAdd = 0x7F4A7C15u;
+constexpr uint32_t kMask = 0x8FFF8FFFu;  // sign, 2 low exponent bits, 10 fraction bits per half
+constexpr uint32_t kXor = 0x30003000u;   // exponent field 0b011xx: |half| in [1/8, 2)
+
+constexpr float kRsqrt128 = 0.088388347648318440550f;  // 1/sqrt(128), correctly rounded
+
+// The mask/XOR constants are laundered through empty asm so the compiler keeps
+// them in registers and emits the bit insert as one v_and_or_b32 (the constant
+// bus allows one SGPR operand, the other constant lives in a VGPR). Since the
+// XOR constant only touches masked-off bits, AND-then-OR equals AND-then-XOR.
+struct CodeRegs {
+  uint32_t mask, xr;
+  __device__ __forceinline__ CodeRegs() : mask(kMask), xr(kXor) {
+    asm volatile("" : "+s"(mask));
+    asm volatile("" : "+v"(xr));
+  }
+};
+
+// 16-bit state -> 32-bit word holding the two fp16 halves of the weight.
+__device__ __forceinline__ uint32_t code_halves(uint32_t state, const CodeRegs& c) {
+  const uint32_t h = state * kMul + kAdd;  // state < 2^16: v_mad_u32_u24
+  return (h & c.mask) | c.xr;
+}
+
+// fp16 weight = round-to-nearest-even(lo + hi), as a 16-bit pattern.
+__device__ __forceinline__ _Float16 halves_sum_rne(uint32_t u) {
+  const half2_t p = __builtin_bit_cast(half2_t, u);
+  return p[0] + p[1];
+}
+
+__device__ __forceinline__ uint32_t ubfe(uint32_t v, uint32_t off, uint32_t width) {
+  return __builtin_amdgcn_ubfe(v, off, width);
+}
+
+// 32 bits of the stream starting "shift" bits before the end of hi:  ({hi, lo} >> shift)[31:0].
+__device__ __forceinline__ uint32_t alignbit(uint32_t hi, uint32_t lo, uint32_t shift) {
+  return __builtin_amdgcn_alignbit(hi, lo, shift);
+}
+
+// fp32 accumulate of (a.lo*b.lo + a.hi*b.hi).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
+}
+
+// Value of lane (lane+1) mod 4 within each quad (DPP quad_perm [1,2,3,0]).
+__device__ __forceinline__ uint32_t quad_rotate_next(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, 0x39, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+__device__ __forceinline__ uint32_t sign_bit(const uint32_t* __restrict__ words, int i) {
+  return (words[i >> 5] >> (i & 31)) & 1u;
+}
+
+// Unnormalised 128-point Sylvester-order Walsh-Hadamard transform held by one
+// wave: lane l owns elements l (v0) and l+64 (v1). Seven butterfly stages
+// (a, b) -> (a+b, a-b); the stride-64 stage is in-lane, the others pair lanes
+// l and l^h.
+__device__ __forceinline__ void fwht128_wave(float& v0, float& v1, int lane) {
+  const float a = v0 + v1, b = v0 - v1;
+  v0 = a;
+  v1 = b;
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const float p0 = shfl_xor(v0, h), p1 = shfl_xor(v1, h);
+    const bool upper = (lane & h) != 0;
+    v0 = upper ? (p0 - v0) : (v0 + p0);
+    v1 = upper ? (p1 - v1) : (v1 + p1);
+  }
+}
+
+// Raw inputs of one 128-block for the input-side transform: the fp16 patterns
+// of elements lane and lane+64 and the sign words that hold their bits. No
+// arithmetic happens at load time, so the loads can be issued early.
+struct XBlock {
+  uint16_t b0, b1;
+  uint32_t s0, s1;
+  int base;
+};
+
+__device__ __forceinline__ XBlock load_x_block(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
+                                               int base, int lane) {
+  XBlock r;
+  r.b0 = x[base + lane];
+  r.b1 = x[base + lane + 64];
+  r.s0 = sign_in[(base + lane) >> 5];
+  r.s1 = sign_in[(base + lane + 64) >> 5];
+  r.base = base;
+  return r;
+}
+
+// Input-side transform of one 128-block held by a wave: x~ = H diag(s) x / sqrt(128),
+// returned as fp16 in both halves of a 32-bit word (the fused dot consumes pairs (x~, x~)).
+__device__ __forceinline__ void rht_in_block_dup(XBlock xb, int lane, uint32_t& d0, uint32_t& d1) {
+  const uint16_t b0 = xb.b0 ^ (uint16_t)(((xb.s0 >> ((xb.base + lane) & 31)) & 1u) << 15);
+  const uint16_t b1 = xb.b1 ^ (uint16_t)(((xb.s1 >> ((xb.base + lane + 64) & 31)) & 1u) << 15);
+  float v0 = half_bits_to_float(b0), v1 = half_bits_to_float(b1);
+  fwht128_wave(v0, v1, lane);
+  const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(v0 * kRsqrt128));
+  const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(v1 * kRsqrt128));
+  d0 = (uint32_t)h0 | ((uint32_t)h0 << 16);
+  d1 = (uint32_t)h1 | ((uint32_t)h1 << 16);
+}
+
+__device__ __forceinline__ void rht_in_block_dup(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
+                                                 int base, int lane, uint32_t& d0, uint32_t& d1) {
+  rht_in_block_dup(load_x_block(x, sign_in, base, lane), lane, d0, d1);
+}
+
+// Output-side epilogue of one 128-block held by a wave:
+// y = diag(s_out) H (g * y~) / sqrt(128), written as fp32.
+__device__ __forceinline__ void rht_out_block(float v0, float v1, const uint16_t* __restrict__ scales,
+                                              const uint32_t* __restrict__ sign_out, float* __restrict__ y,
+                                              int base, int lane) {
+  v0 *= half_bits_to_float(scales[base + lane]);
+  v1 *= half_bits_to_float(scales[base + lane + 64]);
+  fwht128_wave(v0, v1, lane);
+  v0 *= kRsqrt128;
+  v1 *= kRsqrt128;
+  if (sign_bit(sign_out, base + lane)) v0 = -v0;
+  if (sign_bit(sign_out, base + lane + 64)) v1 = -v1;
+  y[base + lane] = v0;
+  y[base + lane + 64] = v1;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K handoff between workgroups without cache writebacks.
+//
+// Partial sums are written and read with device-scope relaxed atomic stores /
+// loads, which this target performs coherently at device scope (write-through
+// stores and L2-coherent loads), so no L2 writeback or invalidate is needed.
+// Each workgroup waits for its own partial stores to complete before it
+// increments the arrival counter; the workgroup that sees the count reach
+// `total - 1` reads all partials (issued after it observed the counter) and
+// resets the counter to zero for the next call. No workgroup ever waits for
+// another one.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns true in every thread of the last-arriving workgroup. `flag` is a word of LDS.
+__device__ __forceinline__ bool arrive_is_last(uint32_t* counter, uint32_t total, uint32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = (__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1u) ? 1u : 0u;
+  __syncthreads();
+  return *flag != 0u;
+}
+
+__device__ __forceinline__ void reset_counter(uint32_t* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace tg

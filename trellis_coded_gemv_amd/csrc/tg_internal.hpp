@@ -1,0 +1,79 @@
+// Host-side declarations shared by the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tg {
+
+constexpr int kTile = 16;
+constexpr int kBlock = 128;              // Hadamard block; 8 tile rows / 8 tile columns
+constexpr int kGemvWaves = 8;            // one wave per tile row of a 128-output block
+constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kMaxChunkBlocks = 64;      // 128-blocks of x~ held in LDS by one GEMV workgroup
+
+// One batch-1 GEMV as a workgroup sees it.
+struct GemvArgs {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint32_t* sign_in;
+  const uint32_t* sign_out;
+  const uint16_t* x;
+  float* y;
+  float* partials;      // [splits][m]   (unused when splits == 1)
+  uint32_t* counters;   // [m/128]       arrival counters, zero between calls
+  int32_t m, n, splits;
+};
+
+// Grouped batch-1 GEMVs: the layer table lives in device memory.
+struct LayerDev {          // mirrors tg_layer
+  int32_t m, n, k_bits, code_id, flags, reserved;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint32_t* sign_in;
+  const uint32_t* sign_out;
+};
+
+struct GroupedArgs {
+  const LayerDev* layers;
+  const int32_t* sel;
+  int32_t n_layers, n_sel;
+  const uint16_t* x;
+  int64_t x_stride;
+  float* y;
+  int64_t y_stride;
+  float* partials;      // [n_sel][splits][max_m]
+  uint32_t* counters;   // [n_sel][max_m/128]
+  int32_t max_m, splits, round_weights;
+};
+
+// Small-batch MFMA path.
+struct GemmArgs {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint32_t* sign_out;
+  const uint32_t* xt;   // [mpad][n] fp16 pairs (x~, x~) prepared by the input transform kernel
+  float* y;
+  int64_t ldy;
+  float* partials;      // [splits][M][m]
+  uint32_t* counters;   // [m/128]
+  int32_t m, n, M, mpad, splits;
+};
+
+hipError_t launch_gemv(const GemvArgs& a, int k_bits, bool round_weights, hipStream_t s);
+hipError_t launch_grouped(const GroupedArgs& a, int max_ob, int max_n, hipStream_t s);
+hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in,
+                             int k_bits, bool round_weights, hipStream_t s);
+hipError_t launch_rht(int n, int rows, const uint16_t* in, float* out, const uint32_t* signs, bool inverse,
+                      hipStream_t s);
+hipError_t launch_decode(const uint32_t* codes, uint16_t* out, int m, int n, int k_bits, hipStream_t s);
+hipError_t launch_code_table(uint16_t* out, hipStream_t s);
+
+// LDS bytes a GEMV workgroup needs for a chunk of `chunk_blocks` 128-blocks.
+inline size_t gemv_lds_bytes(int chunk_blocks) {
+  const int padded_blocks = (chunk_blocks + 1) & ~1;   // steps cover 2 blocks
+  return (size_t)padded_blocks * kBlock * 4 + kBlock * 4 + 16;
+}
+
+}  // namespace tg
