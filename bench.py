@@ -1,22 +1,30 @@
 #!/usr/bin/env python3
-"""Benchmark of the batch-1 trellis-coded GEMV on one MI355X.
+"""Benchmark of the trellis-coded GEMV hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies R] [--workload cfg2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
-A step is one pass of the whole hot path on one layer: input-side randomized
-Hadamard transform, trellis decode of every weight, dot products, split-K
-reduction, scale and output-side transform -- one trellis_gemv call through
-the C ABI. The default workload is the Llama-3-8B-shaped MLP down-projection
-(14336 in x 4096 out, K=3, batch 1). R seeded copies of the layer (at least
-1 GiB together, four times the 256 MB Infinity Cache) are used round-robin so
-the timed reads come from HBM. Inputs are resident in device memory before
-the timed region starts.
+A step is one pass of the whole hot path over one batch of synthetic input:
+input-side randomized Hadamard transform, trellis decode of every weight,
+dot products, split-K reduction, per-output scale and output-side transform,
+through the C ABI. Workloads (seeded, synthetic; no trained weights):
 
-Prints ONE JSON line: value = compressed-weight GB/s over the timed region
-(K steps between two synchronisations, HIP events on the launch stream), the
-roofline of the GEMV kernel (achieved / 8 TB/s, per-launch durations from
-HIP events bracketing each launch) and the CPU oracle timed on a bounded
-sample of the same layer on the host.
+  1  one 256x256 linear, K=2, batch 1
+  2  Llama-3-8B-shaped MLP down-projection 14336 -> 4096, K=3, batch 1 (default)
+  3  the seven linears of a 70B-shaped decoder layer, K=2, batch 1 (a step = 7 GEMVs)
+  4  gate projection 8192 -> 28672, K=4, 16 activation rows (MFMA path)
+  5  MoE: 128 experts (gate/up 2048->768, down 768->2048, K in {1,2,3}), top-8 per
+     token, a step = one token = 2 grouped launches
+
+Enough seeded copies of the weights (>= 1 GiB, four times the 256 MB Infinity
+Cache) are used round-robin that the timed reads come from HBM. Inputs are in
+device memory before the timed region starts.
+
+Prints ONE JSON line: value = compressed-weight GB/s over the timed region (K
+steps between two synchronisations, HIP events on the launch stream, steps
+replayed from a captured HIP graph), the roofline of the dominant kernel
+(algorithmic bytes / mean launch duration from HIP events bracketing every
+launch of an eager pass over the same steps), and the CPU oracle timed on a
+bounded sample of the same workload on the host.
 """
 from __future__ import annotations
 
@@ -26,6 +34,7 @@ import math
 import os
 import sys
 import time
+from collections import defaultdict
 
 import numpy as np
 
@@ -35,125 +44,301 @@ if ROOT not in sys.path:
 
 METRIC = "batch-1 trellis GEMV: compressed-weight HBM GB/s (% of peak) + µs/layer"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 CACHE_DEFEAT_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter-derived traffic is only reported for the kernels it was taken on."""
+    import hashlib
+    d = os.path.join(ROOT, "trellis_coded_gemv_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: int, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("csrc_sha") != kernel_source_hash():
+        return None
+    ent = rec.get("workloads", {}).get(str(workload), {}).get(kernel)
+    return None if ent is None else int(ent["hbm_bytes_per_launch"])
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(m: int, n: int, k: int, M: int = 1) -> int:
-    """Bytes the GEMV must move: codes + x (fp16) + y (fp32) + scales (fp16) + sign bits."""
+def gemv_bytes(m: int, n: int, k: int, M: int = 1) -> int:
+    """Algorithmic bytes of one layer call: codes + x (fp16) + y (fp32) + scales (fp16) + sign bits."""
     return m * n * k // 8 + 2 * n * M + 4 * m * M + 2 * m + (n + m) // 8
 
 
-def gpu_gemv_bench(m, n, k, seed, steps, warmup, copies, use_graph):
+class Launches:
+    """Runs the launches of a step; `only` restricts a pass to one kernel (for its own timing)."""
+
+    def __init__(self, only=None):
+        self.only = only
+
+    def __call__(self, name, fn):
+        if self.only is None or name == self.only:
+            fn()
+
+
+def graph_time_ms(torch, step, steps, launches):
+    """Capture `steps` steps into one HIP graph, replay it once between two events; return ms."""
+    stream = torch.cuda.current_stream()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                step(i, launches)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+# ---------------------------------------------------------------------------
+# workloads: each returns (step(i, launches), info) with device data prepared
+# ---------------------------------------------------------------------------
+
+MAX_COPIES = 64
+
+
+def _copies(total_bytes):
+    # tiny layers (the 256x256 case) cannot defeat the caches with a sane number of copies:
+    # they are latency-bound and their number is reported as such
+    return max(1, min(MAX_COPIES, math.ceil(CACHE_DEFEAT_BYTES / total_bytes)))
+
+
+def setup_linears(torch, tg, inputs, wl, dev):
+    """Workloads 1-3: batch-1 GEMVs over the workload's tensors, one call each per step."""
+    names = list(wl.tensors)
+    code_bytes = sum(m * n * k // 8 for (m, n, k) in wl.tensors.values())
+    copies = _copies(code_bytes)
+    log(f"{wl.name}: {len(names)} tensor(s), {code_bytes} code bytes per step, {copies} copies")
+    per = []
+    for c in range(copies):
+        layers = {}
+        for ti, name in enumerate(names):
+            m, n, k = wl.tensors[name]
+            L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=ti, copy=c), dev)
+            x = tg.fp16_tensor(inputs.make_x(n, wl.seed, tensor=ti, copy=c), dev)
+            y = torch.empty(m, dtype=torch.float32, device=dev)
+            layers[name] = (L, x, y)
+        per.append(layers)
+    ws = {name: tg.workspace(per[0][name][0], 1, dev) for name in names}
+
+    def step(i, launch):
+        layers = per[i % copies]
+        for name in names:
+            L, x, y = layers[name]
+            launch(name, lambda L=L, x=x, y=y, w=ws[name]: tg.trellis_gemv(L, x, y, w, torch.cuda.current_stream()))
+
+    alg = {name: gemv_bytes(*wl.tensors[name]) for name in names}
+    return step, dict(code_bytes=code_bytes, copies=copies, alg_bytes=alg, names=names,
+                      units="layer" if len(names) == 1 else "decoder layer (7 GEMVs)")
+
+
+def setup_gemm(torch, tg, inputs, wl, dev):
+    name = "gate"
+    m, n, k = wl.tensors[name]
+    M = wl.batch
+    code_bytes = m * n * k // 8
+    copies = _copies(code_bytes)
+    log(f"{wl.name}: M={M}, {code_bytes} code bytes, {copies} copies")
+    per = []
+    for c in range(copies):
+        L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=0, copy=c), dev)
+        X = tg.fp16_tensor(inputs.make_x(n, wl.seed, tensor=0, copy=c, rows=M), dev)
+        Y = torch.empty(M, m, dtype=torch.float32, device=dev)
+        per.append((L, X, Y))
+    ws = tg.workspace(per[0][0], M, dev)
+
+    def step(i, launch):
+        L, X, Y = per[i % copies]
+        launch(name, lambda: tg.trellis_gemm_small(L, X, Y, ws, torch.cuda.current_stream()))
+
+    return step, dict(code_bytes=code_bytes, copies=copies, alg_bytes={name: gemv_bytes(m, n, k, M)},
+                      names=[name], units="layer (16 rows)", flops=2.0 * m * n * M)
+
+
+def setup_moe(torch, tg, inputs, wl, dev):
+    routing = wl.routing()
+    gu_arr = [wl.layer(e, w) for e in range(wl.experts) for w in ("gate", "up")]
+    dn_arr = [wl.layer(e, "down") for e in range(wl.experts)]
+    all_bytes = sum(a.code_bytes for a in gu_arr + dn_arr)
+    copies = _copies(all_bytes)
+    log(f"{wl.name}: {all_bytes} code bytes for all experts, {copies} copies, {wl.tokens} tokens")
+    tables = []
+    for c in range(copies):
+        gu = [tg.DeviceLayer(wl.layer(e, w, copy=c), dev) for e in range(wl.experts) for w in ("gate", "up")]
+        dn = [tg.DeviceLayer(wl.layer(e, "down", copy=c), dev) for e in range(wl.experts)]
+        tables.append((tg.LayerTable(gu, dev), tg.LayerTable(dn, dev)))
+    sel_gu = [torch.tensor([2 * int(e) + w for e in routing[t] for w in (0, 1)], dtype=torch.int32, device=dev)
+              for t in range(wl.tokens)]
+    sel_dn = [torch.tensor([int(e) for e in routing[t]], dtype=torch.int32, device=dev) for t in range(wl.tokens)]
+    xs = [tg.fp16_tensor(inputs.make_x(wl.hidden, wl.seed, tensor=10_000 + t), dev) for t in range(wl.tokens)]
+    xds = [tg.fp16_tensor(inputs.make_x(wl.inter, wl.seed, tensor=20_000 + t, rows=wl.top_k), dev)
+           for t in range(wl.tokens)]
+    Y1 = torch.empty(2 * wl.top_k, wl.inter, dtype=torch.float32, device=dev)
+    Y2 = torch.empty(wl.top_k, wl.hidden, dtype=torch.float32, device=dev)
+    ws1 = tg.grouped_workspace(tables[0][0], 2 * wl.top_k, dev)
+    ws2 = tg.grouped_workspace(tables[0][1], wl.top_k, dev)
+    tok_bytes = [sum(gu_arr[2 * int(e) + w].code_bytes for e in routing[t] for w in (0, 1)) +
+                 sum(dn_arr[int(e)].code_bytes for e in routing[t]) for t in range(wl.tokens)]
+
+    def step(i, launch):
+        t = i % wl.tokens
+        gu_t, dn_t = tables[(i // wl.tokens) % copies]
+        s = torch.cuda.current_stream()
+        launch("gate_up", lambda: tg.trellis_gemv_grouped(gu_t, sel_gu[t], xs[t], 0, Y1, wl.inter, ws1, s))
+        launch("down", lambda: tg.trellis_gemv_grouped(dn_t, sel_dn[t], xds[t], wl.inter, Y2, wl.hidden, ws2, s))
+
+    mean_tok = float(np.mean(tok_bytes))
+    alg = {"gate_up": mean_tok * 2 / 3 + 2 * wl.hidden + 16 * 6 * wl.inter,
+           "down": mean_tok / 3 + 8 * 2 * wl.inter + 8 * 6 * wl.hidden}
+    return step, dict(code_bytes=mean_tok, copies=copies, alg_bytes=alg, names=["gate_up", "down"],
+                      units="token (24 GEMVs, 2 launches)")
+
+
+def run_gpu(workload, steps, warmup, use_graph):
+    """Time `steps` steps of the workload. Returns (info, timings).
+
+    region_ms: the timed region (all launches of K steps, graph replay unless disabled).
+    dom_ms: the dominant kernel alone -- the same K steps restricted to its launches,
+            replayed back to back -- i.e. K times its mean launch duration.
+    """
     import torch
     from trellis_coded_gemv_amd import binding as tg
     from trellis_coded_gemv_amd import inputs
 
     dev = "cuda"
-    code_bytes = m * n * k // 8
-    if copies <= 0:
-        copies = max(1, math.ceil(CACHE_DEFEAT_BYTES / code_bytes))
-    log(f"layer {m}x{n} K={k}: {code_bytes} code bytes, {copies} copies")
-    layers, xs = [], []
-    for c in range(copies):
-        layers.append(tg.DeviceLayer(inputs.make_layer(m, n, k, seed, tensor=0, copy=c), dev))
-        xs.append(tg.fp16_tensor(inputs.make_x(n, seed, tensor=0, copy=c), dev))
-    ys = [torch.empty(m, dtype=torch.float32, device=dev) for _ in range(copies)]
-    ws = tg.workspace(layers[0], 1, dev)
+    wl = inputs.WORKLOADS[workload]
+    setup = {1: setup_linears, 2: setup_linears, 3: setup_linears, 4: setup_gemm, 5: setup_moe}[workload]
+    step, info = setup(torch, tg, inputs, wl, dev)
+    dom = max(info["names"], key=lambda k: info["alg_bytes"][k])     # kernel moving the most bytes
     stream = torch.cuda.current_stream()
-
-    def step(i):
-        c = i % copies
-        tg.trellis_gemv(layers[c], xs[c], ys[c], ws, stream)
-
     for i in range(warmup):
-        step(i)
+        step(i, Launches())
     torch.cuda.synchronize()
 
-    # per-launch kernel durations: events bracketing each launch on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
+        step(i, Launches())
     t1.record(stream)
     torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    eager_region_ms = t0.elapsed_time(t1)
+    eager_ms = t0.elapsed_time(t1)
 
-    region_ms = eager_region_ms
-    graph_ms = None
+    region_ms, dom_ms, timing = eager_ms, None, "eager launches"
     if use_graph:
-        # the same K steps captured once and replayed: removes host launch gaps from the region
         try:
-            g = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream()
-            s.wait_stream(stream)
-            with torch.cuda.stream(s):
-                with torch.cuda.graph(g, stream=s):
-                    for i in range(steps):
-                        c = i % copies
-                        tg.trellis_gemv(layers[c], xs[c], ys[c], ws, torch.cuda.current_stream())
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            g.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            graph_ms = a.elapsed_time(b)
-            region_ms = graph_ms
-        except Exception as e:  # noqa: BLE001 - report and keep the eager number
+            region_ms = graph_time_ms(torch, step, steps, Launches())
+            dom_ms = graph_time_ms(torch, step, steps, Launches(only=dom))
+            timing = "graph replay"
+        except Exception as e:  # noqa: BLE001 - keep the eager number
             log("graph replay unavailable:", repr(e))
+    if dom_ms is None:
+        t0.record(stream)
+        for i in range(steps):
+            step(i, Launches(only=dom))
+        t1.record(stream)
+        torch.cuda.synchronize()
+        dom_ms = t0.elapsed_time(t1)
+    return info, dict(region_ms=region_ms, eager_ms=eager_ms, dom=dom, dom_ms=dom_ms, timing=timing)
 
-    # spot-check copy 0 against the oracle after timing (sampled outputs)
+
+def parity_spot_check(workload):
+    """Copy 0 of the workload against the oracle on sampled outputs (after timing)."""
+    import torch
     from oracle import gemv as ogemv
-    arr0 = inputs.make_layer(m, n, k, seed, tensor=0, copy=0)
-    x0 = inputs.make_x(n, seed, tensor=0, copy=0)
-    tg.trellis_gemv(layers[0], xs[0], ys[0], ws, stream)
+    from trellis_coded_gemv_amd import binding as tg
+    from trellis_coded_gemv_amd import inputs
+
+    wl = inputs.WORKLOADS[workload]
+    if workload == 5:
+        e, which = int(wl.routing()[0][0]), "gate"
+        arr, x = wl.layer(e, which), inputs.make_x(wl.hidden, wl.seed, tensor=10_000)
+        rows, M = np.arange(0, wl.inter, 5), 1
+    else:
+        name = list(wl.tensors)[-1]
+        m, n, k = wl.tensors[name]
+        ti = list(wl.tensors).index(name)
+        arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti)
+        M = wl.batch
+        x = inputs.make_x(n, wl.seed, tensor=ti, rows=M)
+        rows = np.concatenate([np.arange(0, 128, 7), np.arange(m - 128, m, 11)])
+    L = tg.DeviceLayer(arr, "cuda")
+    if M == 1:
+        y = tg.trellis_gemv(L, tg.fp16_tensor(x, "cuda"))[None, :]
+        ref = ogemv.gemv_rows(arr, x, rows)[None, :]
+    else:
+        y = tg.trellis_gemm_small(L, tg.fp16_tensor(x, "cuda"))
+        ref = ogemv.gemm_rows(arr, x[:2], rows)
     torch.cuda.synchronize()
-    rows = np.concatenate([np.arange(0, 128, 7), np.arange(m - 128, m, 11)])
-    ref = ogemv.gemv_rows(arr0, x0, rows)
-    err = float(np.abs(ys[0].cpu().numpy()[rows] - ref).max() / np.abs(ref).max())
-    return dict(code_bytes=code_bytes, copies=copies, launch_ms=launch_ms, eager_region_ms=eager_region_ms,
-                graph_region_ms=graph_ms, region_ms=region_ms, parity_rel_err=err)
+    y = y.cpu().numpy()[: ref.shape[0], rows]
+    return float(np.abs(y - ref).max() / np.abs(ref).max())
 
 
-def cpu_baseline(m, n, k, seed, sample_blocks):
-    """The oracle, untuned, on `sample_blocks` 128-output blocks of the same layer; scaled to the whole layer."""
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+def cpu_baseline(workload, sample_blocks):
+    """The oracle, untuned, on a bounded sample of the workload, scaled to the same unit (GB/s of codes)."""
+    from threadpoolctl import threadpool_limits
     from oracle import gemv as ogemv
     from trellis_coded_gemv_amd import inputs
 
-    arr = inputs.make_layer(m, n, k, seed)
-    x = inputs.make_x(n, seed)
-    nb = m // 128
-    blocks = np.linspace(0, nb - 1, min(sample_blocks, nb)).astype(int)
-    rows = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    t = time.perf_counter()
-    if ctx:
-        with ctx:
-            ogemv.gemv_rows(arr, x, rows)
+    wl = inputs.WORKLOADS[workload]
+    if workload == 5:
+        arrs = [wl.layer(int(e), w) for e in wl.routing()[0][:2] for w in ("gate", "up", "down")]
+        xs = [inputs.make_x(a.n, 1) for a in arrs]
+        with threadpool_limits(limits=1):
+            t = time.perf_counter()
+            for a, x in zip(arrs, xs):
+                ogemv.gemv(a, x)
+            dt = time.perf_counter() - t
+        nbytes = sum(a.code_bytes for a in arrs)
+        sample = f"gate/up/down of 2 experts (6 full GEMVs, {nbytes} code bytes), {dt:.1f} s"
+        rate = nbytes / dt
     else:
-        ogemv.gemv_rows(arr, x, rows)
-    dt = time.perf_counter() - t
-    full_s = dt * nb / len(blocks)
-    return {"value": round(m * n * k / 8 / full_s / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(blocks)} of {nb} 128-output blocks of the {m}x{n} K={k} layer "
-                      f"(decode + fp64 GEMV), {dt:.1f} s, scaled to the whole layer: {full_s * 1e6:.0f} us/layer",
-            "us_per_layer": round(full_s * 1e6, 1)}
+        name = max(wl.tensors, key=lambda k: wl.tensors[k][0] * wl.tensors[k][1])
+        m, n, k = wl.tensors[name]
+        ti = list(wl.tensors).index(name)
+        arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti)
+        M = wl.batch
+        X = inputs.make_x(n, wl.seed, tensor=ti, rows=M)
+        nb = m // 128
+        nblk = max(1, sample_blocks // M)
+        blocks = np.linspace(0, nb - 1, min(nblk, nb)).astype(int)
+        rows = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
+        with threadpool_limits(limits=1):
+            for _ in range(2):                 # the second (warm) pass is the one reported
+                t = time.perf_counter()
+                if M == 1:
+                    ogemv.gemv_rows(arr, X, rows)
+                else:
+                    ogemv.gemm_rows(arr, X, rows)
+                dt = time.perf_counter() - t
+        nbytes = len(rows) * n * k // 8
+        sample = (f"{len(blocks)} of {nb} 128-output blocks of the {m}x{n} K={k} '{name}' tensor"
+                  f"{'' if M == 1 else f' x {M} rows'} (decode + fp64 GEMV), {dt:.1f} s")
+        rate = nbytes / dt
+    return {"value": round(rate / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}
 
 
 def main(argv=None):
@@ -161,9 +346,11 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--copies", type=int, default=0, help="rotating layer copies (0: enough for 1 GiB)")
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=16, help="oracle sample size in 128-output blocks (0: skip)")
+    ap.add_argument("--cpu-blocks", type=int, default=32, help="oracle sample size in 128-output blocks (0: skip)")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="after timing, write (fill) and read (sum) this many MiB (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -171,31 +358,47 @@ def main(argv=None):
         return 2
 
     from trellis_coded_gemv_amd import inputs
-    wl = inputs.CFG2
-    m, n, k = wl.tensors["down"]
-    r = gpu_gemv_bench(m, n, k, wl.seed, args.steps, args.warmup, args.copies, not args.no_graph)
+    wl = inputs.WORKLOADS[args.workload]
+    info, t = run_gpu(args.workload, args.steps, args.warmup, not args.no_graph)
     steps = args.steps
-    ms_per_step = r["region_ms"] / steps
-    value = r["code_bytes"] / (ms_per_step * 1e-3) / 1e9
-    avg_launch_ms = float(np.mean(r["launch_ms"]))
-    alg = algorithmic_bytes(m, n, k)
-    achieved = alg / (avg_launch_ms * 1e-3) / 1e9
+    ms_per_step = t["region_ms"] / steps
+    value = info["code_bytes"] / (ms_per_step * 1e-3) / 1e9
+    dom = t["dom"]
+    dom_launch_ms = t["dom_ms"] / steps
+    achieved = info["alg_bytes"][dom] / (dom_launch_ms * 1e-3) / 1e9
+    config = {"workload": wl.name, "units": info["units"], "code_bytes_per_step": int(info["code_bytes"]),
+              "copies": info["copies"], "us_per_step": round(ms_per_step * 1e3, 3),
+              "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
+              "eager_us_per_step": round(t["eager_ms"] / steps * 1e3, 3),
+              "parity_max_rel_err": parity_spot_check(args.workload)}
+    if args.workload != 5:
+        config.update({"tensors": {k: list(v) for k, v in wl.tensors.items()}, "batch": wl.batch})
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": wl.name, "m": m, "n": n, "k_bits": k, "batch": 1, "code_bytes": r["code_bytes"],
-                   "copies": r["copies"], "us_per_layer": round(ms_per_step * 1e3, 3),
-                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "timing": "graph replay" if r["graph_region_ms"] is not None else "eager launches",
-                   "eager_us_per_layer": round(r["eager_region_ms"] / steps * 1e3, 3),
-                   "parity_max_rel_err": r["parity_rel_err"]},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_us": round(avg_launch_ms * 1e3, 3), "algorithmic_bytes": alg},
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic", "config": config,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.workload, dom),
+                     "algorithmic_bytes": int(info["alg_bytes"][dom]),
+                     "launch_us": round(dom_launch_ms * 1e3, 3)},
     }
+    if "flops" in info:
+        tf = info["flops"] / (dom_launch_ms * 1e-3) / 1e12
+        out["roofline"]["mfma"] = {"achieved_tflops": round(tf, 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                                   "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 5)}
+    if args.copy_calib_mb > 0:
+        # counter calibration: a pure write (fill) and a pure read (sum) of known size
+        import torch
+        buf = torch.empty(args.copy_calib_mb << 18, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            buf.fill_(1.0)
+            buf.sum()
+        torch.cuda.synchronize()
+        out["config"]["calibration_bytes"] = buf.numel() * 4
     if args.cpu_blocks > 0:
-        out["cpu_baseline"] = cpu_baseline(m, n, k, wl.seed, args.cpu_blocks)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_blocks)
+    out["config"]["csrc_sha"] = kernel_source_hash()
     print(json.dumps(out), flush=True)
     return 0
 

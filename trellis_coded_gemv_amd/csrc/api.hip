@@ -42,17 +42,27 @@ int32_t check_layer(const tg_layer* L) {
   return TG_OK;
 }
 
-// Number of input chunks (split-K) for a batch-1 GEMV: enough workgroups to
-// fill 256 CUs several times over, at least one whole 16-tile step per wave,
-// and a chunk that fits the LDS budget. TG_SPLITK overrides (tuning aid).
+// Number of input chunks (split-K) for a batch-1 GEMV. About 256 workgroups
+// (one 128-output block x one chunk each) measured best on 256 CUs for every
+// workload shape; chunks are kept equal and a whole number of 16-tile steps
+// (two 128-blocks), since a half step costs the decode work of a full one.
+// The chunk also has to fit the LDS budget. TG_SPLITK overrides (tuning aid).
+int split_for_target(int nb, int target) {
+  const int steps = nb / 2;                      // whole steps along the input
+  if (steps < 1) return 1;
+  int best = 1;
+  for (int s = 1; s <= steps; ++s) {
+    if (steps % s) continue;
+    const int d = abs(s - target), bd = abs(best - target);
+    if (d < bd || (d == bd && s > best)) best = s;
+  }
+  return best;
+}
+
 int gemv_splits(int m, int n) {
   const int ob = m / kBlock, nb = n / kBlock;
   int s = env_int("TG_SPLITK");
-  if (s <= 0) {
-    const int target_wg = 1024;
-    s = (target_wg + ob - 1) / ob;
-    s = s < (nb / 2 > 0 ? nb / 2 : 1) ? s : (nb / 2 > 0 ? nb / 2 : 1);
-  }
+  if (s <= 0) s = split_for_target(nb, (256 + ob / 2) / ob);
   const int min_s = (nb + kMaxChunkBlocks - 1) / kMaxChunkBlocks;
   if (s < min_s) s = min_s;
   if (s > nb) s = nb;
@@ -122,11 +132,7 @@ int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel
   }
   const int max_ob = max_m / kBlock, max_nb = max_n / kBlock;
   int s = env_int("TG_SPLITK");
-  if (s <= 0) {
-    s = (1024 + n_sel * max_ob - 1) / (n_sel * max_ob);
-    const int cap = max_nb / 2 > 0 ? max_nb / 2 : 1;
-    if (s > cap) s = cap;
-  }
+  if (s <= 0) s = split_for_target(max_nb, (256 + n_sel * max_ob / 2) / (n_sel * max_ob));
   const int min_s = (max_nb + kMaxChunkBlocks - 1) / kMaxChunkBlocks;
   if (s < min_s) s = min_s;
   if (s > max_nb) s = max_nb;

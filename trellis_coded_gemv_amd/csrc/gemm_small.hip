@@ -197,7 +197,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
   if (!arrive_is_last(&a.counters[ob], (uint32_t)a.splits, flag)) return;
   for (int r = wave; r < a.M; r += kGemvWaves) {
     float v0 = 0.f, v1 = 0.f;
-    for (int t = 0; t < a.splits; ++t) {
+#pragma unroll 8
+    for (int t = 0; t < a.splits; ++t) {   // unrolled so the loads are in flight together
       const float* pp = a.partials + ((size_t)t * a.M + r) * a.m + ob * kBlock;
       v0 += load_partial(pp + lane);
       v1 += load_partial(pp + lane + 64);

@@ -35,8 +35,16 @@
 namespace tg {
 
 // Prefetch depth in steps (each step is 8K bytes per lane).
+// Prefetch depth in steps. Kept even so the x~ double buffer alternates
+// statically inside the unrolled loop.
+#ifndef TG_GEMV_PF_SMALL_K
+#define TG_GEMV_PF_SMALL_K 2
+#endif
+#ifndef TG_GEMV_XDB
+#define TG_GEMV_XDB 0   // double-buffer x~ across steps
+#endif
 template <int K>
-constexpr int gemv_pf() { return K <= 2 ? 4 : (K <= 4 ? 3 : 2); }
+constexpr int gemv_pf() { return K <= 4 ? TG_GEMV_PF_SMALL_K : 2; }
 
 // Load this lane's 2K words (8K bytes) of the current step.
 template <int K>
@@ -90,24 +98,61 @@ __device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32
   }
 }
 
-template <int K, bool ROUND, int PF>
+// Sum acc[g] over the 16 tile slots of the wave (lane bits 2..5) with a
+// transposing reduction: the exchanges over bits 2 and 3 each halve the number
+// of values a lane carries, so 5 shuffles replace 16. On return lanes 0..15
+// hold the total of tile row 4*(l&3) + 2*((l>>2)&1) + ((l>>3)&1).
+__device__ __forceinline__ float reduce_slots(const float (&acc)[4], int lane) {
+  const bool b0 = (lane & 4) != 0, b1 = (lane & 8) != 0;
+  const float s0 = b0 ? acc[0] : acc[2], s1 = b0 ? acc[1] : acc[3];
+  const float c0 = (b0 ? acc[2] : acc[0]) + shfl_xor(s0, 4);
+  const float c1 = (b0 ? acc[3] : acc[1]) + shfl_xor(s1, 4);
+  float d = (b1 ? c1 : c0) + shfl_xor(b1 ? c0 : c1, 8);
+  d += shfl_xor(d, 16);
+  d += shfl_xor(d, 32);
+  return d;
+}
+
+__device__ __forceinline__ int reduced_row(int lane) {
+  return 4 * (lane & 3) + 2 * ((lane >> 2) & 1) + ((lane >> 3) & 1);
+}
+
+__device__ __forceinline__ void read_xx(const uint32_t* xx_lds, int tile, uint32_t (&xv)[16]) {
+  const u32x4* xs = reinterpret_cast<const u32x4*>(xx_lds + tile * 16);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const u32x4 t = xs[v];
+    xv[4 * v + 0] = t[0];
+    xv[4 * v + 1] = t[1];
+    xv[4 * v + 2] = t[2];
+    xv[4 * v + 3] = t[3];
+  }
+}
+
+// One workgroup = 8 tile rows (a 128-output block) x one input chunk, with P
+// waves per tile row that take interleaved 16-tile steps of the chunk.
+template <int K, bool ROUND, int PF, int P>
 __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int split, uint32_t* lds) {
   constexpr int NW = 2 * K;
+  constexpr int WAVES = 8 * P;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rw = wave & 7, kp = wave >> 3;     // tile row within the block, step phase
   const int nb128 = a.n >> 7;
   const int blk0 = (int)((int64_t)split * nb128 / a.splits);
   const int blk1 = (int)((int64_t)(split + 1) * nb128 / a.splits);
   const int cb = blk1 - blk0;             // 128-blocks in this chunk
   const int ntiles = cb * 8;              // tiles of the chunk in one tile row
   const int nsteps = (cb + 1) >> 1;       // 16 tiles per step
+  const int nls = nsteps > kp ? (nsteps - kp + P - 1) / P : 0;   // this wave's steps: kp, kp+P, ...
   const int jslot = lane >> 2;
-  const int R = ob * 8 + wave;
+  const int R = ob * 8 + rw;
   const uint32_t* __restrict__ rowp =
       a.codes + ((size_t)R * (size_t)(a.n >> 4) + (size_t)blk0 * 8) * (size_t)(8 * K) + (size_t)lane * NW;
 
   uint32_t* xx_lds = lds;                                        // [2*nsteps blocks][128] pairs
   float* ybuf = reinterpret_cast<float*>(lds + nsteps * 256);    // [128]
-  uint32_t* flag = lds + nsteps * 256 + 128;
+  float* red = ybuf + 128;                                       // [P-1][128]
+  uint32_t* flag = lds + nsteps * 256 + 128 * P;
 
   // The first input block of this wave is fetched before the code prefetch:
   // loads complete in order, so fetching it later would make the transform
@@ -120,15 +165,16 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   // through the loop issues the same loads and the waits stay exact.
   uint32_t buf[PF][NW];
   const uint32_t* __restrict__ dummy = a.codes;
-  auto issue = [&](int st, uint32_t(&dst)[NW]) {
-    const bool ok = st < nsteps && st * 16 + jslot < ntiles;
+  auto issue = [&](int ls, uint32_t(&dst)[NW]) {
+    const int st = kp + ls * P;
+    const bool ok = ls < nls && st * 16 + jslot < ntiles;
     load_lane_words<K>(ok ? rowp + (size_t)st * (128 * K) : dummy, dst);
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, buf[p]);
 
   // Prologue: x~ for the chunk, padded with zeros to whole steps.
-  for (int bb = wave; bb < 2 * nsteps; bb += kGemvWaves) {
+  for (int bb = wave; bb < 2 * nsteps; bb += WAVES) {
     uint32_t d0 = 0u, d1 = 0u;
     if (bb < cb) {
       const XBlock xb = bb == wave ? xfirst : load_x_block(a.x, a.sign_in, (blk0 + bb) * kBlock, lane);
@@ -141,63 +187,72 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const CodeRegs cr;
-  for (int st0 = 0; st0 < nsteps; st0 += PF) {
+  // x~ of the current and the next step (double buffer, alternating with p).
+  uint32_t xv[1 + TG_GEMV_XDB][16];
+  if (TG_GEMV_XDB && nls > 0) read_xx(xx_lds, kp * 16 + jslot, xv[0]);
+  for (int ls0 = 0; ls0 < nls; ls0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int st = st0 + p;
-      uint32_t w[NW];
-#pragma unroll
-      for (int i = 0; i < NW; ++i) w[i] = buf[p][i];
-      issue(st + PF, buf[p]);
-      if (st < nsteps) {
-        uint32_t xv[16];
-        const u32x4* xs = reinterpret_cast<const u32x4*>(xx_lds + (st * 16 + jslot) * 16);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const u32x4 t = xs[v];
-          xv[4 * v + 0] = t[0];
-          xv[4 * v + 1] = t[1];
-          xv[4 * v + 2] = t[2];
-          xv[4 * v + 3] = t[3];
+      const int ls = ls0 + p;
+      if (ls < nls) {
+        if constexpr (TG_GEMV_XDB) {
+          const int nxt = ls + 1 < nls ? kp + (ls + 1) * P : kp + ls * P;
+          read_xx(xx_lds, nxt * 16 + jslot, xv[(p + 1) & TG_GEMV_XDB]);   // in flight during this step
+        } else {
+          read_xx(xx_lds, (kp + ls * P) * 16 + jslot, xv[0]);
         }
-        const uint32_t nbw = quad_rotate_next(w[0]);
-        decode_dot_64<K, ROUND>(w, nbw, xv, acc, cr);
+        const uint32_t nbw = quad_rotate_next(buf[p][0]);
+        decode_dot_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
       }
+      issue(ls + PF, buf[p]);   // refill after use: the ring needs no register copies
     }
   }
 
-  // Sum the 16 tile slots (lane bits 2..5); every lane ends with its rows' totals.
+  float d = reduce_slots(acc, lane);
+  const int orow = rw * 16 + reduced_row(lane);   // output within the 128-block (lanes 0..15)
+  if constexpr (P > 1) {
+    if (kp > 0 && lane < 16) red[(kp - 1) * kBlock + orow] = d;
+    __syncthreads();
+    if (kp == 0) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-#pragma unroll
-    for (int mask = 4; mask <= 32; mask <<= 1) acc[g] += shfl_xor(acc[g], mask);
+      for (int t = 1; t < P; ++t) d += red[(t - 1) * kBlock + orow];
+    }
   }
-  const int orow = wave * 16 + (lane & 3) * 4;   // output within the 128-block
 
   if (a.splits == 1) {
-    if (lane < 4) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) ybuf[orow + g] = acc[g];
-    }
+    if (kp == 0 && lane < 16) ybuf[orow] = d;
     __syncthreads();
     if (wave == 0) rht_out_block(ybuf[lane], ybuf[lane + 64], a.scales, a.sign_out, a.y, ob * kBlock, lane);
     return;
   }
 
-  if (lane < 4) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) store_partial(a.partials + (size_t)split * a.m + ob * kBlock + orow + g, acc[g]);
-  }
+  if (kp == 0 && lane < 16) store_partial(a.partials + (size_t)split * a.m + ob * kBlock + orow, d);
   if (!arrive_is_last(&a.counters[ob], (uint32_t)a.splits, flag)) return;
-  if (wave == 0) {
+  // Last arrival: the waves load the splits' partials in parallel (wave w takes
+  // splits w, w+WAVES, ...), then wave 0 adds the per-wave sums in a fixed order.
+  {
     float v0 = 0.f, v1 = 0.f;
     const float* pp = a.partials + ob * kBlock;
-    for (int t = 0; t < a.splits; ++t) {
+    for (int t = wave; t < a.splits; t += WAVES) {
       v0 += load_partial(pp + (size_t)t * a.m + lane);
       v1 += load_partial(pp + (size_t)t * a.m + lane + 64);
     }
-    rht_out_block(v0, v1, a.scales, a.sign_out, a.y, ob * kBlock, lane);
-    if (lane == 0) reset_counter(&a.counters[ob]);
+    float* wsum = reinterpret_cast<float*>(xx_lds);   // reuse x~ storage: [WAVES][128]
+    __syncthreads();
+    wsum[wave * kBlock + lane] = v0;
+    wsum[wave * kBlock + lane + 64] = v1;
+    __syncthreads();
+    if (wave == 0) {
+      v0 = 0.f;
+      v1 = 0.f;
+      const int nw = a.splits < WAVES ? a.splits : WAVES;
+      for (int w = 0; w < nw; ++w) {
+        v0 += wsum[w * kBlock + lane];
+        v1 += wsum[w * kBlock + lane + 64];
+      }
+      rht_out_block(v0, v1, a.scales, a.sign_out, a.y, ob * kBlock, lane);
+      if (lane == 0) reset_counter(&a.counters[ob]);
+    }
   }
 }
 
@@ -207,16 +262,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return (nblk & 7) == 0 ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
 }
 
-template <int K, bool ROUND, int PF>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
+template <int K, bool ROUND, int PF, int P>
+__global__ __launch_bounds__(64 * 8 * P) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int ob = bid / a.splits;
-  gemv_workgroup<K, ROUND, PF>(a, ob, bid - ob * a.splits, lds);
+  gemv_workgroup<K, ROUND, PF, P>(a, ob, bid - ob * a.splits, lds);
 }
 
 template <bool ROUND>
-__global__ __launch_bounds__(kGemvThreads) void grouped_kernel(GroupedArgs g, int max_ob) {
+__global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g, int max_ob) {
   extern __shared__ uint32_t lds[];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_sel = max_ob * g.splits;
@@ -240,14 +295,14 @@ __global__ __launch_bounds__(kGemvThreads) void grouped_kernel(GroupedArgs g, in
   a.n = L.n;
   a.splits = g.splits;
   switch (L.k_bits) {
-    case 1: gemv_workgroup<1, ROUND, gemv_pf<1>()>(a, ob, split, lds); break;
-    case 2: gemv_workgroup<2, ROUND, gemv_pf<2>()>(a, ob, split, lds); break;
-    case 3: gemv_workgroup<3, ROUND, gemv_pf<3>()>(a, ob, split, lds); break;
-    case 4: gemv_workgroup<4, ROUND, gemv_pf<4>()>(a, ob, split, lds); break;
-    case 5: gemv_workgroup<5, ROUND, gemv_pf<5>()>(a, ob, split, lds); break;
-    case 6: gemv_workgroup<6, ROUND, gemv_pf<6>()>(a, ob, split, lds); break;
-    case 7: gemv_workgroup<7, ROUND, gemv_pf<7>()>(a, ob, split, lds); break;
-    default: gemv_workgroup<8, ROUND, gemv_pf<8>()>(a, ob, split, lds); break;
+    case 1: gemv_workgroup<1, ROUND, gemv_pf<1>(), kGemvP>(a, ob, split, lds); break;
+    case 2: gemv_workgroup<2, ROUND, gemv_pf<2>(), kGemvP>(a, ob, split, lds); break;
+    case 3: gemv_workgroup<3, ROUND, gemv_pf<3>(), kGemvP>(a, ob, split, lds); break;
+    case 4: gemv_workgroup<4, ROUND, gemv_pf<4>(), kGemvP>(a, ob, split, lds); break;
+    case 5: gemv_workgroup<5, ROUND, gemv_pf<5>(), kGemvP>(a, ob, split, lds); break;
+    case 6: gemv_workgroup<6, ROUND, gemv_pf<6>(), kGemvP>(a, ob, split, lds); break;
+    case 7: gemv_workgroup<7, ROUND, gemv_pf<7>(), kGemvP>(a, ob, split, lds); break;
+    default: gemv_workgroup<8, ROUND, gemv_pf<8>(), kGemvP>(a, ob, split, lds); break;
   }
 }
 
@@ -257,7 +312,8 @@ static hipError_t launch_k(const GemvArgs& a, hipStream_t s) {
   const int nb128 = a.n >> 7;
   const int max_chunk = (nb128 + a.splits - 1) / a.splits;
   const int grid = (a.m >> 7) * a.splits;
-  hipLaunchKernelGGL((gemv_kernel<K, ROUND, PF>), dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(max_chunk), s, a);
+  hipLaunchKernelGGL((gemv_kernel<K, ROUND, PF, kGemvP>), dim3(grid), dim3(64 * 8 * kGemvP),
+                     gemv_lds_bytes(max_chunk), s, a);
   return hipGetLastError();
 }
 
@@ -276,9 +332,11 @@ hipError_t launch_grouped(const GroupedArgs& g, int max_ob, int max_n, hipStream
   if (grid == 0) return hipSuccess;
   const int max_chunk = ((max_n >> 7) + g.splits - 1) / g.splits;
   if (g.round_weights)
-    hipLaunchKernelGGL(grouped_kernel<true>, dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(max_chunk), s, g, max_ob);
+    hipLaunchKernelGGL(grouped_kernel<true>, dim3(grid), dim3(64 * 8 * kGemvP), gemv_lds_bytes(max_chunk), s, g,
+                       max_ob);
   else
-    hipLaunchKernelGGL(grouped_kernel<false>, dim3(grid), dim3(kGemvThreads), gemv_lds_bytes(max_chunk), s, g, max_ob);
+    hipLaunchKernelGGL(grouped_kernel<false>, dim3(grid), dim3(64 * 8 * kGemvP), gemv_lds_bytes(max_chunk), s, g,
+                       max_ob);
   return hipGetLastError();
 }
 

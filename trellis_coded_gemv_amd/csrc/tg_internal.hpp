@@ -9,8 +9,12 @@ namespace tg {
 
 constexpr int kTile = 16;
 constexpr int kBlock = 128;              // Hadamard block; 8 tile rows / 8 tile columns
-constexpr int kGemvWaves = 8;            // one wave per tile row of a 128-output block
+constexpr int kGemvWaves = 8;            // one wave per tile row of a 128-output block (MFMA path)
 constexpr int kGemvThreads = 64 * kGemvWaves;
+#ifndef TG_GEMV_P
+#define TG_GEMV_P 1
+#endif
+constexpr int kGemvP = TG_GEMV_P;        // batch-1 path: waves per tile row (interleaved steps)
 constexpr int kMaxChunkBlocks = 64;      // 128-blocks of x~ held in LDS by one GEMV workgroup
 
 // One batch-1 GEMV as a workgroup sees it.
@@ -71,9 +75,11 @@ hipError_t launch_decode(const uint32_t* codes, uint16_t* out, int m, int n, int
 hipError_t launch_code_table(uint16_t* out, hipStream_t s);
 
 // LDS bytes a GEMV workgroup needs for a chunk of `chunk_blocks` 128-blocks.
+// The x~ region doubles as [8P][128] fp32 per-wave sums in the final reduction.
 inline size_t gemv_lds_bytes(int chunk_blocks) {
-  const int padded_blocks = (chunk_blocks + 1) & ~1;   // steps cover 2 blocks
-  return (size_t)padded_blocks * kBlock * 4 + kBlock * 4 + 16;
+  int padded_blocks = (chunk_blocks + 1) & ~1;   // steps cover 2 blocks
+  if (padded_blocks < 8 * kGemvP) padded_blocks = 8 * kGemvP;
+  return (size_t)padded_blocks * kBlock * 4 + (size_t)kBlock * 4 * kGemvP + 16;
 }
 
 }  // namespace tg
