@@ -71,15 +71,14 @@ int gemv_splits(int m, int n) {
 }
 
 // Splits of the small-batch path: the fp32 partials cost 8*S*M*m bytes of
-// traffic against m*n*K/8 code bytes, so keep S small; sub-chunks are 128
-// (M <= 32) or 64 inputs.
+// traffic against m*n*K/8 code bytes, so keep S small; a chunk keeps at
+// least 8 tile columns (one per wave).
 int gemm_splits(int m, int n, int M, int k_bits) {
   const int ob = m / kBlock;
-  const int mpad = (M + 15) / 16 * 16;
-  const int nsub = n / (mpad <= 32 ? 128 : 64);
+  const int nsub = n / kBlock;
   int s = env_int("TG_SPLITK_MFMA");
   if (s <= 0) {
-    s = (512 + ob - 1) / ob;
+    s = (256 + ob / 2) / ob;                                     // about 256 workgroups
     const int cap = (int)((int64_t)n * k_bits / (1024 * M));   // partial traffic <= 1/16 of the code bytes
     if (s > cap) s = cap;
   }

@@ -19,13 +19,20 @@
 // loop-invariant shift over two (three for K >= 6) loaded words -- then
 // v_bfe + v_mad_u32_u24 + v_and_or_b32 per weight.
 //
-// Decomposition: a workgroup of 8 waves owns one 128-output block (a wave per
-// tile row) and a chunk of the input; x~ rows (prepared once per call by
-// xt_prep_kernel, already transformed) are staged through double-buffered LDS
-// a sub-chunk at a time and shared by the 8 waves. Split-K partials and the
+// Decomposition: a workgroup of 8 waves owns one 128-output block and a chunk
+// of the input's tile columns; every wave covers all 8 tile rows of the block
+// for every 8th column of the chunk, so the MFMA accumulators of a wave stay
+// put for the whole loop and the x~ operand of a column (prepared once per
+// call by xt_prep_kernel, read from L2) is loaded once for 8 tiles. The 8
+// waves are summed through LDS at the end; split-K partials and the
 // last-arriving-workgroup epilogue are as in the batch-1 kernel.
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
+
+// Tiles whose B operands are decoded before their MFMAs are issued.
+#ifndef TG_MFMA_GROUP
+#define TG_MFMA_GROUP 4
+#endif
 
 namespace tg {
 
@@ -41,39 +48,48 @@ __global__ __launch_bounds__(64) void xt_prep_kernel(const uint16_t* __restrict_
   xt[ob + lane + 64] = d1;
 }
 
-template <int SUB>   // tiles per LDS sub-chunk
-struct GemmLds {
-  static constexpr int kCols = SUB * 16;       // inputs per sub-chunk
-  static constexpr int kStride = kCols + 4;    // padded row stride in words (bank spread)
-};
+// Per-lane code words of one tile column step: lane l holds K words of tile
+// l/8 of the column (tile rows R0..R0+7), starting at word (l%8)*K.
+template <int K>
+__device__ __forceinline__ void load_column(const uint32_t* __restrict__ p, uint32_t (&w)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) w[i] = __builtin_nontemporal_load(p + i);
+}
 
-template <int K, bool ROUND, int MB, int SUB>
-__global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
-  extern __shared__ uint32_t lds[];
-  constexpr int NLW = K >= 6 ? 3 : 2;            // code words loaded per lane per tile
-  constexpr int MPAD = 16 * MB;
-  constexpr int STRIDE = GemmLds<SUB>::kStride;
-  constexpr int COLS = GemmLds<SUB>::kCols;
-  constexpr int WPT = 8 * K;                      // words per tile
+// Store a lane's K staged words with the widest aligned LDS stores (contiguous
+// across lanes, so conflict-free).
+template <int K>
+__device__ __forceinline__ void stage_words(uint32_t* dst, const uint32_t (&w)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i)
+      reinterpret_cast<u32x4*>(dst)[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+  } else if constexpr (K % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) reinterpret_cast<u32x2*>(dst)[i] = u32x2{w[2 * i], w[2 * i + 1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) dst[i] = w[i];
+  }
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int ob = bid / a.splits, split = bid - ob * a.splits;
-
-  const int nsub_total = a.n / COLS;
-  const int sub0 = (int)((int64_t)split * nsub_total / a.splits);
-  const int sub1 = (int)((int64_t)(split + 1) * nsub_total / a.splits);
-  const int nsub = sub1 - sub0;
-
-  // Per-lane decode geometry (identical for every tile).
+// One wave: 8 tile rows (a 128-output block) x the tile columns col0, col0+step, ...
+// For each column the wave loads the 8 tiles (one contiguous 32K-byte run per
+// tile, 8 lanes per tile), restages them through its private LDS slice so that
+// each lane can pick the two (three) words its four windows need, decodes one
+// B operand per tile and issues MB MFMAs per tile against the column's x~ rows.
+template <int K, bool ROUND, int MB, int PF>
+__device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, int ncol, int cstep, uint32_t* slice,
+                                          float4_t (&acc)[8][MB]) {
+  constexpr int NLW = K >= 6 ? 3 : 2;   // words a lane needs per tile
+  constexpr int WPT = 8 * K;             // words per tile
+  const int lane = threadIdx.x & 63;
   const int jrow = lane & 15, g = lane >> 4;
   const int b0 = K * (16 * jrow + 4 * g);
   const int q0 = b0 & 31, j0 = b0 >> 5;
   int widx[NLW];
   uint32_t shift;
-  if (q0 == 0) {
+  if (q0 == 0) {        // window starts on a word: alignbit with shift 0 returns its second operand
     widx[0] = (j0 + WPT - 1) % WPT;
     shift = 0u;
 #pragma unroll
@@ -83,117 +99,158 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < NLW; ++i) widx[i] = (j0 + i) % WPT;
   }
+  const size_t n16 = (size_t)(a.n >> 4);
+  const int tl = lane >> 3;                                  // tile row this lane loads
+  const uint32_t* __restrict__ cptr = a.codes + ((size_t)(ob * 8 + tl) * n16 + col0) * WPT + (lane & 7) * K;
+  const uint32_t* __restrict__ xptr = a.xt + (size_t)jrow * a.n + 4 * g + (size_t)col0 * 16;
+  const uint32_t* __restrict__ cfirst = cptr;
+  const uint32_t* __restrict__ xfirst = xptr;
+  const size_t cadv = (size_t)cstep * WPT, xadv = (size_t)cstep * 16;
 
-  const int R = ob * 8 + wave;
-  const uint32_t* __restrict__ rowp = a.codes + ((size_t)R * (size_t)(a.n >> 4) + (size_t)sub0 * SUB) * WPT;
-
-  auto xb = [&](int b) -> uint32_t* { return lds + b * (MPAD * STRIDE); };
-
-  // Stage x~ of sub-chunk `s` (rows 0..MPAD-1, COLS inputs) into LDS buffer `b`.
-  constexpr int kStageVec = MPAD * COLS / 4;                       // u32x4 per sub-chunk
-  constexpr int kStagePer = (kStageVec + kGemvThreads - 1) / kGemvThreads;
-  u32x4 stage[kStagePer];
-  auto stage_load = [&](int s) {
+  // Prefetch ring; out-of-range columns re-read the first column (valid addresses,
+  // and every path issues the same loads so the waits stay exact).
+  uint32_t cw[PF][K];
+  u32x4 xa[PF][MB];
+  int issued = 0;
+  auto issue = [&](uint32_t(&dst)[K], u32x4(&xd)[MB]) {
+    const bool ok = issued < ncol;
+    load_column<K>(ok ? cptr : cfirst, dst);
+    const uint32_t* xq = ok ? xptr : xfirst;
 #pragma unroll
-    for (int v = 0; v < kStagePer; ++v) {
-      const int idx = threadIdx.x + v * kGemvThreads;
-      if (idx < kStageVec) {
-        const int row = idx / (COLS / 4), c4 = idx - row * (COLS / 4);
-        const int sc = s < nsub ? sub0 + s : sub0;    // out of range: re-read a valid line
-        stage[v] = *reinterpret_cast<const u32x4*>(a.xt + (size_t)row * a.n + (size_t)sc * COLS + c4 * 4);
-      }
-    }
+    for (int mb = 0; mb < MB; ++mb) xd[mb] = *reinterpret_cast<const u32x4*>(xq + (size_t)(16 * mb) * a.n);
+    cptr += cadv;
+    xptr += xadv;
+    ++issued;
   };
-  auto stage_store = [&](int b) {
 #pragma unroll
-    for (int v = 0; v < kStagePer; ++v) {
-      const int idx = threadIdx.x + v * kGemvThreads;
-      if (idx < kStageVec) {
-        const int row = idx / (COLS / 4), c4 = idx - row * (COLS / 4);
-        *reinterpret_cast<u32x4*>(xb(b) + row * STRIDE + c4 * 4) = stage[v];
-      }
-    }
-  };
+  for (int p = 0; p < PF; ++p) issue(cw[p], xa[p]);
 
-  uint32_t cw[SUB][NLW];
-  auto code_load = [&](int s) {
-#pragma unroll
-    for (int t = 0; t < SUB; ++t) {
-#pragma unroll
-      for (int i = 0; i < NLW; ++i)
-        cw[t][i] = __builtin_nontemporal_load((s < nsub ? rowp + ((size_t)s * SUB + t) * WPT : a.codes) + widx[i]);
-    }
-  };
-
-  float4_t acc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
   const CodeRegs cr;
-
-  if (nsub > 0) {
-    stage_load(0);
-    code_load(0);
-    stage_store(0);
-    __syncthreads();
-  }
-  for (int s = 0; s < nsub; ++s) {
-    const int cur = s & 1;
-    uint32_t cc[SUB][NLW];
+  for (int i0 = 0; i0 < ncol; i0 += PF) {
 #pragma unroll
-    for (int t = 0; t < SUB; ++t)
+    for (int p = 0; p < PF; ++p) {
+      if (i0 + p < ncol) {
+        // stage the column's words, read back the words of all 8 tiles,
+        // decode all 8 B operands, then issue the MFMAs back to back
+        stage_words<K>(slice + lane * K, cw[p]);   // lane l's K words sit at word l*K
+        uint32_t wv[8][NLW];
 #pragma unroll
-      for (int i = 0; i < NLW; ++i) cc[t][i] = cw[t][i];
-    stage_load(s + 1);
-    code_load(s + 1);
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int t = 0; t < SUB; ++t) {
-      const uint32_t r1 = alignbit(cc[t][0], cc[t][1], shift);
-      uint32_t r2 = 0u;
-      if constexpr (NLW == 3) r2 = alignbit(cc[t][1], cc[t][2], shift);
-      uint32_t bw[4];
+          for (int k = 0; k < NLW; ++k) wv[t][k] = slice[t * WPT + widx[k]];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int P = K * e;
-        uint32_t st;
-        if (P <= 16) st = ubfe(r1, 16 - P, 16);
-        else st = ubfe(alignbit(r1, r2, 48 - P), 0, 16);
-        const uint32_t u = code_halves(st, cr);
-        if constexpr (ROUND) bw[e] = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
-        else bw[e] = u;
+        for (int t0 = 0; t0 < 8; t0 += TG_MFMA_GROUP) {
+        uint32_t bw[TG_MFMA_GROUP][4];
+#pragma unroll
+        for (int tt = 0; tt < TG_MFMA_GROUP; ++tt) {
+          const int t = t0 + tt;
+          const uint32_t r1 = alignbit(wv[t][0], wv[t][1], shift);
+          uint32_t r2 = 0u;
+          if constexpr (NLW == 3) r2 = alignbit(wv[t][1], wv[t][2], shift);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int P = K * e;
+            const uint32_t st = P <= 16 ? ubfe(r1, 16 - P, 16) : ubfe(alignbit(r1, r2, 48 - P), 0, 16);
+            const uint32_t u = code_halves(st, cr);
+            if constexpr (ROUND) bw[tt][e] = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
+            else bw[tt][e] = u;
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TG_MFMA_GROUP; ++tt) {
+          const half8_t bop = __builtin_bit_cast(half8_t, u32x4{bw[tt][0], bw[tt][1], bw[tt][2], bw[tt][3]});
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[t0 + tt][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xa[p][mb]), bop,
+                                                                      acc[t0 + tt][mb], 0, 0, 0);
+        }
+        }
       }
-      const half8_t bop = __builtin_bit_cast(half8_t, u32x4{bw[0], bw[1], bw[2], bw[3]});
+      issue(cw[p], xa[p]);
+    }
+  }
+}
+
+template <int K, bool ROUND, int MB>
+__global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
+  extern __shared__ uint32_t lds[];
+  constexpr int PF = 2;
+  constexpr int WPT = 8 * K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int ob = bid / a.splits, split = bid - ob * a.splits;
+  const int ncols = a.n >> 4;
+  const int c0 = (int)((int64_t)split * ncols / a.splits);
+  const int c1 = (int)((int64_t)(split + 1) * ncols / a.splits);
+  // wave w takes columns c0+w, c0+w+8, ... of the chunk
+  const int nmine = c1 - c0 > wave ? (c1 - c0 - wave + kGemvWaves - 1) / kGemvWaves : 0;
+
+  float4_t acc[8][MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(xb(cur) + (16 * mb + jrow) * STRIDE + t * 16 + 4 * g);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bop, acc[mb], 0, 0, 0);
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[t][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+  if (nmine > 0) gemm_wave<K, ROUND, MB, PF>(a, ob, c0 + wave, nmine, kGemvWaves, lds + wave * 8 * WPT, acc);
+
+  // Sum the 8 waves' accumulators: a fixed tree through LDS (4 -> 2 -> 1 waves),
+  // one 16-row group at a time to bound the LDS footprint.
+  float* red = reinterpret_cast<float*>(lds + kGemvWaves * 8 * WPT);   // [4][8*4][64]
+  constexpr int NV = 8 * 4;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int half = 4; half >= 1; half >>= 1) {
+      __syncthreads();
+      if (wave >= half && wave < 2 * half) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[(((wave - half) * NV) + t * 4 + v) * 64 + lane] = acc[t][mb][v];
+      }
+      __syncthreads();
+      if (wave < half) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[t][mb][v] += red[((wave * NV) + t * 4 + v) * 64 + lane];
       }
     }
-    if (s + 1 < nsub) stage_store(cur ^ 1);
-    __syncthreads();
   }
 
-  // acc[mb][v] = partial Y[16mb + 4g + v][16R + jrow]
-  float* ybuf = reinterpret_cast<float*>(lds);   // [MPAD][128], reuses the staging buffers
-  uint32_t* flag = lds + MPAD * 128;
-  const int ocol = wave * 16 + jrow;
+  // Wave 0 now holds the block: acc[t][mb][v] = Y[16mb + 4g + v][ob*128 + 16t + (lane&15)].
+  float* ybuf = reinterpret_cast<float*>(lds);   // [16*MB][128]
+  uint32_t* flag = lds + 16 * MB * 128;
+  const int g = lane >> 4, jrow = lane & 15;
+  __syncthreads();
   if (a.splits == 1) {
+    if (wave == 0) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ybuf[(16 * mb + 4 * g + v) * 128 + ocol] = acc[mb][v];
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ybuf[(16 * mb + 4 * g + v) * 128 + 16 * t + jrow] = acc[t][mb][v];
+    }
     __syncthreads();
     for (int r = wave; r < a.M; r += kGemvWaves)
       rht_out_block(ybuf[r * 128 + lane], ybuf[r * 128 + lane + 64], a.scales, a.sign_out, a.y + (size_t)r * a.ldy,
                     ob * kBlock, lane);
     return;
   }
+  if (wave == 0) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 16 * mb + 4 * g + v;
-      if (r < a.M) store_partial(a.partials + ((size_t)split * a.M + r) * a.m + ob * kBlock + ocol, acc[mb][v]);
-    }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = 16 * mb + 4 * g + v;
+          if (r < a.M)
+            store_partial(a.partials + ((size_t)split * a.M + r) * a.m + ob * kBlock + 16 * t + jrow, acc[t][mb][v]);
+        }
+  }
   if (!arrive_is_last(&a.counters[ob], (uint32_t)a.splits, flag)) return;
   for (int r = wave; r < a.M; r += kGemvWaves) {
     float v0 = 0.f, v1 = 0.f;
@@ -208,22 +265,20 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
   if (threadIdx.x == 0) reset_counter(&a.counters[ob]);
 }
 
-template <int MB>
-constexpr int gemm_sub() { return MB <= 2 ? 8 : 4; }
-
-template <int MB>
+template <int K, int MB>
 size_t gemm_lds_bytes() {
-  constexpr int SUB = gemm_sub<MB>();
-  const size_t staging = 2ull * 16 * MB * GemmLds<SUB>::kStride * 4;
+  const size_t slices = (size_t)kGemvWaves * 8 * 8 * K * 4;   // per-wave code staging
+  const size_t red = 4ull * 8 * 4 * 64 * 4;                     // tree reduction buffer (one row group)
   const size_t ybuf = 16ull * MB * 128 * 4 + 16;
-  return staging > ybuf ? staging : ybuf;
+  const size_t a = slices + red;
+  return a > ybuf ? a : ybuf;
 }
 
 template <int K, bool ROUND, int MB>
 static void launch_main(const GemmArgs& a, hipStream_t s) {
   const int grid = (a.m >> 7) * a.splits;
-  hipLaunchKernelGGL((gemm_small_kernel<K, ROUND, MB, gemm_sub<MB>()>), dim3(grid), dim3(kGemvThreads),
-                     gemm_lds_bytes<MB>(), s, a);
+  const size_t lds = gemm_lds_bytes<K, MB>();
+  hipLaunchKernelGGL((gemm_small_kernel<K, ROUND, MB>), dim3(grid), dim3(kGemvThreads), lds, s, a);
 }
 
 template <int K, bool ROUND>
@@ -235,8 +290,6 @@ static void launch_mb(const GemmArgs& a, hipStream_t s) {
     default: launch_main<K, ROUND, 4>(a, s); break;
   }
 }
-
-int gemm_sub_tiles(int mpad) { return mpad <= 32 ? 8 : 4; }
 
 hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in, int k_bits,
                              bool round_weights, hipStream_t s) {
