@@ -71,3 +71,31 @@ def weight_values(states) -> np.ndarray:
 def table() -> np.ndarray:
     """The whole code: fp16 bits for all 65,536 states."""
     return weight_bits(np.arange(1 << 16))
+
+
+# ---------------------------------------------------------------------------
+# code_id 1, the pair code (this library's V=2 variant; readings in DESIGN.md):
+# one state per two consecutive weights ([DD] Section 3: b*V bits per
+# V-dimensional step; its decode snippet yields a pair of halves per state).
+# The state goes through the same multiply-add and mask/XOR; the halves a, b
+# give the rotated pair (a + b, b - a), each rounded to binary16 -- every
+# weight is again a sum of two bounded halves ([TQ] Part nine).
+# Pins (tests/test_oracle_code.py): hand-derived values
+# (tests/golden/pair_code_hand_values.txt), NumPy's float16 cast on all states,
+# the pair's sum/difference identities.
+# ---------------------------------------------------------------------------
+
+def pair_weight_bits(states):
+    """fp16 bits of (RNE(a + b), RNE(b - a)) for each state; returns two arrays."""
+    lo, hi = halves(mask_xor(lcg(states)))
+    a, b = fp16.value(lo), fp16.value(hi)
+    return fp16.round_rne(a + b), fp16.round_rne(b - a)
+
+
+def pair_table() -> np.ndarray:
+    """The pair code for all states: uint16 [65536, 2] = (even weight, odd weight)."""
+    e, o = pair_weight_bits(np.arange(1 << 16))
+    return np.stack([e, o], axis=-1)
+
+
+CODE_V = {0: 1, 1: 2}     # weights per trellis step of each code_id

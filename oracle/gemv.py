@@ -4,6 +4,7 @@ What the path computes ([DD] Section 2 equations; [TQ] Parts eight, nine,
 eleven; [FG] "out_scales always"):
 
     W^[o, i] = code(S_t) of tile (o // 16, i // 16), t = 16 (o % 16) + (i % 16)
+               (code_id 1: weights t = 2 tau, 2 tau + 1 share the state S_tau)
     x~ = blockdiag(H_128) diag(s_in) x
     y~ = diag(g) W^ x~                          (g: per-output fp16 scale)
     y  = diag(s_out) blockdiag(H_128) y~
@@ -26,9 +27,20 @@ from . import code, fp16, hadamard, trellis
 
 
 def decode_layer(layer, tile_rows=None) -> np.ndarray:
-    """fp16 bit patterns of the decoded weights, [m, n] (or only the listed tile rows)."""
-    states = trellis.layer_states(layer.codes, layer.m, layer.n, layer.k_bits, tile_rows)
-    return code.weight_bits(trellis.states_to_matrix(states)).astype(np.uint16)
+    """fp16 bit patterns of the decoded weights, [m, n] (or only the listed tile rows).
+
+    code_id 0: one state per weight. code_id 1: one state per pair of weights
+    (t = 2*tau, 2*tau + 1 of the row-major tile order).
+    """
+    cid = int(getattr(layer, "code_id", 0))
+    v = code.CODE_V[cid]
+    states = trellis.layer_states(layer.codes, layer.m, layer.n, layer.k_bits, tile_rows, v)
+    if cid == 0:
+        w = code.weight_bits(states)
+    else:
+        even, odd = code.pair_weight_bits(states)
+        w = np.stack([even, odd], axis=-1).reshape(*states.shape[:-1], trellis.SEQ)
+    return trellis.states_to_matrix(w).astype(np.uint16)
 
 
 def weight_matrix(layer, tile_rows=None) -> np.ndarray:

@@ -10,6 +10,10 @@ Definitions followed:
     trellis treats the stream as a circle, so a sequence holds exactly 256*K
     bits and the final windows wrap onto the first bits.
 
+V-dimensional steps ([DD] Section 3, "b*V bits per V-dimensional sub-vector"):
+with V=2 a sequence of 256 weights is 128 steps of two weights; each step
+shifts 2K bits and the state of step tau starts at stream bit 2K*tau.
+
 Readings where the pages are silent (each listed in the design doc):
   * the first stream bit of a window is the state's most significant bit;
   * stream bit p of a tile is bit (31 - p mod 32) of 32-bit word p // 32
@@ -60,71 +64,75 @@ def _bits_to_int(bits: np.ndarray) -> np.ndarray:
     return out
 
 
-def walk_states(bits: np.ndarray, k_bits: int) -> np.ndarray:
-    """Walk the tail-biting trellis state by state. bits uint8 [..., 256K] -> states int64 [..., 256].
+def walk_states(bits: np.ndarray, k_bits: int, v: int = 1) -> np.ndarray:
+    """Walk the tail-biting trellis state by state. bits uint8 [..., 256K] -> states int64 [..., 256/v].
 
     S_0 is the first 16 bits of the circle; each later state shifts in the
-    next K bits, taken cyclically.
+    next b = v*K bits, taken cyclically.
     """
     nbits = bits.shape[-1]
     assert nbits == SEQ * k_bits
-    states = np.empty(bits.shape[:-1] + (SEQ,), dtype=np.int64)
+    b, nsteps = v * k_bits, SEQ // v
+    states = np.empty(bits.shape[:-1] + (nsteps,), dtype=np.int64)
     s = _bits_to_int(bits[..., :L])
     states[..., 0] = s
-    for t in range(1, SEQ):
-        first = L + k_bits * (t - 1)                              # next unread bit of the circle
-        idx = [(first + i) % nbits for i in range(k_bits)]
-        s = step(s, _bits_to_int(bits[..., idx]), k_bits)
+    for t in range(1, nsteps):
+        first = L + b * (t - 1)                                   # next unread bit of the circle
+        idx = [(first + i) % nbits for i in range(b)]
+        s = step(s, _bits_to_int(bits[..., idx]), b)
         states[..., t] = s
     return states
 
 
-def window_states(bits: np.ndarray, k_bits: int) -> np.ndarray:
-    """Random-access route ([TQ] Part eight): S_t = 16-bit window starting at bit K*t of the circle."""
+def window_states(bits: np.ndarray, k_bits: int, v: int = 1) -> np.ndarray:
+    """Random-access route ([TQ] Part eight): S_t = 16-bit window starting at bit v*K*t of the circle."""
     nbits = bits.shape[-1]
-    t = np.arange(SEQ)
-    idx = (k_bits * t[:, None] + np.arange(L)[None, :]) % nbits   # [256, 16]
+    t = np.arange(SEQ // v)
+    idx = (v * k_bits * t[:, None] + np.arange(L)[None, :]) % nbits   # [256/v, 16]
     return _bits_to_int(bits[..., idx])
 
 
-def stream_from_states(states: np.ndarray, k_bits: int) -> np.ndarray:
-    """Inverse map: concatenating the top K bits of S_0..S_255 gives back the 256K-bit stream."""
+def stream_from_states(states: np.ndarray, k_bits: int, v: int = 1) -> np.ndarray:
+    """Inverse map: concatenating the top v*K bits of every state gives back the 256K-bit stream."""
     s = np.asarray(states, dtype=np.int64)
-    cols = [((s >> (L - 1 - i)) & 1) for i in range(k_bits)]      # [..., 256] each
+    b = v * k_bits
+    cols = [((s >> (L - 1 - i)) & 1) for i in range(b)]            # [..., 256/v] each
     return np.stack(cols, axis=-1).reshape(*s.shape[:-1], SEQ * k_bits).astype(np.uint8)
 
 
-def is_valid_path(states: np.ndarray, k_bits: int) -> np.ndarray:
+def is_valid_path(states: np.ndarray, k_bits: int, v: int = 1) -> np.ndarray:
     """True where every consecutive pair (cyclically) is a bitshift-trellis edge.
 
-    S_{t+1} must keep the low 16-K bits of S_t as its top 16-K bits.
+    S_{t+1} must keep the low 16-b bits of S_t as its top 16-b bits (b = v*K).
     """
     s = np.asarray(states, dtype=np.int64)
+    b = v * k_bits
     nxt = np.roll(s, -1, axis=-1)
-    keep = (1 << (L - k_bits)) - 1
-    return np.all((nxt >> k_bits) == (s & keep), axis=-1)
+    keep = (1 << (L - b)) - 1
+    return np.all((nxt >> b) == (s & keep), axis=-1)
 
 
-def closes_circle(states: np.ndarray, bits: np.ndarray, k_bits: int) -> np.ndarray:
-    """Tail-biting closure: stepping S_255 with bits 16-K..15 of the circle gives S_0 again."""
-    tail = _bits_to_int(bits[..., L - k_bits:L])
-    return step(states[..., -1], tail, k_bits) == states[..., 0]
+def closes_circle(states: np.ndarray, bits: np.ndarray, k_bits: int, v: int = 1) -> np.ndarray:
+    """Tail-biting closure: stepping the last state with bits 16-b..15 of the circle gives S_0 again."""
+    b = v * k_bits
+    tail = _bits_to_int(bits[..., L - b:L])
+    return step(states[..., -1], tail, b) == states[..., 0]
 
 
 def tile_index(R: int, C: int, n: int) -> int:
     return R * (n // TILE) + C
 
 
-def layer_states(codes: np.ndarray, m: int, n: int, k_bits: int, tile_rows=None) -> np.ndarray:
+def layer_states(codes: np.ndarray, m: int, n: int, k_bits: int, tile_rows=None, v: int = 1) -> np.ndarray:
     """States of a whole layer (or of the listed tile rows) by walking every tile.
 
-    Returns int64 [len(tile_rows), n/16, 256] with tile_rows defaulting to all m/16.
+    Returns int64 [len(tile_rows), n/16, 256/v] with tile_rows defaulting to all m/16.
     """
     wpt = words_per_tile(k_bits)
     tiles = np.asarray(codes, dtype=np.uint32).reshape(m // TILE, n // TILE, wpt)
     if tile_rows is not None:
         tiles = tiles[np.asarray(tile_rows)]
-    return walk_states(stream_bits(tiles, k_bits), k_bits)
+    return walk_states(stream_bits(tiles, k_bits), k_bits, v)
 
 
 def states_to_matrix(states: np.ndarray) -> np.ndarray:

@@ -80,3 +80,31 @@ def test_sum_is_near_gaussian_and_finite():
     kurt = ((w - w.mean()) ** 4).mean() / w.var() ** 2
     assert 2.5 < kurt < 3.5
     assert np.abs(w).max() < 4.0
+
+
+def test_pair_code_hand_values():
+    """The pair code (code_id 1): rotated pair of the two halves, each rounded to binary16."""
+    for state, lo, hi, en, ed, we, on, od, wo in golden_rows("pair_code_hand_values.txt"):
+        s = np.array([int(state, 16)])
+        l, h = code.halves(code.mask_xor(code.lcg(s)))
+        assert int(l[0]) == int(lo, 16) and int(h[0]) == int(hi, 16)
+        e, o = code.pair_weight_bits(s)
+        assert int(e[0]) == int(we, 16) and int(o[0]) == int(wo, 16)
+        a, b = fp16.value(l)[0], fp16.value(h)[0]
+        assert Fraction(float(a + b)) == Fraction(int(en), int(ed))
+        assert Fraction(float(b - a)) == Fraction(int(on), int(od))
+
+
+def test_pair_table_matches_numpy_and_is_balanced():
+    lo, hi = code.halves(code.mask_xor(code.lcg(np.arange(1 << 16))))
+    a = lo.view(np.float16).astype(np.float64)
+    b = hi.view(np.float16).astype(np.float64)
+    t = code.pair_table()
+    assert (t[:, 0] == (a + b).astype(np.float16).view(np.uint16)).all()
+    assert (t[:, 1] == (b - a).astype(np.float16).view(np.uint16)).all()
+    # the even weight is the V=1 code's weight for the same state
+    assert (t[:, 0] == code.table()).all()
+    we, wo = fp16.value(t[:, 0]), fp16.value(t[:, 1])
+    for w in (we, wo):
+        assert np.isfinite(w).all() and abs(w.mean()) < 0.02 and 1.1 < w.std() < 1.4
+    assert abs(np.corrcoef(we, wo)[0, 1]) < 0.05

@@ -143,3 +143,51 @@ def test_rows_batched_grouped_reduce_to_single_vector():
     L2 = inputs.make_layer(128, 256, 1, 14)
     out = gemv.grouped([L, L2], [1, 0], X[0], shared_x=True)
     assert np.array_equal(out[1], gemv.gemv(L, X[0])) and np.array_equal(out[0], gemv.gemv(L2, X[0]))
+
+
+def _pair_hand(state):
+    for row in golden_rows("pair_code_hand_values.txt"):
+        if int(row[0], 16) == state:
+            return (float(np.array([int(row[5], 16)], np.uint16).view(np.float16)[0]),
+                    float(np.array([int(row[8], 16)], np.uint16).view(np.float16)[0]))
+    raise KeyError(state)
+
+
+def test_pair_code_all_zero_stream_closed_form():
+    """Pair code, all-zero stream: even columns hold w_e = code(0) even weight, odd columns w_o.
+    Per input block, the even entries of H v sum to 64 (v_0 + v_1) / sqrt(128) and the odd
+    ones to 64 (v_0 - v_1) / sqrt(128), so with g = 1 every row of y~ is
+        c = sum_b 64/sqrt(128) * (w_e (v_b0 + v_b1) + w_o (v_b0 - v_b1)),  v = s_in * x,
+    and y_o = s_out[o] * c * sqrt(128) for o = 0 mod 128, 0 otherwise."""
+    m, n, k = 256, 384, 3
+    L = _layer(m, n, k, codes=np.zeros(inputs.words_per_layer(m, n, k), np.uint32),
+               scales=_bits(np.ones(m)))
+    L.code_id = 1
+    x = inputs.make_x(n, 21)
+    we, wo = _pair_hand(0)
+    s_in = 1 - 2 * ((L.sign_in[np.arange(n) // 32] >> (np.arange(n) % 32)) & 1).astype(np.float64)
+    s_out = 1 - 2 * ((L.sign_out[np.arange(m) // 32] >> (np.arange(m) % 32)) & 1).astype(np.float64)
+    v = s_in * x.view(np.float16).astype(np.float64)
+    c = sum(64 / SQ * (we * (v[128 * b] + v[128 * b + 1]) + wo * (v[128 * b] - v[128 * b + 1]))
+            for b in range(n // 128))
+    expect = np.zeros(m)
+    expect[::128] = s_out[::128] * c * SQ
+    y = gemv.gemv(L, x)
+    assert np.allclose(y, expect, rtol=1e-12, atol=1e-12 * np.abs(expect).max())
+
+
+def test_pair_code_tile_layout():
+    """Pair code: one all-ones tile gives alternating (even, odd) weights of state 0xFFFF there."""
+    m, n, k = 128, 256, 2
+    codes = np.zeros(inputs.words_per_layer(m, n, k), np.uint32)
+    R, C = 3, 9
+    T = R * (n // 16) + C
+    codes[T * 8 * k:(T + 1) * 8 * k] = 0xFFFFFFFF
+    L = _layer(m, n, k, codes=codes)
+    L.code_id = 1
+    W = gemv.decode_layer(L)
+    e0, o0 = _pair_hand(0)
+    e1, o1 = _pair_hand(0xFFFF)
+    expect = np.tile(_bits([e0, o0]), (m, n // 2))
+    expect[16 * R:16 * R + 16, 16 * C:16 * C + 16] = np.tile(_bits([e1, o1]), (16, 8))
+    assert np.array_equal(W, expect)

@@ -114,3 +114,35 @@ def test_layer_addressing_tile_row_major():
     codes[(k * t) // 32] = np.uint32(1 << (31 - (k * t) % 32))
     mat = trellis.states_to_matrix(trellis.layer_states(codes, m, n, k))
     assert mat[t // 16, t % 16] == 0x8000
+
+
+@pytest.mark.parametrize("k", range(1, 9))
+def test_pair_steps_walk_equals_random_access(k):
+    """V=2 steps ([DD] Section 3: b*V bits per V-dimensional step): 128 states of 2K new bits."""
+    b = trellis.stream_bits(_random_tiles(k, 32, 40 + k), k)
+    s = trellis.walk_states(b, k, v=2)
+    assert s.shape[-1] == 128
+    assert (s == trellis.window_states(b, k, v=2)).all()
+    assert (trellis.stream_from_states(s, k, v=2) == b).all()
+    assert trellis.closes_circle(s, b, k, v=2).all()
+    assert trellis.is_valid_path(s, k, v=2).all()
+
+
+def test_pair_steps_weight100_reads_bit200():
+    """With V=2 at K=2, weights 100 and 101 share state 50, whose window starts at bit 200."""
+    bits = np.zeros(512, dtype=np.uint8)
+    bits[200] = 1
+    s = trellis.walk_states(trellis.stream_bits(_tile_from_bits(bits), 2), 2, v=2)
+    assert s[50] == 0x8000 and s[49] == 0x0800 and s[51] == 0
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_pair_steps_single_bits(k):
+    nb = 256 * k
+    tau = np.arange(128)
+    for p in range(nb):
+        bits = np.zeros(nb, dtype=np.uint8)
+        bits[p] = 1
+        s = trellis.walk_states(trellis.stream_bits(_tile_from_bits(bits), k), k, v=2)
+        d = (p - 2 * k * tau) % nb
+        assert (s == np.where(d <= 15, 1 << (15 - np.minimum(d, 15)), 0)).all(), p
