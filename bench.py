@@ -61,7 +61,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: int, kernel: str):
+def recorded_traffic(workload: int, kernel: str, code_id: int = 0):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -69,7 +69,8 @@ def recorded_traffic(workload: int, kernel: str):
         return None
     if rec.get("csrc_sha") != kernel_source_hash():
         return None
-    ent = rec.get("workloads", {}).get(str(workload), {}).get(kernel)
+    key = str(workload) if code_id == 0 else f"{workload}/code{code_id}"
+    ent = rec.get("workloads", {}).get(key, {}).get(kernel)
     return None if ent is None else int(ent["hbm_bytes_per_launch"])
 
 
@@ -127,7 +128,7 @@ def _copies(total_bytes):
     return max(1, min(MAX_COPIES, math.ceil(CACHE_DEFEAT_BYTES / total_bytes)))
 
 
-def setup_linears(torch, tg, inputs, wl, dev):
+def setup_linears(torch, tg, inputs, wl, dev, code_id):
     """Workloads 1-3: batch-1 GEMVs over the workload's tensors, one call each per step."""
     names = list(wl.tensors)
     code_bytes = sum(m * n * k // 8 for (m, n, k) in wl.tensors.values())
@@ -138,7 +139,7 @@ def setup_linears(torch, tg, inputs, wl, dev):
         layers = {}
         for ti, name in enumerate(names):
             m, n, k = wl.tensors[name]
-            L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=ti, copy=c), dev)
+            L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=ti, copy=c, code_id=code_id), dev)
             x = tg.fp16_tensor(inputs.make_x(n, wl.seed, tensor=ti, copy=c), dev)
             y = torch.empty(m, dtype=torch.float32, device=dev)
             layers[name] = (L, x, y)
@@ -156,7 +157,7 @@ def setup_linears(torch, tg, inputs, wl, dev):
                       units="layer" if len(names) == 1 else "decoder layer (7 GEMVs)")
 
 
-def setup_gemm(torch, tg, inputs, wl, dev):
+def setup_gemm(torch, tg, inputs, wl, dev, code_id):
     name = "gate"
     m, n, k = wl.tensors[name]
     M = wl.batch
@@ -165,7 +166,7 @@ def setup_gemm(torch, tg, inputs, wl, dev):
     log(f"{wl.name}: M={M}, {code_bytes} code bytes, {copies} copies")
     per = []
     for c in range(copies):
-        L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=0, copy=c), dev)
+        L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=0, copy=c, code_id=code_id), dev)
         X = tg.fp16_tensor(inputs.make_x(n, wl.seed, tensor=0, copy=c, rows=M), dev)
         Y = torch.empty(M, m, dtype=torch.float32, device=dev)
         per.append((L, X, Y))
@@ -179,17 +180,17 @@ def setup_gemm(torch, tg, inputs, wl, dev):
                       names=[name], units="layer (16 rows)", flops=2.0 * m * n * M)
 
 
-def setup_moe(torch, tg, inputs, wl, dev):
+def setup_moe(torch, tg, inputs, wl, dev, code_id):
     routing = wl.routing()
-    gu_arr = [wl.layer(e, w) for e in range(wl.experts) for w in ("gate", "up")]
-    dn_arr = [wl.layer(e, "down") for e in range(wl.experts)]
+    gu_arr = [wl.layer(e, w, code_id=code_id) for e in range(wl.experts) for w in ("gate", "up")]
+    dn_arr = [wl.layer(e, "down", code_id=code_id) for e in range(wl.experts)]
     all_bytes = sum(a.code_bytes for a in gu_arr + dn_arr)
     copies = _copies(all_bytes)
     log(f"{wl.name}: {all_bytes} code bytes for all experts, {copies} copies, {wl.tokens} tokens")
     tables = []
     for c in range(copies):
-        gu = [tg.DeviceLayer(wl.layer(e, w, copy=c), dev) for e in range(wl.experts) for w in ("gate", "up")]
-        dn = [tg.DeviceLayer(wl.layer(e, "down", copy=c), dev) for e in range(wl.experts)]
+        gu = [tg.DeviceLayer(wl.layer(e, w, copy=c, code_id=code_id), dev) for e in range(wl.experts) for w in ("gate", "up")]
+        dn = [tg.DeviceLayer(wl.layer(e, "down", copy=c, code_id=code_id), dev) for e in range(wl.experts)]
         tables.append((tg.LayerTable(gu, dev), tg.LayerTable(dn, dev)))
     sel_gu = [torch.tensor([2 * int(e) + w for e in routing[t] for w in (0, 1)], dtype=torch.int32, device=dev)
               for t in range(wl.tokens)]
@@ -218,7 +219,7 @@ def setup_moe(torch, tg, inputs, wl, dev):
                       units="token (24 GEMVs, 2 launches)")
 
 
-def run_gpu(workload, steps, warmup, use_graph):
+def run_gpu(workload, steps, warmup, use_graph, code_id=0):
     """Time `steps` steps of the workload. Returns (info, timings).
 
     region_ms: the timed region (all launches of K steps, graph replay unless disabled).
@@ -232,7 +233,7 @@ def run_gpu(workload, steps, warmup, use_graph):
     dev = "cuda"
     wl = inputs.WORKLOADS[workload]
     setup = {1: setup_linears, 2: setup_linears, 3: setup_linears, 4: setup_gemm, 5: setup_moe}[workload]
-    step, info = setup(torch, tg, inputs, wl, dev)
+    step, info = setup(torch, tg, inputs, wl, dev, code_id)
     dom = max(info["names"], key=lambda k: info["alg_bytes"][k])     # kernel moving the most bytes
     stream = torch.cuda.current_stream()
     for i in range(warmup):
@@ -265,7 +266,7 @@ def run_gpu(workload, steps, warmup, use_graph):
     return info, dict(region_ms=region_ms, eager_ms=eager_ms, dom=dom, dom_ms=dom_ms, timing=timing)
 
 
-def parity_spot_check(workload):
+def parity_spot_check(workload, code_id=0):
     """Copy 0 of the workload against the oracle on sampled outputs (after timing)."""
     import torch
     from oracle import gemv as ogemv
@@ -275,13 +276,13 @@ def parity_spot_check(workload):
     wl = inputs.WORKLOADS[workload]
     if workload == 5:
         e, which = int(wl.routing()[0][0]), "gate"
-        arr, x = wl.layer(e, which), inputs.make_x(wl.hidden, wl.seed, tensor=10_000)
+        arr, x = wl.layer(e, which, code_id=code_id), inputs.make_x(wl.hidden, wl.seed, tensor=10_000)
         rows, M = np.arange(0, wl.inter, 5), 1
     else:
         name = list(wl.tensors)[-1]
         m, n, k = wl.tensors[name]
         ti = list(wl.tensors).index(name)
-        arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti)
+        arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
         M = wl.batch
         x = inputs.make_x(n, wl.seed, tensor=ti, rows=M)
         rows = np.concatenate([np.arange(0, 128, 7), np.arange(m - 128, m, 11)])
@@ -297,7 +298,7 @@ def parity_spot_check(workload):
     return float(np.abs(y - ref).max() / np.abs(ref).max())
 
 
-def cpu_baseline(workload, sample_blocks):
+def cpu_baseline(workload, sample_blocks, code_id=0):
     """The oracle, untuned, on a bounded sample of the workload, scaled to the same unit (GB/s of codes)."""
     from threadpoolctl import threadpool_limits
     from oracle import gemv as ogemv
@@ -305,7 +306,7 @@ def cpu_baseline(workload, sample_blocks):
 
     wl = inputs.WORKLOADS[workload]
     if workload == 5:
-        arrs = [wl.layer(int(e), w) for e in wl.routing()[0][:2] for w in ("gate", "up", "down")]
+        arrs = [wl.layer(int(e), w, code_id=code_id) for e in wl.routing()[0][:2] for w in ("gate", "up", "down")]
         xs = [inputs.make_x(a.n, 1) for a in arrs]
         with threadpool_limits(limits=1):
             t = time.perf_counter()
@@ -319,7 +320,7 @@ def cpu_baseline(workload, sample_blocks):
         name = max(wl.tensors, key=lambda k: wl.tensors[k][0] * wl.tensors[k][1])
         m, n, k = wl.tensors[name]
         ti = list(wl.tensors).index(name)
-        arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti)
+        arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
         M = wl.batch
         X = inputs.make_x(n, wl.seed, tensor=ti, rows=M)
         nb = m // 128
@@ -347,6 +348,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--code", type=int, default=0, choices=[0, 1],
+                    help="code_id of every layer: 0 the three-instruction code, 1 the pair code")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=32, help="oracle sample size in 128-output blocks (0: skip)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -359,7 +362,7 @@ def main(argv=None):
 
     from trellis_coded_gemv_amd import inputs
     wl = inputs.WORKLOADS[args.workload]
-    info, t = run_gpu(args.workload, args.steps, args.warmup, not args.no_graph)
+    info, t = run_gpu(args.workload, args.steps, args.warmup, not args.no_graph, args.code)
     steps = args.steps
     ms_per_step = t["region_ms"] / steps
     value = info["code_bytes"] / (ms_per_step * 1e-3) / 1e9
@@ -370,7 +373,7 @@ def main(argv=None):
               "copies": info["copies"], "us_per_step": round(ms_per_step * 1e3, 3),
               "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
               "eager_us_per_step": round(t["eager_ms"] / steps * 1e3, 3),
-              "parity_max_rel_err": parity_spot_check(args.workload)}
+              "code_id": args.code, "parity_max_rel_err": parity_spot_check(args.workload, args.code)}
     if args.workload != 5:
         config.update({"tensors": {k: list(v) for k, v in wl.tensors.items()}, "batch": wl.batch})
     out = {
@@ -379,7 +382,7 @@ def main(argv=None):
         "vs_baseline": None, "dtype": "fp16", "data": "synthetic", "config": config,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.workload, dom),
+                     "traffic": recorded_traffic(args.workload, dom, args.code),
                      "algorithmic_bytes": int(info["alg_bytes"][dom]),
                      "launch_us": round(dom_launch_ms * 1e3, 3)},
     }
@@ -397,7 +400,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         out["config"]["calibration_bytes"] = buf.numel() * 4
     if args.cpu_blocks > 0:
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_blocks)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_blocks, args.code)
     out["config"]["csrc_sha"] = kernel_source_hash()
     print(json.dumps(out), flush=True)
     return 0

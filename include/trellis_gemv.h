@@ -28,6 +28,16 @@
  *             taken cyclically (tail-biting), first bit most significant.
  *   code    : h = (0x9E3779*S + 0x7F4A7C15) mod 2^32; u = (h & 0x8FFF8FFF) ^ 0x30003000;
  *             w = fp16_rne(half(u[15:0]) + half(u[31:16])).
+ *
+ * Storage format (code_id 1, the pair code): as code_id 0, except that one
+ *   trellis step carries two weights (Deep Dive, Section 3: b*V bits per
+ *   V-dimensional step, here V = 2): weights t = 2*tau and 2*tau+1 of a tile
+ *   (the same row, columns 2j and 2j+1) share the state whose 16-bit window
+ *   starts at stream bit 2*K*tau, taken cyclically. With a = half(u[15:0]),
+ *   b = half(u[31:16]) of the same u as above, w_{2 tau} = fp16_rne(a + b) and
+ *   w_{2 tau + 1} = fp16_rne(b - a). Each weight is again a sum of two bounded
+ *   halves (lecture, Part nine); the pair costs one code evaluation, so the
+ *   decode work per weight is about half that of code_id 0.
  *   scales  : m fp16 bit patterns (g).
  *   sign_in : ceil(n/32) uint32 words; bit i%32 of word i/32 set means s_in[i] = -1.
  *   sign_out: ceil(m/32) uint32 words, same convention.
@@ -66,7 +76,7 @@ typedef enum tg_status {
   TG_ERR_KBITS = -3,      /* k_bits outside 1..8                                      */
   TG_ERR_ALIGN = -4,      /* a pointer is not aligned as documented                   */
   TG_ERR_WORKSPACE = -5,  /* workspace missing or smaller than tg_workspace_size()     */
-  TG_ERR_CODE_ID = -6,    /* unsupported code_id                                      */
+  TG_ERR_CODE_ID = -6,    /* code_id other than 0 or 1                                */
   TG_ERR_LAUNCH = -7,     /* the HIP runtime rejected a kernel launch                 */
   TG_ERR_ARG = -8         /* any other invalid argument (stride, flags, index range)   */
 } tg_status;
@@ -81,7 +91,7 @@ typedef struct tg_layer {
   int32_t m;                 /* out_features, multiple of 128                              */
   int32_t n;                 /* in_features, multiple of 128                               */
   int32_t k_bits;            /* bits per weight K, 1..8 (lecture, Part eleven)              */
-  int32_t code_id;           /* 0 = the three-instruction code above                        */
+  int32_t code_id;           /* 0 = the three-instruction code; 1 = the pair code            */
   int32_t flags;             /* TG_FLAG_*                                                  */
   int32_t reserved;          /* must be 0                                                  */
   const uint32_t *codes;     /* device, (m/16)*(n/16)*8*K words, 16-byte aligned            */
@@ -169,12 +179,18 @@ size_t tg_grouped_workspace_size(const tg_layer *layers, int32_t n_layers, int32
 /*
  * Decode the whole layer to fp16 weights (test / export hook): w_out[o*n + i]
  * = W^[o, i] as fp16 patterns, bit-exact with the code's definition. Only
- * codes and shape are used; m, n need only be positive multiples of 16.
+ * codes, k_bits, code_id and shape are used; m, n need only be positive
+ * multiples of 16.
  *   w_out : device, m*n uint16.
  */
 int32_t trellis_decode(const tg_layer *layer, uint16_t *w_out, void *stream);
 
-/* The whole code as a table: out[S] = fp16 pattern of the weight for state S, S < 65536. */
+/*
+ * The whole code as a table, for every state S < 65536:
+ *   code_id 0: out[S] = fp16 pattern of the weight for state S  (65536 entries);
+ *   code_id 1: out[2S], out[2S+1] = the state's weight pair      (131072 entries).
+ *   out : device, 2-byte aligned.
+ */
 int32_t tg_code_table(int32_t code_id, uint16_t *out, void *stream);
 
 #ifdef __cplusplus

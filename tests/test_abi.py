@@ -52,7 +52,7 @@ def test_status_strings():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(k_bits=0), -3), (dict(k_bits=9), -3), (dict(m=100), -2), (dict(n=0), -2), (dict(m=-128), -2),
-    (dict(code_id=1), -6), (dict(flags=4), -8), (dict(reserved=1), -8), (dict(codes=0), -1),
+    (dict(code_id=2), -6), (dict(code_id=-1), -6), (dict(flags=4), -8), (dict(reserved=1), -8), (dict(codes=0), -1),
     (dict(sign_out=0), -1), (dict(codes=A16 + 8), -4), (dict(scales=A16 + 1), -4), (dict(sign_in=A4 + 2), -4)])
 def test_gemv_layer_validation(kw, status):
     d = _layer(**kw)
@@ -128,3 +128,14 @@ def test_grouped_validation():
     assert L.trellis_gemv_grouped(arr, A16, 2, A16, 4, A16, 100, A16, 256, A16, ws, None) == -8
     assert L.trellis_gemv_grouped(arr, A16, 2, A16, 4, A16, 0, A16, 255, A16, ws, None) == -8
     assert L.trellis_gemv_grouped(arr, A16, 2, A16, 4, A16, 0, A16, 256, A16, 64, None) == -5
+
+
+def test_pair_code_passes_layer_validation():
+    """code_id 1 is accepted: the call gets past the layer checks and stops at the missing workspace."""
+    L = tg.lib()
+    d = _layer(code_id=1)
+    assert L.tg_workspace_size(ctypes.byref(d), 1) > 0
+    assert L.trellis_gemv(ctypes.byref(d), A16, A16, 0, 1 << 30, None) == -5
+    assert L.trellis_gemm_small(ctypes.byref(d), 16, A16, 512, A16, 256, 0, 1 << 30, None) == -5
+    assert L.tg_code_table(1, 0, None) == -1
+    assert L.trellis_decode(ctypes.byref(d), 0, None) == -1

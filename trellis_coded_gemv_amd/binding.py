@@ -224,8 +224,10 @@ def trellis_decode(layer: DeviceLayer, out=None, stream=None):
     return out
 
 
-def code_table(device="cuda", stream=None):
+def code_table(device="cuda", code_id: int = 0, stream=None):
+    """The code for all 65536 states: int16 [65536] (code 0) or [65536, 2] (pair code)."""
     torch = _torch()
-    out = torch.empty(1 << 16, dtype=torch.int16, device=device)
-    _check(lib().tg_code_table(0, _ptr(out), _stream(stream)), "tg_code_table")
+    shape = (1 << 16,) if code_id == 0 else (1 << 16, 2)
+    out = torch.empty(shape, dtype=torch.int16, device=device)
+    _check(lib().tg_code_table(int(code_id), _ptr(out), _stream(stream)), "tg_code_table")
     return out

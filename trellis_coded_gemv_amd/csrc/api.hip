@@ -30,7 +30,7 @@ int env_int(const char* name) {
 
 int32_t check_layer(const tg_layer* L) {
   if (!L) return TG_ERR_NULL;
-  if (L->code_id != 0) return TG_ERR_CODE_ID;
+  if (L->code_id != 0 && L->code_id != 1) return TG_ERR_CODE_ID;
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || (L->m % kBlock) != 0 || (L->n % kBlock) != 0) return TG_ERR_SHAPE;
   if (L->m > (1 << 22) || L->n > (1 << 22)) return TG_ERR_SHAPE;
@@ -72,10 +72,11 @@ int gemv_splits(int m, int n) {
 
 // Splits of the small-batch path: the fp32 partials cost 8*S*M*m bytes of
 // traffic against m*n*K/8 code bytes, so keep S small; a chunk keeps at
-// least 8 tile columns (one per wave).
-int gemm_splits(int m, int n, int M, int k_bits) {
+// least 8 MFMA steps (one per wave): 8 tile columns for code 0, 16 for the
+// pair code, whose MFMA spans two tiles.
+int gemm_splits(int m, int n, int M, int k_bits, int code_id) {
   const int ob = m / kBlock;
-  const int nsub = n / kBlock;
+  const int nsub = n / (code_id == 0 ? kBlock : 2 * kBlock);
   int s = env_int("TG_SPLITK_MFMA");
   if (s <= 0) {
     s = (256 + ob / 2) / ob;                                     // about 256 workgroups
@@ -168,7 +169,7 @@ TG_API const char* tg_status_str(int32_t status) {
 
 TG_API size_t tg_workspace_size(const tg_layer* L, int32_t M) {
   if (check_layer(L) != TG_OK || M < 1 || M > 64) return 0;
-  const size_t g = gemm_ws(L->m, L->n, M, gemm_splits(L->m, L->n, M, L->k_bits)).total;
+  const size_t g = gemm_ws(L->m, L->n, M, gemm_splits(L->m, L->n, M, L->k_bits, L->code_id)).total;
   if (M > 1) return g;
   const size_t v = gemv_ws(L->m, gemv_splits(L->m, L->n)).total;
   return v > g ? v : g;
@@ -196,7 +197,8 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
   a.m = L->m;
   a.n = L->n;
   a.splits = splits;
-  return launch_status(launch_gemv(a, L->k_bits, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
+  return launch_status(
+      launch_gemv(a, L->k_bits, L->code_id, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
 }
 
 TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* X, int64_t ldx, float* Y,
@@ -207,7 +209,7 @@ TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* 
   if (!X || !Y) return TG_ERR_NULL;
   if (ldx < L->n || ldy < L->m) return TG_ERR_ARG;
   if (misaligned(X, 2) || misaligned(Y, 4)) return TG_ERR_ALIGN;
-  const int splits = gemm_splits(L->m, L->n, M, L->k_bits);
+  const int splits = gemm_splits(L->m, L->n, M, L->k_bits, L->code_id);
   const GemmWs w = gemm_ws(L->m, L->n, M, splits);
   if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
   if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
@@ -225,8 +227,8 @@ TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* 
   a.M = M;
   a.mpad = (M + 15) / 16 * 16;
   a.splits = splits;
-  return launch_status(launch_gemm_small(a, X, ldx, L->sign_in, L->k_bits, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0,
-                                         (hipStream_t)stream));
+  return launch_status(launch_gemm_small(a, X, ldx, L->sign_in, L->k_bits, L->code_id,
+                                         (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
 }
 
 TG_API int32_t rht_apply(int32_t n, int32_t rows, const uint16_t* in, float* out, const uint32_t* signs,
@@ -273,18 +275,18 @@ TG_API int32_t trellis_gemv_grouped(const tg_layer* layers, const tg_layer* d_la
 
 TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) {
   if (!L) return TG_ERR_NULL;
-  if (L->code_id != 0) return TG_ERR_CODE_ID;
+  if (L->code_id != 0 && L->code_id != 1) return TG_ERR_CODE_ID;
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || L->m % kTile != 0 || L->n % kTile != 0 || L->m > (1 << 22) || L->n > (1 << 22))
     return TG_ERR_SHAPE;
   if (!L->codes || !w_out) return TG_ERR_NULL;
   if (misaligned(L->codes, 4) || misaligned(w_out, 2)) return TG_ERR_ALIGN;
-  return launch_status(launch_decode(L->codes, w_out, L->m, L->n, L->k_bits, (hipStream_t)stream));
+  return launch_status(launch_decode(L->codes, w_out, L->m, L->n, L->k_bits, L->code_id, (hipStream_t)stream));
 }
 
 TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
-  if (code_id != 0) return TG_ERR_CODE_ID;
+  if (code_id != 0 && code_id != 1) return TG_ERR_CODE_ID;
   if (!out) return TG_ERR_NULL;
   if (misaligned(out, 2)) return TG_ERR_ALIGN;
-  return launch_status(launch_code_table(out, (hipStream_t)stream));
+  return launch_status(launch_code_table(code_id, out, (hipStream_t)stream));
 }

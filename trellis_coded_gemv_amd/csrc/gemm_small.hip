@@ -26,6 +26,15 @@
 // call by xt_prep_kernel, read from L2) is loaded once for 8 tiles. The 8
 // waves are summed through LDS at the end; split-K partials and the
 // last-arriving-workgroup epilogue are as in the batch-1 kernel.
+//
+// Pair code (code_id 1): a state covers two input columns, so one tile row of
+// 16 weights needs only 8 code words (k = 16) and one MFMA spans two adjacent
+// tiles of a tile row (tile columns 2C, 2C+1 -- contiguous in memory):
+// lane l decodes states 4(g%2)..+3 of row l%16 of tile 2C + g/2, and A holds
+// the rotated input pairs (x~0 - x~1, x~0 + x~1) of the same column pairs, so
+// the MFMA forms a (x~0 - x~1) + b (x~0 + x~1) = (a + b) x~0 + (b - a) x~1.
+// TG_FLAG_ROUND_WEIGHTS pairs the rounded weights (RNE(a+b), RNE(b-a)) with
+// the plain input pairs (x~0, x~1).
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
@@ -36,17 +45,37 @@
 
 namespace tg {
 
-// x~ = H diag(s_in) x / sqrt(128) for every row (rows >= M are zero), stored as fp16 pairs.
+// x~ = H diag(s_in) x / sqrt(128) for every row (rows >= M are zero), stored as
+// fp16 pairs: mode 0 (x~, x~) per column, row stride n words; mode 1 the rotated
+// column pairs (x~0 - x~1, x~0 + x~1) and mode 2 the plain pairs (x~0, x~1),
+// row stride n/2 words.
 __global__ __launch_bounds__(64) void xt_prep_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                       const uint32_t* __restrict__ sign_in, uint32_t* __restrict__ xt,
-                                                      int n, int M) {
+                                                      int n, int M, int mode) {
   const int lane = threadIdx.x, row = blockIdx.y;
-  const size_t ob = (size_t)row * n + (size_t)blockIdx.x * kBlock;
-  uint32_t d0 = 0u, d1 = 0u;
-  if (row < M) rht_in_block_dup(X + (size_t)row * ldx, sign_in, blockIdx.x * kBlock, lane, d0, d1);
-  xt[ob + lane] = d0;
-  xt[ob + lane + 64] = d1;
+  if (mode == 0) {
+    const size_t ob = (size_t)row * n + (size_t)blockIdx.x * kBlock;
+    uint32_t d0 = 0u, d1 = 0u;
+    if (row < M) rht_in_block_dup(X + (size_t)row * ldx, sign_in, blockIdx.x * kBlock, lane, d0, d1);
+    xt[ob + lane] = d0;
+    xt[ob + lane + 64] = d1;
+  } else {
+    uint32_t d = 0u;
+    if (row < M)
+      d = rht_in_block_pair(load_x_block(X + (size_t)row * ldx, sign_in, blockIdx.x * kBlock, lane), lane, mode == 1);
+    xt[(size_t)row * (n >> 1) + (size_t)blockIdx.x * 64 + pair_index(lane)] = d;
+  }
 }
+
+// Geometry of one MFMA step per code.
+template <int K, int CODE>
+struct MfmaGeom {
+  static constexpr int SPAN = CODE == 0 ? 1 : 2;          // tile columns per MFMA step
+  static constexpr int STEP = CODE == 0 ? K : 2 * K;      // stream bits between a lane's 4 windows
+  static constexpr int WPT = 8 * K;                       // code words per tile
+  static constexpr int LW = SPAN * K;                     // code words a lane loads per step
+  static constexpr int NLW = 3 * STEP > 16 ? 3 : 2;       // staged words a lane reads per tile
+};
 
 // Per-lane code words of one tile column step: lane l holds K words of tile
 // l/8 of the column (tile rows R0..R0+7), starting at word (l%8)*K.
@@ -73,19 +102,22 @@ __device__ __forceinline__ void stage_words(uint32_t* dst, const uint32_t (&w)[K
   }
 }
 
-// One wave: 8 tile rows (a 128-output block) x the tile columns col0, col0+step, ...
-// For each column the wave loads the 8 tiles (one contiguous 32K-byte run per
-// tile, 8 lanes per tile), restages them through its private LDS slice so that
-// each lane can pick the two (three) words its four windows need, decodes one
-// B operand per tile and issues MB MFMAs per tile against the column's x~ rows.
-template <int K, bool ROUND, int MB, int PF>
+// One wave: 8 tile rows (a 128-output block) x the steps col0, col0+step, ...
+// (a step is SPAN tile columns). For each step the wave loads the 8 x SPAN
+// tiles (one contiguous 32*K*SPAN-byte run per tile row, 8 lanes per run),
+// restages them through its private LDS slice so that each lane can pick the
+// two (three) words its four windows need, decodes one B operand per tile row
+// and issues MB MFMAs per tile row against the step's x~ rows.
+template <int K, int CODE, bool ROUND, int MB, int PF>
 __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, int ncol, int cstep, uint32_t* slice,
                                           float4_t (&acc)[8][MB]) {
-  constexpr int NLW = K >= 6 ? 3 : 2;   // words a lane needs per tile
-  constexpr int WPT = 8 * K;             // words per tile
+  using G = MfmaGeom<K, CODE>;
+  constexpr int NLW = G::NLW, WPT = G::WPT, LW = G::LW, SPAN = G::SPAN, STEP = G::STEP;
   const int lane = threadIdx.x & 63;
   const int jrow = lane & 15, g = lane >> 4;
-  const int b0 = K * (16 * jrow + 4 * g);
+  // first stream bit of the lane's four windows, and the tile of the step they lie in
+  const int b0 = CODE == 0 ? K * (16 * jrow + 4 * g) : 2 * K * (8 * jrow + 4 * (g & 1));
+  const int toff = CODE == 0 ? 0 : (g >> 1) * WPT;
   const int q0 = b0 & 31, j0 = b0 >> 5;
   int widx[NLW];
   uint32_t shift;
@@ -99,25 +131,29 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
 #pragma unroll
     for (int i = 0; i < NLW; ++i) widx[i] = (j0 + i) % WPT;
   }
+#pragma unroll
+  for (int i = 0; i < NLW; ++i) widx[i] += toff;
   const size_t n16 = (size_t)(a.n >> 4);
+  const size_t xrow = (size_t)(a.n / SPAN);                  // words per x~ row
   const int tl = lane >> 3;                                  // tile row this lane loads
-  const uint32_t* __restrict__ cptr = a.codes + ((size_t)(ob * 8 + tl) * n16 + col0) * WPT + (lane & 7) * K;
-  const uint32_t* __restrict__ xptr = a.xt + (size_t)jrow * a.n + 4 * g + (size_t)col0 * 16;
+  const uint32_t* __restrict__ cptr =
+      a.codes + ((size_t)(ob * 8 + tl) * n16 + (size_t)col0 * SPAN) * WPT + (lane & 7) * LW;
+  const uint32_t* __restrict__ xptr = a.xt + (size_t)jrow * xrow + 4 * g + (size_t)col0 * 16;
   const uint32_t* __restrict__ cfirst = cptr;
   const uint32_t* __restrict__ xfirst = xptr;
-  const size_t cadv = (size_t)cstep * WPT, xadv = (size_t)cstep * 16;
+  const size_t cadv = (size_t)cstep * SPAN * WPT, xadv = (size_t)cstep * 16;
 
-  // Prefetch ring; out-of-range columns re-read the first column (valid addresses,
+  // Prefetch ring; out-of-range steps re-read the first step (valid addresses,
   // and every path issues the same loads so the waits stay exact).
-  uint32_t cw[PF][K];
+  uint32_t cw[PF][LW];
   u32x4 xa[PF][MB];
   int issued = 0;
-  auto issue = [&](uint32_t(&dst)[K], u32x4(&xd)[MB]) {
+  auto issue = [&](uint32_t(&dst)[LW], u32x4(&xd)[MB]) {
     const bool ok = issued < ncol;
-    load_column<K>(ok ? cptr : cfirst, dst);
+    load_column<LW>(ok ? cptr : cfirst, dst);
     const uint32_t* xq = ok ? xptr : xfirst;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) xd[mb] = *reinterpret_cast<const u32x4*>(xq + (size_t)(16 * mb) * a.n);
+    for (int mb = 0; mb < MB; ++mb) xd[mb] = *reinterpret_cast<const u32x4*>(xq + (size_t)(16 * mb) * xrow);
     cptr += cadv;
     xptr += xadv;
     ++issued;
@@ -130,14 +166,14 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       if (i0 + p < ncol) {
-        // stage the column's words, read back the words of all 8 tiles,
+        // stage the step's words, read back the words of all 8 tile rows,
         // decode all 8 B operands, then issue the MFMAs back to back
-        stage_words<K>(slice + lane * K, cw[p]);   // lane l's K words sit at word l*K
+        stage_words<LW>(slice + lane * LW, cw[p]);   // lane l's LW words sit at word l*LW
         uint32_t wv[8][NLW];
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-          for (int k = 0; k < NLW; ++k) wv[t][k] = slice[t * WPT + widx[k]];
+          for (int k = 0; k < NLW; ++k) wv[t][k] = slice[t * SPAN * WPT + widx[k]];
 #pragma unroll
         for (int t0 = 0; t0 < 8; t0 += TG_MFMA_GROUP) {
         uint32_t bw[TG_MFMA_GROUP][4];
@@ -149,11 +185,12 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
           if constexpr (NLW == 3) r2 = alignbit(wv[t][1], wv[t][2], shift);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int P = K * e;
+            const int P = STEP * e;
             const uint32_t st = P <= 16 ? ubfe(r1, 16 - P, 16) : ubfe(alignbit(r1, r2, 48 - P), 0, 16);
             const uint32_t u = code_halves(st, cr);
-            if constexpr (ROUND) bw[tt][e] = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
-            else bw[tt][e] = u;
+            if constexpr (!ROUND) bw[tt][e] = u;
+            else if constexpr (CODE == 0) bw[tt][e] = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
+            else bw[tt][e] = pair_weights_rne(u);
           }
         }
 #pragma unroll
@@ -171,20 +208,21 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
   }
 }
 
-template <int K, bool ROUND, int MB>
+template <int K, int CODE, bool ROUND, int MB>
 __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
   extern __shared__ uint32_t lds[];
   constexpr int PF = 2;
-  constexpr int WPT = 8 * K;
+  using G = MfmaGeom<K, CODE>;
+  constexpr int SLICE = 8 * G::SPAN * G::WPT;   // staged words per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int ob = bid / a.splits, split = bid - ob * a.splits;
-  const int ncols = a.n >> 4;
+  const int ncols = (a.n >> 4) / G::SPAN;   // MFMA steps along the input
   const int c0 = (int)((int64_t)split * ncols / a.splits);
   const int c1 = (int)((int64_t)(split + 1) * ncols / a.splits);
-  // wave w takes columns c0+w, c0+w+8, ... of the chunk
+  // wave w takes steps c0+w, c0+w+8, ... of the chunk
   const int nmine = c1 - c0 > wave ? (c1 - c0 - wave + kGemvWaves - 1) / kGemvWaves : 0;
 
   float4_t acc[8][MB];
@@ -192,11 +230,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[t][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-  if (nmine > 0) gemm_wave<K, ROUND, MB, PF>(a, ob, c0 + wave, nmine, kGemvWaves, lds + wave * 8 * WPT, acc);
+  if (nmine > 0) gemm_wave<K, CODE, ROUND, MB, PF>(a, ob, c0 + wave, nmine, kGemvWaves, lds + wave * SLICE, acc);
 
   // Sum the 8 waves' accumulators: a fixed tree through LDS (4 -> 2 -> 1 waves),
   // one 16-row group at a time to bound the LDS footprint.
-  float* red = reinterpret_cast<float*>(lds + kGemvWaves * 8 * WPT);   // [4][8*4][64]
+  float* red = reinterpret_cast<float*>(lds + kGemvWaves * SLICE);   // [4][8*4][64]
   constexpr int NV = 8 * 4;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -265,46 +303,52 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
   if (threadIdx.x == 0) reset_counter(&a.counters[ob]);
 }
 
-template <int K, int MB>
+template <int K, int CODE, int MB>
 size_t gemm_lds_bytes() {
-  const size_t slices = (size_t)kGemvWaves * 8 * 8 * K * 4;   // per-wave code staging
+  const size_t slices = (size_t)kGemvWaves * 8 * MfmaGeom<K, CODE>::SPAN * 8 * K * 4;   // per-wave code staging
   const size_t red = 4ull * 8 * 4 * 64 * 4;                     // tree reduction buffer (one row group)
   const size_t ybuf = 16ull * MB * 128 * 4 + 16;
   const size_t a = slices + red;
   return a > ybuf ? a : ybuf;
 }
 
-template <int K, bool ROUND, int MB>
+template <int K, int CODE, bool ROUND, int MB>
 static void launch_main(const GemmArgs& a, hipStream_t s) {
   const int grid = (a.m >> 7) * a.splits;
-  const size_t lds = gemm_lds_bytes<K, MB>();
-  hipLaunchKernelGGL((gemm_small_kernel<K, ROUND, MB>), dim3(grid), dim3(kGemvThreads), lds, s, a);
+  const size_t lds = gemm_lds_bytes<K, CODE, MB>();
+  hipLaunchKernelGGL((gemm_small_kernel<K, CODE, ROUND, MB>), dim3(grid), dim3(kGemvThreads), lds, s, a);
 }
 
-template <int K, bool ROUND>
+template <int K, int CODE, bool ROUND>
 static void launch_mb(const GemmArgs& a, hipStream_t s) {
   switch (a.mpad / 16) {
-    case 1: launch_main<K, ROUND, 1>(a, s); break;
-    case 2: launch_main<K, ROUND, 2>(a, s); break;
-    case 3: launch_main<K, ROUND, 3>(a, s); break;
-    default: launch_main<K, ROUND, 4>(a, s); break;
+    case 1: launch_main<K, CODE, ROUND, 1>(a, s); break;
+    case 2: launch_main<K, CODE, ROUND, 2>(a, s); break;
+    case 3: launch_main<K, CODE, ROUND, 3>(a, s); break;
+    default: launch_main<K, CODE, ROUND, 4>(a, s); break;
   }
 }
 
-hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in, int k_bits,
-                             bool round_weights, hipStream_t s) {
-  hipLaunchKernelGGL(xt_prep_kernel, dim3(a.n / kBlock, a.mpad), dim3(64), 0, s, X, ldx, sign_in,
-                     const_cast<uint32_t*>(a.xt), a.n, a.M);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+template <int CODE>
+static hipError_t launch_code(const GemmArgs& a, int k_bits, bool round_weights, hipStream_t s) {
 #define TG_CASE(K) \
-  case K: round_weights ? launch_mb<K, true>(a, s) : launch_mb<K, false>(a, s); break;
+  case K: round_weights ? launch_mb<K, CODE, true>(a, s) : launch_mb<K, CODE, false>(a, s); break;
   switch (k_bits) {
     TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
     default: return hipErrorInvalidValue;
   }
 #undef TG_CASE
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in, int k_bits,
+                             int code_id, bool round_weights, hipStream_t s) {
+  const int mode = code_id == 0 ? 0 : (round_weights ? 2 : 1);
+  hipLaunchKernelGGL(xt_prep_kernel, dim3(a.n / kBlock, a.mpad), dim3(64), 0, s, X, ldx, sign_in,
+                     const_cast<uint32_t*>(a.xt), a.n, a.M, mode);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return code_id == 0 ? launch_code<0>(a, k_bits, round_weights, s) : launch_code<1>(a, k_bits, round_weights, s);
 }
 
 }  // namespace tg

@@ -22,6 +22,10 @@
 // lo+hi is used exactly inside the fp32 product; TG_FLAG_ROUND_WEIGHTS
 // instead rounds lo+hi to fp16 first (one v_add_f16 more per weight).
 //
+// Pair code (code_id 1): one state per two weights, so a lane's 64 weights
+// take 32 windows, and the fused product a (x~0 - x~1) + b (x~0 + x~1) needs
+// one v_dot2c per state: about half the decode work per weight of code 0.
+//
 // Prologue: each workgroup transforms its input chunk (signs by XOR on the
 // fp16 sign bit, 128-point FWHT in registers with lane shuffles, 1/sqrt(128))
 // into LDS as fp16 pairs. Epilogue: lane -> wave reduction by lane shuffles,
@@ -98,6 +102,37 @@ __device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32
   }
 }
 
+// Pair code (code_id 1): the lane's 64 weights are 32 states, state s at
+// stream bit 2K*s (two weights per trellis step), weights 2s and 2s+1 of the
+// lane's run = columns 2(s%8), 2(s%8)+1 of row s/8. Per state: one window
+// extract, v_mad_u32_u24, v_and_or_b32 and one v_dot2c_f32_f16 against the
+// rotated input pair (x~0 - x~1, x~0 + x~1) -- two weights per dot.
+// ROUND: the rounded pair (RNE(a+b), RNE(b-a)) against the plain pair (x~0, x~1).
+//   xp : 8 pair words for the tile's 8 column pairs
+template <int K, bool ROUND>
+__device__ __forceinline__ void decode_dot_pair_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xp)[8],
+                                                   float (&acc)[4], const CodeRegs& cr) {
+  constexpr int NW = 2 * K;
+  auto word = [&](int j) -> uint32_t { return j < NW ? w[j] : nb; };
+#pragma unroll
+  for (int sl = 0; sl < 32; ++sl) {
+    const int p = 2 * K * sl;
+    const int j = p >> 5, q = p & 31;
+    uint32_t s;
+    if (q <= 16) {
+      s = ubfe(word(j), 16 - q, 16);
+    } else {
+      s = ubfe(alignbit(word(j), word(j + 1), 16), 32 - q, 16);
+    }
+    const uint32_t u = code_halves(s, cr);
+    if constexpr (ROUND) {
+      acc[sl >> 3] = dot2(pair_weights_rne(u), xp[sl & 7], acc[sl >> 3]);
+    } else {
+      acc[sl >> 3] = dot2(u, xp[sl & 7], acc[sl >> 3]);
+    }
+  }
+}
+
 // Sum acc[g] over the 16 tile slots of the wave (lane bits 2..5) with a
 // transposing reduction: the exchanges over bits 2 and 3 each halve the number
 // of values a lane carries, so 5 shuffles replace 16. On return lanes 0..15
@@ -117,10 +152,13 @@ __device__ __forceinline__ int reduced_row(int lane) {
   return 4 * (lane & 3) + 2 * ((lane >> 2) & 1) + ((lane >> 3) & 1);
 }
 
-__device__ __forceinline__ void read_xx(const uint32_t* xx_lds, int tile, uint32_t (&xv)[16]) {
-  const u32x4* xs = reinterpret_cast<const u32x4*>(xx_lds + tile * 16);
+// The NX input words of one tile column (NX = 16 fp16 pairs (x~, x~) for
+// code 0, 8 column-pair words for code 1).
+template <int NX>
+__device__ __forceinline__ void read_xx(const uint32_t* xx_lds, int tile, uint32_t (&xv)[NX]) {
+  const u32x4* xs = reinterpret_cast<const u32x4*>(xx_lds + tile * NX);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < NX / 4; ++v) {
     const u32x4 t = xs[v];
     xv[4 * v + 0] = t[0];
     xv[4 * v + 1] = t[1];
@@ -131,9 +169,11 @@ __device__ __forceinline__ void read_xx(const uint32_t* xx_lds, int tile, uint32
 
 // One workgroup = 8 tile rows (a 128-output block) x one input chunk, with P
 // waves per tile row that take interleaved 16-tile steps of the chunk.
-template <int K, bool ROUND, int PF, int P>
+template <int K, int CODE, bool ROUND, int PF, int P>
 __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int split, uint32_t* lds) {
   constexpr int NW = 2 * K;
+  constexpr int NX = CODE == 0 ? 16 : 8;   // input words per tile column
+  constexpr int XB = NX * 8;               // input words per 128-block
   constexpr int WAVES = 8 * P;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rw = wave & 7, kp = wave >> 3;     // tile row within the block, step phase
@@ -149,7 +189,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   const uint32_t* __restrict__ rowp =
       a.codes + ((size_t)R * (size_t)(a.n >> 4) + (size_t)blk0 * 8) * (size_t)(8 * K) + (size_t)lane * NW;
 
-  uint32_t* xx_lds = lds;                                        // [2*nsteps blocks][128] pairs
+  uint32_t* xx_lds = lds;                                        // [2*nsteps blocks][XB] words
   float* ybuf = reinterpret_cast<float*>(lds + nsteps * 256);    // [128]
   float* red = ybuf + 128;                                       // [P-1][128]
   uint32_t* flag = lds + nsteps * 256 + 128 * P;
@@ -175,20 +215,29 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
 
   // Prologue: x~ for the chunk, padded with zeros to whole steps.
   for (int bb = wave; bb < 2 * nsteps; bb += WAVES) {
-    uint32_t d0 = 0u, d1 = 0u;
-    if (bb < cb) {
-      const XBlock xb = bb == wave ? xfirst : load_x_block(a.x, a.sign_in, (blk0 + bb) * kBlock, lane);
-      rht_in_block_dup(xb, lane, d0, d1);
+    if constexpr (CODE == 0) {
+      uint32_t d0 = 0u, d1 = 0u;
+      if (bb < cb) {
+        const XBlock xb = bb == wave ? xfirst : load_x_block(a.x, a.sign_in, (blk0 + bb) * kBlock, lane);
+        rht_in_block_dup(xb, lane, d0, d1);
+      }
+      xx_lds[bb * XB + lane] = d0;
+      xx_lds[bb * XB + lane + 64] = d1;
+    } else {
+      uint32_t d = 0u;
+      if (bb < cb) {
+        const XBlock xb = bb == wave ? xfirst : load_x_block(a.x, a.sign_in, (blk0 + bb) * kBlock, lane);
+        d = rht_in_block_pair(xb, lane, !ROUND);
+      }
+      xx_lds[bb * XB + pair_index(lane)] = d;
     }
-    xx_lds[bb * kBlock + lane] = d0;
-    xx_lds[bb * kBlock + lane + 64] = d1;
   }
   __syncthreads();
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const CodeRegs cr;
   // x~ of the current and the next step (double buffer, alternating with p).
-  uint32_t xv[1 + TG_GEMV_XDB][16];
+  uint32_t xv[1 + TG_GEMV_XDB][NX];
   if (TG_GEMV_XDB && nls > 0) read_xx(xx_lds, kp * 16 + jslot, xv[0]);
   for (int ls0 = 0; ls0 < nls; ls0 += PF) {
 #pragma unroll
@@ -202,7 +251,8 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
           read_xx(xx_lds, (kp + ls * P) * 16 + jslot, xv[0]);
         }
         const uint32_t nbw = quad_rotate_next(buf[p][0]);
-        decode_dot_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
+        if constexpr (CODE == 0) decode_dot_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
+        else decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
       }
       issue(ls + PF, buf[p]);   // refill after use: the ring needs no register copies
     }
@@ -262,12 +312,26 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return (nblk & 7) == 0 ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
 }
 
-template <int K, bool ROUND, int PF, int P>
+template <int K, int CODE, bool ROUND, int PF, int P>
 __global__ __launch_bounds__(64 * 8 * P) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int ob = bid / a.splits;
-  gemv_workgroup<K, ROUND, PF, P>(a, ob, bid - ob * a.splits, lds);
+  gemv_workgroup<K, CODE, ROUND, PF, P>(a, ob, bid - ob * a.splits, lds);
+}
+
+template <int CODE, bool ROUND>
+__device__ __forceinline__ void grouped_dispatch(const GemvArgs& a, int k_bits, int ob, int split, uint32_t* lds) {
+  switch (k_bits) {
+    case 1: gemv_workgroup<1, CODE, ROUND, gemv_pf<1>(), kGemvP>(a, ob, split, lds); break;
+    case 2: gemv_workgroup<2, CODE, ROUND, gemv_pf<2>(), kGemvP>(a, ob, split, lds); break;
+    case 3: gemv_workgroup<3, CODE, ROUND, gemv_pf<3>(), kGemvP>(a, ob, split, lds); break;
+    case 4: gemv_workgroup<4, CODE, ROUND, gemv_pf<4>(), kGemvP>(a, ob, split, lds); break;
+    case 5: gemv_workgroup<5, CODE, ROUND, gemv_pf<5>(), kGemvP>(a, ob, split, lds); break;
+    case 6: gemv_workgroup<6, CODE, ROUND, gemv_pf<6>(), kGemvP>(a, ob, split, lds); break;
+    case 7: gemv_workgroup<7, CODE, ROUND, gemv_pf<7>(), kGemvP>(a, ob, split, lds); break;
+    default: gemv_workgroup<8, CODE, ROUND, gemv_pf<8>(), kGemvP>(a, ob, split, lds); break;
+  }
 }
 
 template <bool ROUND>
@@ -294,37 +358,34 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
   a.m = L.m;
   a.n = L.n;
   a.splits = g.splits;
-  switch (L.k_bits) {
-    case 1: gemv_workgroup<1, ROUND, gemv_pf<1>(), kGemvP>(a, ob, split, lds); break;
-    case 2: gemv_workgroup<2, ROUND, gemv_pf<2>(), kGemvP>(a, ob, split, lds); break;
-    case 3: gemv_workgroup<3, ROUND, gemv_pf<3>(), kGemvP>(a, ob, split, lds); break;
-    case 4: gemv_workgroup<4, ROUND, gemv_pf<4>(), kGemvP>(a, ob, split, lds); break;
-    case 5: gemv_workgroup<5, ROUND, gemv_pf<5>(), kGemvP>(a, ob, split, lds); break;
-    case 6: gemv_workgroup<6, ROUND, gemv_pf<6>(), kGemvP>(a, ob, split, lds); break;
-    case 7: gemv_workgroup<7, ROUND, gemv_pf<7>(), kGemvP>(a, ob, split, lds); break;
-    default: gemv_workgroup<8, ROUND, gemv_pf<8>(), kGemvP>(a, ob, split, lds); break;
-  }
+  if (L.code_id == 0) grouped_dispatch<0, ROUND>(a, L.k_bits, ob, split, lds);
+  else grouped_dispatch<1, ROUND>(a, L.k_bits, ob, split, lds);
 }
 
-template <int K, bool ROUND>
+template <int K, int CODE, bool ROUND>
 static hipError_t launch_k(const GemvArgs& a, hipStream_t s) {
   constexpr int PF = gemv_pf<K>();
   const int nb128 = a.n >> 7;
   const int max_chunk = (nb128 + a.splits - 1) / a.splits;
   const int grid = (a.m >> 7) * a.splits;
-  hipLaunchKernelGGL((gemv_kernel<K, ROUND, PF, kGemvP>), dim3(grid), dim3(64 * 8 * kGemvP),
+  hipLaunchKernelGGL((gemv_kernel<K, CODE, ROUND, PF, kGemvP>), dim3(grid), dim3(64 * 8 * kGemvP),
                      gemv_lds_bytes(max_chunk), s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv(const GemvArgs& a, int k_bits, bool round_weights, hipStream_t s) {
+template <int CODE>
+static hipError_t launch_code(const GemvArgs& a, int k_bits, bool round_weights, hipStream_t s) {
 #define TG_CASE(K) \
-  case K: return round_weights ? launch_k<K, true>(a, s) : launch_k<K, false>(a, s);
+  case K: return round_weights ? launch_k<K, CODE, true>(a, s) : launch_k<K, CODE, false>(a, s);
   switch (k_bits) {
     TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
     default: return hipErrorInvalidValue;
   }
 #undef TG_CASE
+}
+
+hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_weights, hipStream_t s) {
+  return code_id == 0 ? launch_code<0>(a, k_bits, round_weights, s) : launch_code<1>(a, k_bits, round_weights, s);
 }
 
 hipError_t launch_grouped(const GroupedArgs& g, int max_ob, int max_n, hipStream_t s) {

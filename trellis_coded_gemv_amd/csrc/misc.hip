@@ -7,27 +7,38 @@ namespace tg {
 
 // One thread per weight, in row-major output order (coalesced 16-bit stores).
 // The state is read by random access: the 16 bits starting at stream bit K*t
-// of the tile, taken cyclically ("Trellis Quantization" lecture, Part eight).
+// of the tile (2K*(t/2) for the pair code), taken cyclically ("Trellis
+// Quantization" lecture, Part eight).
 __global__ __launch_bounds__(256) void decode_kernel(const uint32_t* __restrict__ codes, uint16_t* __restrict__ out,
-                                                     int m, int n, int K) {
+                                                     int m, int n, int K, int code_id) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)m * (size_t)n) return;
   const int o = (int)(idx / (size_t)n), i = (int)(idx - (size_t)o * n);
   const int wpt = 8 * K;
   const uint32_t* tile = codes + ((size_t)(o >> 4) * (size_t)(n >> 4) + (size_t)(i >> 4)) * (size_t)wpt;
   const int t = 16 * (o & 15) + (i & 15);
-  const int p = K * t;
+  const int p = code_id == 0 ? K * t : 2 * K * (t >> 1);
   const int j = p >> 5, q = p & 31;
   const uint64_t v = ((uint64_t)tile[j] << 32) | (uint64_t)tile[(j + 1) % wpt];
   const uint32_t state = (uint32_t)(v >> (48 - q)) & 0xFFFFu;
   const CodeRegs cr;
-  out[idx] = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(state, cr)));
+  const uint32_t u = code_halves(state, cr);
+  if (code_id == 0) out[idx] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
+  else out[idx] = (uint16_t)(pair_weights_rne(u) >> (16 * (t & 1)));
 }
 
-__global__ __launch_bounds__(256) void code_table_kernel(uint16_t* __restrict__ out) {
+// code_id 0: out[S] = weight of state S; code_id 1: out[2S], out[2S+1] = the state's weight pair.
+__global__ __launch_bounds__(256) void code_table_kernel(uint16_t* __restrict__ out, int code_id) {
   const uint32_t s = blockIdx.x * 256 + threadIdx.x;
   const CodeRegs cr;
-  out[s] = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(s, cr)));
+  const uint32_t u = code_halves(s, cr);
+  if (code_id == 0) {
+    out[s] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
+  } else {
+    const uint32_t w = pair_weights_rne(u);
+    out[2 * s] = (uint16_t)w;
+    out[2 * s + 1] = (uint16_t)(w >> 16);
+  }
 }
 
 // One wave per (row, 128-block). inverse == 0: H diag(s) x; inverse == 1: diag(s) H x.
@@ -55,16 +66,16 @@ __global__ __launch_bounds__(64) void rht_kernel(const uint16_t* __restrict__ in
   out[base + lane + 64] = v1;
 }
 
-hipError_t launch_decode(const uint32_t* codes, uint16_t* out, int m, int n, int k_bits, hipStream_t s) {
+hipError_t launch_decode(const uint32_t* codes, uint16_t* out, int m, int n, int k_bits, int code_id, hipStream_t s) {
   const size_t total = (size_t)m * (size_t)n;
   const size_t blocks = (total + 255) / 256;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, out, m, n, k_bits);
+  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, out, m, n, k_bits, code_id);
   return hipGetLastError();
 }
 
-hipError_t launch_code_table(uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(code_table_kernel, dim3(256), dim3(256), 0, s, out);
+hipError_t launch_code_table(int code_id, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(code_table_kernel, dim3(256), dim3(256), 0, s, out, code_id);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Code constants (code_id 0).
+// Code constants (shared by code_id 0 and the pair code, code_id 1).
 constexpr uint32_t kMul = 0x009E3779u;   // 24-bit LCG multiplier: one full-rate v_mad_u32_u24
 constexpr uint32_t kAdd = 0x7F4A7C15u;
 constexpr uint32_t kMask = 0x8FFF8FFFu;  // sign, 2 low exponent bits, 10 fraction bits per half
@@ -133,6 +133,38 @@ __device__ __forceinline__ void rht_in_block_dup(XBlock xb, int lane, uint32_t& 
 __device__ __forceinline__ void rht_in_block_dup(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
                                                  int base, int lane, uint32_t& d0, uint32_t& d1) {
   rht_in_block_dup(load_x_block(x, sign_in, base, lane), lane, d0, d1);
+}
+
+// Pair code (code_id 1): a state carries the weights of input columns 2j and
+// 2j+1, and w0 x0 + w1 x1 = a (x0 - x1) + b (x0 + x1) for the halves a, b of
+// the state's code word (w0 = a + b, w1 = b - a). The input side is therefore
+// kept as one fp16 pair per column pair. Lane 2i returns pair i (elements 2i,
+// 2i+1 of the block), lane 2i+1 returns pair 32+i (elements 64+2i, 64+2i+1).
+__device__ __forceinline__ int pair_index(int lane) { return (lane & 1) ? 32 + (lane >> 1) : (lane >> 1); }
+
+// rotate: (x~0 - x~1, x~0 + x~1); otherwise the plain pair (x~0, x~1). Low half first.
+__device__ __forceinline__ uint32_t rht_in_block_pair(XBlock xb, int lane, bool rotate) {
+  const uint16_t b0 = xb.b0 ^ (uint16_t)(((xb.s0 >> ((xb.base + lane) & 31)) & 1u) << 15);
+  const uint16_t b1 = xb.b1 ^ (uint16_t)(((xb.s1 >> ((xb.base + lane + 64) & 31)) & 1u) << 15);
+  float v0 = half_bits_to_float(b0), v1 = half_bits_to_float(b1);
+  fwht128_wave(v0, v1, lane);
+  v0 *= kRsqrt128;
+  v1 *= kRsqrt128;
+  const float p0 = shfl_xor(v0, 1), p1 = shfl_xor(v1, 1);
+  const bool odd = (lane & 1) != 0;
+  const float e = odd ? p1 : v0;   // even element of the pair
+  const float o = odd ? v1 : p0;   // odd element
+  const float lo = rotate ? e - o : e;
+  const float hi = rotate ? e + o : o;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+// Pair code weights rounded to fp16: (RNE(a + b), RNE(b - a)) from the code word's halves.
+__device__ __forceinline__ uint32_t pair_weights_rne(uint32_t u) {
+  const half2_t p = __builtin_bit_cast(half2_t, u);
+  const _Float16 w0 = p[0] + p[1], w1 = p[1] - p[0];
+  return (uint32_t)__builtin_bit_cast(uint16_t, w0) | ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
 }
 
 // Output-side epilogue of one 128-block held by a wave:

@@ -57,7 +57,7 @@ struct GemmArgs {
   const uint32_t* codes;
   const uint16_t* scales;
   const uint32_t* sign_out;
-  const uint32_t* xt;   // [mpad][n] fp16 pairs (x~, x~) prepared by the input transform kernel
+  const uint32_t* xt;   // [mpad][n] (code 0) or [mpad][n/2] (code 1) fp16 pair words from the input transform
   float* y;
   int64_t ldy;
   float* partials;      // [splits][M][m]
@@ -65,14 +65,14 @@ struct GemmArgs {
   int32_t m, n, M, mpad, splits;
 };
 
-hipError_t launch_gemv(const GemvArgs& a, int k_bits, bool round_weights, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_weights, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, int max_ob, int max_n, hipStream_t s);
 hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in,
-                             int k_bits, bool round_weights, hipStream_t s);
+                             int k_bits, int code_id, bool round_weights, hipStream_t s);
 hipError_t launch_rht(int n, int rows, const uint16_t* in, float* out, const uint32_t* signs, bool inverse,
                       hipStream_t s);
-hipError_t launch_decode(const uint32_t* codes, uint16_t* out, int m, int n, int k_bits, hipStream_t s);
-hipError_t launch_code_table(uint16_t* out, hipStream_t s);
+hipError_t launch_decode(const uint32_t* codes, uint16_t* out, int m, int n, int k_bits, int code_id, hipStream_t s);
+hipError_t launch_code_table(int code_id, uint16_t* out, hipStream_t s);
 
 // LDS bytes a GEMV workgroup needs for a chunk of `chunk_blocks` 128-blocks.
 // The x~ region doubles as [8P][128] fp32 per-wave sums in the final reduction.

@@ -59,13 +59,16 @@ class LayerArrays:
         return int(self.codes.nbytes)
 
 
-def make_layer(m: int, n: int, k_bits: int, seed: int, tensor: int = 0, copy: int = 0) -> LayerArrays:
+def make_layer(m: int, n: int, k_bits: int, seed: int, tensor: int = 0, copy: int = 0,
+               code_id: int = 0) -> LayerArrays:
+    """Random-bitstream layer; the code id only labels how the stream is decoded
+    (both codes store 8*K words per 16x16 tile)."""
     codes = _rng(seed, tensor, copy, F_CODES).integers(
         0, 1 << 32, size=words_per_layer(m, n, k_bits), dtype=np.uint32)
     scales = _rng(seed, tensor, copy, F_SCALES).uniform(0.5, 1.5, size=m).astype(np.float16).view(np.uint16)
     sign_in = _rng(seed, tensor, copy, F_SIGN_IN).integers(0, 1 << 32, size=(n + 31) // 32, dtype=np.uint32)
     sign_out = _rng(seed, tensor, copy, F_SIGN_OUT).integers(0, 1 << 32, size=(m + 31) // 32, dtype=np.uint32)
-    return LayerArrays(m, n, k_bits, codes, scales, sign_in, sign_out)
+    return LayerArrays(m, n, k_bits, codes, scales, sign_in, sign_out, code_id)
 
 
 def make_x(n: int, seed: int, tensor: int = 0, copy: int = 0, rows: int = 1) -> np.ndarray:
@@ -129,12 +132,13 @@ class MoEWorkload:
     def kbits(self, expert: int, which: str) -> int:
         return draw_kbits(self.seed, self.tensor_index(expert, which), self.k_choices)
 
-    def layer(self, expert: int, which: str, copy: int = 0) -> LayerArrays:
+    def layer(self, expert: int, which: str, copy: int = 0, code_id: int = 0) -> LayerArrays:
         m, n = self.shape(which)
-        return make_layer(m, n, self.kbits(expert, which), self.seed, self.tensor_index(expert, which), copy)
+        return make_layer(m, n, self.kbits(expert, which), self.seed, self.tensor_index(expert, which), copy,
+                          code_id)
 
-    def all_layers(self, copy: int = 0) -> List[LayerArrays]:
-        return [self.layer(e, w, copy) for e in range(self.experts) for w in ("gate", "up", "down")]
+    def all_layers(self, copy: int = 0, code_id: int = 0) -> List[LayerArrays]:
+        return [self.layer(e, w, copy, code_id) for e in range(self.experts) for w in ("gate", "up", "down")]
 
     def routing(self) -> np.ndarray:
         return draw_routing(self.seed, self.tokens, self.experts, self.top_k)
