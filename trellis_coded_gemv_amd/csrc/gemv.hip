@@ -26,9 +26,9 @@
 // take 32 windows, and the fused product a (x~0 - x~1) + b (x~0 + x~1) needs
 // one v_dot2c per state: about half the decode work per weight of code 0.
 //
-// Prologue: each workgroup transforms its input chunk (signs by XOR on the
-// fp16 sign bit, 128-point FWHT in registers with lane shuffles, 1/sqrt(128))
-// into LDS as fp16 pairs. Epilogue: lane -> wave reduction by lane shuffles,
+// Prologue: each workgroup transforms its input chunk (signs, 128-point
+// Walsh-Hadamard transform, 1/sqrt(128)) into LDS as fp16 pairs, eight lanes
+// per block with one fp32 exchange through LDS and no lane shuffles. Epilogue: lane -> wave reduction by lane shuffles,
 // then either a direct output transform (1 split) or fp32 split-K partials in
 // the workspace; the last-arriving workgroup of a block sums them in a fixed
 // order and applies scale, output FWHT and signs. No waiting on other
@@ -194,10 +194,16 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   float* red = ybuf + 128;                                       // [P-1][128]
   uint32_t* flag = lds + nsteps * 256 + 128 * P;
 
-  // The first input block of this wave is fetched before the code prefetch:
-  // loads complete in order, so fetching it later would make the transform
-  // below wait for every prefetched code word as well.
-  const XBlock xfirst = load_x_block(a.x, a.sign_in, (blk0 + (wave < cb ? wave : cb - 1)) * kBlock, lane);
+  // This lane's part of the input chunk (8 lanes per 128-block, 16 elements
+  // per lane) is fetched before the code prefetch: loads complete in order,
+  // so fetching it later would make the transform below wait for every
+  // prefetched code word as well. Blocks past the chunk read its last block
+  // (valid addresses) and are zeroed below.
+  static_assert(kMaxChunkBlocks <= 8 * WAVES, "one prologue pass covers the largest chunk");
+  const int nbp = 2 * nsteps;                       // blocks incl. the zero padding to whole steps
+  const int xb = 8 * wave + (lane >> 3), xs = lane & 7;
+  const int xfirst = (blk0 + (xb < cb ? xb : cb - 1)) * kBlock + 16 * xs;
+  const X16 xraw = load_x16(a.x, a.sign_in, xfirst);
   __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the prefetch below
 
   // Prefetch ring. Every issue is unconditional (out-of-range steps and tiles
@@ -213,23 +219,41 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, buf[p]);
 
-  // Prologue: x~ for the chunk, padded with zeros to whole steps.
-  for (int bb = wave; bb < 2 * nsteps; bb += WAVES) {
-    if constexpr (CODE == 0) {
-      uint32_t d0 = 0u, d1 = 0u;
-      if (bb < cb) {
-        const XBlock xb = bb == wave ? xfirst : load_x_block(a.x, a.sign_in, (blk0 + bb) * kBlock, lane);
-        rht_in_block_dup(xb, lane, d0, d1);
+  // Prologue: x~ of the chunk into LDS (zeros for the padding blocks), in the
+  // word layout the decode loop reads. The fp32 exchange uses the x~ area
+  // itself; the words are written only after every wave has read its part.
+  {
+    const bool active = xb < nbp, live = xb < cb;
+    float* sc = reinterpret_cast<float*>(xx_lds) + xb * kBlock;
+    float v[16];
+    x16_phase1(xraw, xfirst, v);
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        reinterpret_cast<float4_t*>(sc + 16 * xs)[i] = float4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    }
+    __builtin_amdgcn_wave_barrier();
+    float e[8], o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float2 t = active ? *reinterpret_cast<const float2*>(sc + 16 * j + 2 * xs) : float2{0.f, 0.f};
+      e[j] = live ? t.x : 0.f;
+      o[j] = live ? t.y : 0.f;
+    }
+    x16_phase2(e, o);
+    __syncthreads();   // every wave has read its exchange values
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (CODE == 0) {
+          const uint32_t he = pack_half2(e[j], e[j]), ho = pack_half2(o[j], o[j]);
+          *reinterpret_cast<u32x2*>(xx_lds + xb * XB + 16 * j + 2 * xs) = u32x2{he, ho};
+        } else if constexpr (ROUND) {
+          xx_lds[xb * XB + 8 * j + xs] = pack_half2(e[j], o[j]);
+        } else {
+          xx_lds[xb * XB + 8 * j + xs] = pack_half2(e[j] - o[j], e[j] + o[j]);
+        }
       }
-      xx_lds[bb * XB + lane] = d0;
-      xx_lds[bb * XB + lane + 64] = d1;
-    } else {
-      uint32_t d = 0u;
-      if (bb < cb) {
-        const XBlock xb = bb == wave ? xfirst : load_x_block(a.x, a.sign_in, (blk0 + bb) * kBlock, lane);
-        d = rht_in_block_pair(xb, lane, !ROUND);
-      }
-      xx_lds[bb * XB + pair_index(lane)] = d;
     }
   }
   __syncthreads();

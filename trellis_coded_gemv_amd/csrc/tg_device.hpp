@@ -167,6 +167,77 @@ __device__ __forceinline__ uint32_t pair_weights_rne(uint32_t u) {
   return (uint32_t)__builtin_bit_cast(uint16_t, w0) | ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
 }
 
+// ---------------------------------------------------------------------------
+// Input-side transform of many 128-blocks at once, 8 lanes per block.
+//
+// Lane s (= lane % 8 of its block) first holds elements 16s..16s+15 (one
+// 32-byte load), applies their signs and the 1/sqrt(128) scale, and runs the
+// four butterfly stages over index bits 0..3 in registers (x16_phase1). One
+// exchange through LDS then gives it elements 16j + 2s and 16j + 2s + 1 for
+// j = 0..7, and the stages over index bits 4..6 finish in registers
+// (x16_phase2): the lane ends with x~ of column pairs q = 8j + s. The
+// Sylvester matrix is the tensor product of its 2x2 factors, so the stages
+// may run in any order. No cross-lane shuffles are needed.
+// ---------------------------------------------------------------------------
+struct X16 {
+  u32x4 lo, hi;   // fp16 patterns of elements first .. first+15
+  uint32_t sw;    // the sign word holding their 16 sign bits
+};
+
+// `first` is the element index of the lane's 16 elements (a multiple of 16).
+__device__ __forceinline__ X16 load_x16(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
+                                        int first) {
+  X16 r;
+  const u32x4* p = reinterpret_cast<const u32x4*>(x + first);
+  r.lo = p[0];
+  r.hi = p[1];
+  r.sw = sign_in[first >> 5];
+  return r;
+}
+
+// v[j] = s[first+j] * x[first+j] / sqrt(128), then the 16-point transform over j.
+__device__ __forceinline__ void x16_phase1(const X16& r, int first, float (&v)[16]) {
+  const uint32_t sb = r.sw >> (first & 16);   // bit j: sign of element first + j
+  const uint32_t w[8] = {r.lo[0], r.lo[1], r.lo[2], r.lo[3], r.hi[0], r.hi[1], r.hi[2], r.hi[3]};
+  const uint32_t cbits = __builtin_bit_cast(uint32_t, kRsqrt128);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint16_t h = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
+    const float cs = __builtin_bit_cast(float, cbits | ((sb << (31 - j)) & 0x80000000u));
+    v[j] = half_bits_to_float(h) * cs;
+  }
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & h) == 0) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+}
+
+// The 8-point transform over j for the even (e) and odd (o) elements 16j + 2s (+1).
+__device__ __forceinline__ void x16_phase2(float (&e)[8], float (&o)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((j & h) == 0) {
+        const float a = e[j], b = e[j + h];
+        e[j] = a + b;
+        e[j + h] = a - b;
+        const float c = o[j], d = o[j + h];
+        o[j] = c + d;
+        o[j + h] = c - d;
+      }
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
 // Output-side epilogue of one 128-block held by a wave:
 // y = diag(s_out) H (g * y~) / sqrt(128), written as fp32.
 __device__ __forceinline__ void rht_out_block(float v0, float v1, const uint16_t* __restrict__ scales,
