@@ -1,0 +1,150 @@
+"""Tail-biting trellis encoder: Viterbi search for the best bitstream (test infrastructure).
+
+Given target values v_0..v_{T-1} of one tile (sequence order t = 16r + c) and
+a reconstruction scale alpha, find the 256K-bit circle whose decoded weights
+minimise sum_t (alpha * w_t - v_t)^2.
+
+Followed passages:
+  * [TQ] Part seven: walk the sequence one step at a time; for every state keep
+    the single best path ending there and its total error; at the next step
+    every state looks at the few states that can lead into it and keeps the
+    best; at the end take the best final state and trace back.
+  * [TQ] Part eight: the tail-biting trellis is approximated in two passes --
+    rotate the sequence by half its length, run Viterbi, read off the state in
+    the middle (the window of the original sequence's first step), then run
+    Viterbi on the original sequence constrained to start and end with those
+    bits. [DD] Section 3 / [TQ] Part eight give the trellis itself: a step
+    shifts b = V*K new bits into an L = 16 bit window.
+
+Readings (listed in the design doc):
+  * "read off the bits in the middle" = the pass-one path's state at rotated
+    step T/2, which is the window of original step 0 (its 16 bits become S_0);
+  * "constrained to start and end with those bits": the second pass starts in
+    S_0 and must end in a state whose low L-b bits are S_0's top L-b bits, so
+    that stepping once more returns to S_0 (the circle closes);
+  * errors and costs are float32, in this order: p = alpha*w, e = p - v,
+    d = e*e (pair code: d = e0*e0 + e1*e1, even weight first), cost = d + best
+    predecessor cost; minima keep the first candidate (smallest predecessor
+    top bits; at the end, the smallest state) -- the GPU encoder takes the same
+    decisions in the same precision.
+
+Pins (tests/test_oracle_viterbi.py): exhaustive search on small trellises
+(every linear stream for the open search, every circle for the tail-biting
+bound), exactly representable sequences are encoded with zero error, the
+produced stream decodes to the reported cost, and the mean squared error on a
+Gaussian source at two bits lies between the rate-distortion bound (1/16) and
+a little above the pages' trellis figure ([TQ] Part nine).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import code, trellis
+
+F32 = np.float32
+
+
+def predecessors(n_states_bits: int, b: int) -> np.ndarray:
+    """P[s, a] = the state that reaches s by shifting in s's low b bits, a = its top b bits.
+
+    For an L-bit window, s = ((p << b) | new) mod 2^L, so p = (s >> b) | (a << (L - b)).
+    """
+    L = n_states_bits
+    s = np.arange(1 << L, dtype=np.int64)[:, None]
+    a = np.arange(1 << b, dtype=np.int64)[None, :]
+    return (s >> b) | (a << (L - b))
+
+
+def step_errors(wvals: np.ndarray, alpha, v) -> np.ndarray:
+    """float32 squared error of every state against the step's target(s).
+
+    wvals: float32 [n_states] (one weight per state) or [n_states, 2] (pair code).
+    v: the step's target (scalar) or its two targets.
+    """
+    alpha = F32(alpha)
+    if wvals.ndim == 1:
+        e = (alpha * wvals).astype(F32) - F32(v)
+        return (e * e).astype(F32)
+    e0 = (alpha * wvals[:, 0]).astype(F32) - F32(v[0])
+    e1 = (alpha * wvals[:, 1]).astype(F32) - F32(v[1])
+    return ((e0 * e0).astype(F32) + (e1 * e1).astype(F32)).astype(F32)
+
+
+def viterbi(wvals: np.ndarray, alpha, targets: np.ndarray, L: int, b: int, start=None, end_low=None):
+    """One Viterbi pass over T steps of an L-bit, b-bits-per-step trellis.
+
+    targets: [T] (one weight per step) or [T, 2] (pair code).
+    start: None (any start state) or the forced first state.
+    end_low: None (any end state) or the forced low L-b bits of the last state.
+    Returns (states [T] int64, cost float32): the best path and its total error.
+    """
+    T = targets.shape[0]
+    P = predecessors(L, b)
+    n = 1 << L
+    cost = step_errors(wvals, alpha, targets[0])
+    if start is not None:
+        keep = np.full(n, np.inf, dtype=F32)
+        keep[start] = cost[start]
+        cost = keep
+    back = np.zeros((T, n), dtype=np.uint16)         # back[t, s] = top b bits of s's best predecessor
+    rows = np.arange(n)
+    for t in range(1, T):
+        cand = cost[P]                                # [n, 2^b] costs of the states leading into s
+        a = np.argmin(cand, axis=1)                   # first minimum: smallest top bits
+        back[t] = a
+        cost = (step_errors(wvals, alpha, targets[t]) + cand[rows, a]).astype(F32)
+    if end_low is None:
+        last = int(np.argmin(cost))                   # first minimum: smallest state
+    else:
+        ends = end_low | (np.arange(1 << b, dtype=np.int64) << (L - b))
+        last = int(ends[np.argmin(cost[ends])])
+    states = np.empty(T, dtype=np.int64)
+    states[-1] = last
+    for t in range(T - 1, 0, -1):
+        states[t - 1] = (states[t] >> b) | (int(back[t, states[t]]) << (L - b))
+    return states, F32(cost[last])
+
+
+def encode_tail_biting(wvals: np.ndarray, alpha, targets: np.ndarray, L: int, b: int):
+    """Two-pass tail-biting approximation ([TQ] Part eight). Returns (states [T], cost)."""
+    T = targets.shape[0]
+    h = T // 2
+    rotated = np.concatenate([targets[h:], targets[:h]])
+    s_rot, _ = viterbi(wvals, alpha, rotated, L, b)
+    s0 = int(s_rot[T - h])                            # rotated step T-h is original step 0
+    return viterbi(wvals, alpha, targets, L, b, start=s0, end_low=s0 >> b)
+
+
+def code_values(code_id: int) -> np.ndarray:
+    """float32 weights of every 16-bit state: [65536] (code 0) or [65536, 2] (pair code)."""
+    if code_id == 0:
+        return code.weight_values(np.arange(1 << 16)).astype(F32)
+    e, o = code.pair_weight_bits(np.arange(1 << 16))
+    from . import fp16
+    return np.stack([fp16.value(e), fp16.value(o)], axis=-1).astype(F32)
+
+
+def encode_tile(target: np.ndarray, k_bits: int, code_id: int, alpha, wvals: np.ndarray = None):
+    """Encode one tile's 256 targets. Returns (words uint32 [8K], cost float32)."""
+    v = code.CODE_V[code_id]
+    b = v * k_bits
+    if wvals is None:
+        wvals = code_values(code_id)
+    tg = np.asarray(target, dtype=F32).reshape(trellis.SEQ // v, v) if v > 1 else np.asarray(target, dtype=F32)
+    states, cost = encode_tail_biting(wvals, alpha, tg, trellis.L, b)
+    bits = trellis.stream_from_states(states, k_bits, v)
+    return pack_bits(bits), cost
+
+
+def pack_bits(bits: np.ndarray) -> np.ndarray:
+    """MSB-first bit string [256K] -> uint32 words [8K] (bit p is bit 31 - p%32 of word p/32)."""
+    be = np.packbits(np.asarray(bits, dtype=np.uint8).reshape(-1, 32), axis=-1)   # 4 bytes per word, MSB first
+    return be.view(">u4").reshape(-1).astype(np.uint32)
+
+
+def tile_errors(words: np.ndarray, target: np.ndarray, k_bits: int, code_id: int, alpha) -> float:
+    """float64 squared error of a stored tile against its targets (decoded by the trellis walk)."""
+    v = code.CODE_V[code_id]
+    s = trellis.walk_states(trellis.stream_bits(np.asarray(words, np.uint32), k_bits), k_bits, v)
+    w = code_values(code_id)[s].astype(np.float64).reshape(-1)
+    return float(((float(alpha) * w - np.asarray(target, np.float64)) ** 2).sum())
