@@ -193,6 +193,35 @@ int32_t trellis_decode(const tg_layer *layer, uint16_t *w_out, void *stream);
  */
 int32_t tg_code_table(int32_t code_id, uint16_t *out, void *stream);
 
+/*
+ * Tail-biting Viterbi encoder (offline conversion; lecture, Part seven: the
+ * Viterbi search keeps per state the best path ending there; Part eight: the
+ * tail-biting circle is approximated in two passes -- rotate the sequence by
+ * half, search, take the middle state as the start window, search again
+ * constrained to start and end on it). For every tile it stores the stream
+ * whose decoded weights w minimise sum_t (scale * w_t - target_t)^2.
+ *   n_tiles  : 1 .. 2^24 tiles.
+ *   k_bits   : 1..8 for code_id 0; 1..4 for the pair code (2K bits per step).
+ *   scale    : reconstruction scale, finite and > 0.
+ *   targets  : device, n_tiles * 256 fp32, each tile in sequence order
+ *              t = 16r + c, 4-byte aligned.
+ *   codes    : device, n_tiles * 8K words out (the storage format above).
+ *   sq_err   : device, n_tiles fp32 out (the minimised sum of squared errors),
+ *              or NULL.
+ *   ws       : device workspace of ws_bytes >= tg_encode_workspace_size(...)
+ *              (the search's backpointers; no zero-fill needed).
+ * Errors are float32 with a fixed operation order (p = scale*w, e = p - v,
+ * d = e*e, pair code d = e0*e0 + e1*e1; cost = d + best predecessor cost),
+ * and ties keep the smallest predecessor top bits and, at the open end, the
+ * smallest state, so the result is deterministic.
+ */
+int32_t trellis_encode(int32_t n_tiles, int32_t k_bits, int32_t code_id, float scale,
+                       const float *targets, uint32_t *codes, float *sq_err,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for trellis_encode (0 if the arguments are invalid). */
+size_t tg_encode_workspace_size(int32_t n_tiles, int32_t k_bits, int32_t code_id);
+
 #ifdef __cplusplus
 }
 #endif

@@ -139,3 +139,22 @@ def test_pair_code_passes_layer_validation():
     assert L.trellis_gemm_small(ctypes.byref(d), 16, A16, 512, A16, 256, 0, 1 << 30, None) == -5
     assert L.tg_code_table(1, 0, None) == -1
     assert L.trellis_decode(ctypes.byref(d), 0, None) == -1
+
+
+def test_encode_argument_validation():
+    L = tg.lib()
+    assert L.tg_encode_workspace_size(4, 2, 0) > 0
+    assert L.tg_encode_workspace_size(0, 2, 0) == 0
+    assert L.tg_encode_workspace_size(4, 9, 0) == 0
+    assert L.tg_encode_workspace_size(4, 5, 1) == 0           # pair code: at most 4 bits (8 per step)
+    assert L.tg_encode_workspace_size(4, 2, 2) == 0
+    need = L.tg_encode_workspace_size(4, 2, 0)
+    assert L.trellis_encode(4, 2, 0, 0.75, A16, A16, A16, 0, need, None) == -5
+    assert L.trellis_encode(4, 2, 0, 0.75, 0, A16, A16, A16, need, None) == -1
+    assert L.trellis_encode(4, 2, 0, -1.0, A16, A16, A16, A16, need, None) == -8
+    assert L.trellis_encode(4, 2, 0, float("nan"), A16, A16, A16, A16, need, None) == -8
+    assert L.trellis_encode(4, 0, 0, 0.75, A16, A16, A16, A16, need, None) == -3
+    assert L.trellis_encode(4, 2, 3, 0.75, A16, A16, A16, A16, need, None) == -6
+    assert L.trellis_encode(0, 2, 0, 0.75, A16, A16, A16, A16, need, None) == -2
+    assert L.trellis_encode(4, 2, 0, 0.75, A16 + 2, A16, A16, A16, need, None) == -4
+    assert L.trellis_encode(4, 2, 0, 0.75, A16, A16, A16, A16 + 16, need, None) == -4

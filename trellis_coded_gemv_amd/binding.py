@@ -23,7 +23,8 @@ STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS",
 
 # every symbol the header declares
 EXPORTS = ("tg_abi_version", "tg_status_str", "tg_workspace_size", "trellis_gemv", "trellis_gemm_small",
-           "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table")
+           "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table",
+           "trellis_encode", "tg_encode_workspace_size")
 
 
 class TgLayer(ctypes.Structure):
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         "tg_grouped_workspace_size": (SZ, [LP, I32, I32]),
         "trellis_decode": (I32, [LP, P, P]),
         "tg_code_table": (I32, [I32, P, P]),
+        "trellis_encode": (I32, [I32, I32, I32, ctypes.c_float, P, P, P, P, SZ, P]),
+        "tg_encode_workspace_size": (SZ, [I32, I32, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -231,3 +234,30 @@ def code_table(device="cuda", code_id: int = 0, stream=None):
     out = torch.empty(shape, dtype=torch.int16, device=device)
     _check(lib().tg_code_table(int(code_id), _ptr(out), _stream(stream)), "tg_code_table")
     return out
+
+
+def encode_workspace(n_tiles: int, k_bits: int, code_id: int = 0, device="cuda"):
+    torch = _torch()
+    n = lib().tg_encode_workspace_size(int(n_tiles), int(k_bits), int(code_id))
+    if n == 0:
+        raise TgError(-8, "tg_encode_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def trellis_encode(targets, k_bits: int, code_id: int = 0, scale: float = 1.0, codes=None, sq_err=None, ws=None,
+                   stream=None):
+    """Viterbi-encode tiles: targets fp32 [n_tiles, 256] (sequence order) -> (codes int32 [n_tiles, 8K], sq_err)."""
+    torch = _torch()
+    if targets.dtype != torch.float32 or not targets.is_contiguous() or targets.shape[-1] != 256:
+        raise ValueError("targets must be a contiguous float32 tensor [n_tiles, 256]")
+    n_tiles = int(targets.shape[0])
+    dev = targets.device
+    if codes is None:
+        codes = torch.empty(n_tiles, 8 * k_bits, dtype=torch.int32, device=dev)
+    if sq_err is None:
+        sq_err = torch.empty(n_tiles, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = encode_workspace(n_tiles, k_bits, code_id, dev)
+    _check(lib().trellis_encode(n_tiles, int(k_bits), int(code_id), float(scale), _ptr(targets),
+                                _ptr(codes), _ptr(sq_err), _ptr(ws), ws.numel(), _stream(stream)), "trellis_encode")
+    return codes, sq_err

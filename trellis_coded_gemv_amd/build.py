@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtrellis_gemv.so")
-SOURCES = ["api.hip", "gemv.hip", "gemm_small.hip", "misc.hip"]
+SOURCES = ["api.hip", "gemv.hip", "gemm_small.hip", "misc.hip", "encode.hip"]
 ARCH = "gfx950"
 
 

@@ -290,3 +290,35 @@ TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
   if (misaligned(out, 2)) return TG_ERR_ALIGN;
   return launch_status(launch_code_table(code_id, out, (hipStream_t)stream));
 }
+
+namespace {
+
+int32_t check_encode(int32_t n_tiles, int32_t k_bits, int32_t code_id, float scale) {
+  if (code_id != 0 && code_id != 1) return TG_ERR_CODE_ID;
+  if (k_bits < 1 || k_bits > 8 || (code_id == 1 && k_bits > 4)) return TG_ERR_KBITS;
+  if (n_tiles < 1 || n_tiles > (1 << 24)) return TG_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < 3.0e38f)) return TG_ERR_ARG;
+  return TG_OK;
+}
+
+int encode_slots(int32_t n_tiles) { return n_tiles < kEncMaxSlots ? n_tiles : kEncMaxSlots; }
+
+}  // namespace
+
+TG_API size_t tg_encode_workspace_size(int32_t n_tiles, int32_t k_bits, int32_t code_id) {
+  if (check_encode(n_tiles, k_bits, code_id, 1.f) != TG_OK) return 0;
+  return round_up((size_t)encode_slots(n_tiles) * encode_ws_words_per_slot(k_bits, code_id) * 4, kAlign);
+}
+
+TG_API int32_t trellis_encode(int32_t n_tiles, int32_t k_bits, int32_t code_id, float scale, const float* targets,
+                              uint32_t* codes, float* sq_err, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_encode(n_tiles, k_bits, code_id, scale);
+  if (st != TG_OK) return st;
+  if (!targets || !codes) return TG_ERR_NULL;
+  if (misaligned(targets, 4) || misaligned(codes, 4) || misaligned(sq_err, 4)) return TG_ERR_ALIGN;
+  const size_t need = tg_encode_workspace_size(n_tiles, k_bits, code_id);
+  if (!ws || ws_bytes < need) return TG_ERR_WORKSPACE;
+  if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
+  return launch_status(launch_encode(targets, scale, n_tiles, k_bits, code_id, codes, sq_err,
+                                     reinterpret_cast<uint32_t*>(ws), encode_slots(n_tiles), (hipStream_t)stream));
+}

@@ -73,6 +73,10 @@ hipError_t launch_rht(int n, int rows, const uint16_t* in, float* out, const uin
                       hipStream_t s);
 hipError_t launch_decode(const uint32_t* codes, uint16_t* out, int m, int n, int k_bits, int code_id, hipStream_t s);
 hipError_t launch_code_table(int code_id, uint16_t* out, hipStream_t s);
+hipError_t launch_encode(const float* targets, float alpha, int n_tiles, int k_bits, int code_id, uint32_t* codes,
+                         float* sq_err, uint32_t* ws, int slots, hipStream_t s);
+size_t encode_ws_words_per_slot(int k_bits, int code_id);
+constexpr int kEncMaxSlots = 256;        // encoder workgroups in flight (one tile each at a time)
 
 // LDS bytes a GEMV workgroup needs for a chunk of `chunk_blocks` 128-blocks.
 // The x~ region doubles as [8P][128] fp32 per-wave sums in the final reduction.
