@@ -123,3 +123,17 @@ def test_grouped_out_of_range_selection_writes_nothing():
     assert (y[1] == 7.0).all() and (y[2] == 7.0).all()
     assert rel_err(y[0], ogemv.gemv(arrays[5], x)) <= REL_TOL
     assert rel_err(y[3], ogemv.gemv(arrays[7], x)) <= REL_TOL
+
+
+@pytest.mark.parametrize("M,code_id", [(16, 0), (3, 0), (16, 1)])
+def test_gemm_small_long_chunks(M, code_id):
+    """One split over 6144 inputs: code 0 runs 16-wave workgroups (384 MFMA steps), the pair code
+    8-wave ones; the full output is checked."""
+    dev = device()
+    arr = inputs.make_layer(128, 6144, 2, 3300 + M, code_id=code_id)
+    X = inputs.make_x(6144, 3300 + M, rows=M)
+    say("gemm_small long chunks", M, code_id)
+    Y = _gemm(arr, X, dev)
+    ref = ogemv.gemm(arr, X)
+    for r in range(M):
+        assert rel_err(Y[r], ref[r]) <= REL_TOL, r

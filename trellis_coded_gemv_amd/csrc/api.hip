@@ -70,17 +70,18 @@ int gemv_splits(int m, int n) {
   return s;
 }
 
-// Splits of the small-batch path: the fp32 partials cost 8*S*M*m bytes of
-// traffic against m*n*K/8 code bytes, so keep S small; a chunk keeps at
-// least 8 MFMA steps (one per wave): 8 tile columns for code 0, 16 for the
-// pair code, whose MFMA spans two tiles.
+// Splits of the small-batch path: about 256 workgroups, but the fp32 partials
+// cost 8*S*M*m bytes of traffic against m*n*K/8 code bytes, so they are kept
+// to 1/8 of the code bytes; a chunk keeps at least 8 MFMA steps (one per
+// wave): 8 tile columns for code 0, 16 for the pair code, whose MFMA spans two
+// tiles.
 int gemm_splits(int m, int n, int M, int k_bits, int code_id) {
   const int ob = m / kBlock;
   const int nsub = n / (code_id == 0 ? kBlock : 2 * kBlock);
   int s = env_int("TG_SPLITK_MFMA");
   if (s <= 0) {
     s = (256 + ob / 2) / ob;                                     // about 256 workgroups
-    const int cap = (int)((int64_t)n * k_bits / (1024 * M));   // partial traffic <= 1/16 of the code bytes
+    const int cap = (int)((int64_t)n * k_bits / (512 * M));    // partial traffic <= 1/8 of the code bytes
     if (s > cap) s = cap;
   }
   if (s > nsub) s = nsub;

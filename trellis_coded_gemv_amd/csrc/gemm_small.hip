@@ -19,12 +19,13 @@
 // loop-invariant shift over two (three for K >= 6) loaded words -- then
 // v_bfe + v_mad_u32_u24 + v_and_or_b32 per weight.
 //
-// Decomposition: a workgroup of 8 waves owns one 128-output block and a chunk
-// of the input's tile columns; every wave covers all 8 tile rows of the block
-// for every 8th column of the chunk, so the MFMA accumulators of a wave stay
-// put for the whole loop and the x~ operand of a column (prepared once per
-// call by xt_prep_kernel, read from L2) is loaded once for 8 tiles. The 8
-// waves are summed through LDS at the end; split-K partials and the
+// Decomposition: a workgroup of MW waves (16 for up to 16 activation rows,
+// else 8) owns one 128-output block and a chunk of the input's tile columns;
+// every wave covers all 8 tile rows of the block for every MW-th column of
+// the chunk, so the MFMA accumulators of a wave stay put for the whole loop
+// and the x~ operand of a column (prepared once per call by xt_prep_kernel,
+// read from L2) is loaded once for 8 tiles. The waves are summed through LDS
+// at the end; split-K partials and the
 // last-arriving-workgroup epilogue are as in the batch-1 kernel.
 //
 // Pair code (code_id 1): a state covers two input columns, so one tile row of
@@ -41,6 +42,13 @@
 // Tiles whose B operands are decoded before their MFMAs are issued.
 #ifndef TG_MFMA_GROUP
 #define TG_MFMA_GROUP 4
+#endif
+// A workgroup has 16 waves when the activations fit one 16-row MFMA block and
+// every wave still gets at least this many steps (more waves hide more
+// latency; short loops do not amortise the start-up and the deeper reduction,
+// and wider batches need the registers), else 8.
+#ifndef TG_MFMA_MIN_STEPS16
+#define TG_MFMA_MIN_STEPS16 24
 #endif
 
 namespace tg {
@@ -208,8 +216,8 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
   }
 }
 
-template <int K, int CODE, bool ROUND, int MB>
-__global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
+template <int K, int CODE, bool ROUND, int MB, int MW>
+__global__ __launch_bounds__(64 * MW) void gemm_small_kernel(GemmArgs a) {
   extern __shared__ uint32_t lds[];
   constexpr int PF = 2;
   using G = MfmaGeom<K, CODE>;
@@ -223,36 +231,41 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
   const int c0 = (int)((int64_t)split * ncols / a.splits);
   const int c1 = (int)((int64_t)(split + 1) * ncols / a.splits);
   // wave w takes steps c0+w, c0+w+8, ... of the chunk
-  const int nmine = c1 - c0 > wave ? (c1 - c0 - wave + kGemvWaves - 1) / kGemvWaves : 0;
+  const int nmine = c1 - c0 > wave ? (c1 - c0 - wave + MW - 1) / MW : 0;
 
   float4_t acc[8][MB];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[t][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-  if (nmine > 0) gemm_wave<K, CODE, ROUND, MB, PF>(a, ob, c0 + wave, nmine, kGemvWaves, lds + wave * SLICE, acc);
+  if (nmine > 0) gemm_wave<K, CODE, ROUND, MB, PF>(a, ob, c0 + wave, nmine, MW, lds + wave * SLICE, acc);
 
-  // Sum the 8 waves' accumulators: a fixed tree through LDS (4 -> 2 -> 1 waves),
-  // one 16-row group at a time to bound the LDS footprint.
-  float* red = reinterpret_cast<float*>(lds + kGemvWaves * SLICE);   // [4][8*4][64]
+  // Sum the waves' accumulators: a fixed tree through LDS (MW -> MW/2 -> ... -> 1
+  // waves; wave w + half adds into wave w), at most four writer waves per round
+  // and one 16-row group at a time to bound the LDS footprint.
+  float* red = reinterpret_cast<float*>(lds + MW * SLICE);   // [4][8*4][64]
   constexpr int NV = 8 * 4;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int half = 4; half >= 1; half >>= 1) {
-      __syncthreads();
-      if (wave >= half && wave < 2 * half) {
+    for (int half = MW / 2; half >= 1; half >>= 1) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+      for (int base = 0; base < half; base += 4) {
+        const int lo = base, hi = base + 4 < half ? base + 4 : half;   // this round's receivers [lo, hi)
+        __syncthreads();
+        if (wave >= half + lo && wave < half + hi) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) red[(((wave - half) * NV) + t * 4 + v) * 64 + lane] = acc[t][mb][v];
-      }
-      __syncthreads();
-      if (wave < half) {
+          for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+            for (int v = 0; v < 4; ++v) red[(((wave - half - lo) * NV) + t * 4 + v) * 64 + lane] = acc[t][mb][v];
+        }
+        __syncthreads();
+        if (wave >= lo && wave < hi) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[t][mb][v] += red[((wave * NV) + t * 4 + v) * 64 + lane];
+          for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][mb][v] += red[(((wave - lo) * NV) + t * 4 + v) * 64 + lane];
+        }
       }
     }
   }
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
           for (int v = 0; v < 4; ++v) ybuf[(16 * mb + 4 * g + v) * 128 + 16 * t + jrow] = acc[t][mb][v];
     }
     __syncthreads();
-    for (int r = wave; r < a.M; r += kGemvWaves)
+    for (int r = wave; r < a.M; r += MW)
       rht_out_block(ybuf[r * 128 + lane], ybuf[r * 128 + lane + 64], a.scales, a.sign_out, a.y + (size_t)r * a.ldy,
                     ob * kBlock, lane);
     return;
@@ -290,7 +303,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
         }
   }
   if (!arrive_is_last(&a.counters[ob], (uint32_t)a.splits, flag)) return;
-  for (int r = wave; r < a.M; r += kGemvWaves) {
+  for (int r = wave; r < a.M; r += MW) {
     float v0 = 0.f, v1 = 0.f;
 #pragma unroll 8
     for (int t = 0; t < a.splits; ++t) {   // unrolled so the loads are in flight together
@@ -303,29 +316,36 @@ __global__ __launch_bounds__(kGemvThreads) void gemm_small_kernel(GemmArgs a) {
   if (threadIdx.x == 0) reset_counter(&a.counters[ob]);
 }
 
-template <int K, int CODE, int MB>
+template <int K, int CODE, int MB, int MW>
 size_t gemm_lds_bytes() {
-  const size_t slices = (size_t)kGemvWaves * 8 * MfmaGeom<K, CODE>::SPAN * 8 * K * 4;   // per-wave code staging
+  const size_t slices = (size_t)MW * 8 * MfmaGeom<K, CODE>::SPAN * 8 * K * 4;   // per-wave code staging
   const size_t red = 4ull * 8 * 4 * 64 * 4;                     // tree reduction buffer (one row group)
   const size_t ybuf = 16ull * MB * 128 * 4 + 16;
   const size_t a = slices + red;
   return a > ybuf ? a : ybuf;
 }
 
-template <int K, int CODE, bool ROUND, int MB>
+template <int K, int CODE, bool ROUND, int MB, int MW>
 static void launch_main(const GemmArgs& a, hipStream_t s) {
   const int grid = (a.m >> 7) * a.splits;
-  const size_t lds = gemm_lds_bytes<K, CODE, MB>();
-  hipLaunchKernelGGL((gemm_small_kernel<K, CODE, ROUND, MB>), dim3(grid), dim3(kGemvThreads), lds, s, a);
+  const size_t lds = gemm_lds_bytes<K, CODE, MB, MW>();
+  // raise the dynamic LDS limit (up to 96 KB here); if that fails the launch fails and reports it
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_small_kernel<K, CODE, ROUND, MB, MW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((gemm_small_kernel<K, CODE, ROUND, MB, MW>), dim3(grid), dim3(64 * MW), lds, s, a);
 }
 
 template <int K, int CODE, bool ROUND>
 static void launch_mb(const GemmArgs& a, hipStream_t s) {
+  const int steps = (a.n >> 4) / MfmaGeom<K, CODE>::SPAN / a.splits;   // MFMA steps per workgroup
   switch (a.mpad / 16) {
-    case 1: launch_main<K, CODE, ROUND, 1>(a, s); break;
-    case 2: launch_main<K, CODE, ROUND, 2>(a, s); break;
-    case 3: launch_main<K, CODE, ROUND, 3>(a, s); break;
-    default: launch_main<K, CODE, ROUND, 4>(a, s); break;
+    case 1:
+      if (steps >= 16 * TG_MFMA_MIN_STEPS16) launch_main<K, CODE, ROUND, 1, 16>(a, s);
+      else launch_main<K, CODE, ROUND, 1, 8>(a, s);
+      break;
+    case 2: launch_main<K, CODE, ROUND, 2, 8>(a, s); break;
+    case 3: launch_main<K, CODE, ROUND, 3, 8>(a, s); break;
+    default: launch_main<K, CODE, ROUND, 4, 8>(a, s); break;
   }
 }
 
