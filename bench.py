@@ -21,10 +21,20 @@ device memory before the timed region starts.
 
 Prints ONE JSON line: value = compressed-weight GB/s over the timed region (K
 steps between two synchronisations, HIP events on the launch stream, steps
-replayed from a captured HIP graph), the roofline of the dominant kernel
-(algorithmic bytes / mean launch duration from HIP events bracketing every
-launch of an eager pass over the same steps), and the CPU oracle timed on a
-bounded sample of the same workload on the host.
+replayed from a captured HIP graph), the roofline of the dominant kernel, and
+the CPU oracle timed on a bounded sample of the same workload on the host.
+
+The dominant kernel (the launch moving the most bytes) is timed alone: the same
+K steps restricted to its launches, replayed from their own graph, give its mean
+launch duration. The decode is bound by VALU arithmetic, so the roofline is an
+ALU one: algorithmic lane-operations per launch (decoded weights x the minimum
+VALU operations per weight the code needs on gfx950: window extract,
+multiply-add, and-or, dot2 = 4 for code 0; 2 for the pair code, one state per
+two weights; one fewer per state on the MFMA path, whose dot products run on
+the matrix cores) over the launch duration, against 256 CUs x 4 SIMDs x 16
+lanes x 2.4 GHz = 39.3 T lane-operations/s. The same launch's HBM view
+(algorithmic bytes / duration against 8 TB/s) and the measured HBM traffic
+(rocprofv3 FETCH_SIZE + WRITE_SIZE, profiles/traffic.json) are reported with it.
 """
 from __future__ import annotations
 
@@ -44,6 +54,7 @@ if ROOT not in sys.path:
 
 METRIC = "batch-1 trellis GEMV: compressed-weight HBM GB/s (% of peak) + µs/layer"
 HBM_PEAK_GBS = 8000.0
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12      # VALU lane-operations per second, in T (39.32)
 MFMA_F16_PEAK_TFLOPS = 2500.0
 CACHE_DEFEAT_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -76,6 +87,12 @@ def recorded_traffic(workload: int, kernel: str, code_id: int = 0):
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def alu_ops_per_weight(code_id: int, mfma: bool) -> float:
+    """Minimum VALU lane-operations per decoded weight (see the module docstring)."""
+    per_state = 3 if mfma else 4          # window extract, multiply-add, and-or (+ dot2 on the VALU path)
+    return per_state / (2 if code_id == 1 else 1)
 
 
 def gemv_bytes(m: int, n: int, k: int, M: int = 1) -> int:
@@ -154,6 +171,7 @@ def setup_linears(torch, tg, inputs, wl, dev, code_id):
 
     alg = {name: gemv_bytes(*wl.tensors[name]) for name in names}
     return step, dict(code_bytes=code_bytes, copies=copies, alg_bytes=alg, names=names,
+                      weights={name: wl.tensors[name][0] * wl.tensors[name][1] for name in names}, mfma=False,
                       units="layer" if len(names) == 1 else "decoder layer (7 GEMVs)")
 
 
@@ -177,7 +195,8 @@ def setup_gemm(torch, tg, inputs, wl, dev, code_id):
         launch(name, lambda: tg.trellis_gemm_small(L, X, Y, ws, torch.cuda.current_stream()))
 
     return step, dict(code_bytes=code_bytes, copies=copies, alg_bytes={name: gemv_bytes(m, n, k, M)},
-                      names=[name], units="layer (16 rows)", flops=2.0 * m * n * M)
+                      names=[name], weights={name: m * n}, mfma=True, units="layer (16 rows)",
+                      flops=2.0 * m * n * M)
 
 
 def setup_moe(torch, tg, inputs, wl, dev, code_id):
@@ -216,7 +235,8 @@ def setup_moe(torch, tg, inputs, wl, dev, code_id):
     alg = {"gate_up": mean_tok * 2 / 3 + 2 * wl.hidden + 16 * 6 * wl.inter,
            "down": mean_tok / 3 + 8 * 2 * wl.inter + 8 * 6 * wl.hidden}
     return step, dict(code_bytes=mean_tok, copies=copies, alg_bytes=alg, names=["gate_up", "down"],
-                      units="token (24 GEMVs, 2 launches)")
+                      weights={"gate_up": 2 * wl.top_k * wl.inter * wl.hidden, "down": wl.top_k * wl.hidden * wl.inter},
+                      mfma=False, units="token (24 GEMVs, 2 launches)")
 
 
 def run_gpu(workload, steps, warmup, use_graph, code_id=0):
@@ -369,6 +389,9 @@ def main(argv=None):
     dom = t["dom"]
     dom_launch_ms = t["dom_ms"] / steps
     achieved = info["alg_bytes"][dom] / (dom_launch_ms * 1e-3) / 1e9
+    opw = alu_ops_per_weight(args.code, info["mfma"])
+    alg_ops = info["weights"][dom] * opw
+    alu_achieved = alg_ops / (dom_launch_ms * 1e-3) / 1e12
     config = {"workload": wl.name, "units": info["units"], "code_bytes_per_step": int(info["code_bytes"]),
               "copies": info["copies"], "us_per_step": round(ms_per_step * 1e3, 3),
               "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
@@ -380,11 +403,14 @@ def main(argv=None):
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp16", "data": "synthetic", "config": config,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "alu", "kernel": dom, "achieved": round(alu_achieved, 3), "peak": round(ALU_PEAK_TOPS, 3),
+                     "unit": "T lane-ops/s", "frac": round(alu_achieved / ALU_PEAK_TOPS, 4),
                      "traffic": recorded_traffic(args.workload, dom, args.code),
-                     "algorithmic_bytes": int(info["alg_bytes"][dom]),
-                     "launch_us": round(dom_launch_ms * 1e3, 3)},
+                     "algorithmic_ops": int(alg_ops), "ops_per_weight": opw,
+                     "launch_us": round(dom_launch_ms * 1e3, 3),
+                     "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(achieved / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes": int(info["alg_bytes"][dom])}},
     }
     if "flops" in info:
         tf = info["flops"] / (dom_launch_ms * 1e-3) / 1e12
