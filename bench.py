@@ -14,6 +14,8 @@ through the C ABI. Workloads (seeded, synthetic; no trained weights):
   4  gate projection 8192 -> 28672, K=4, 16 activation rows (MFMA path)
   5  MoE: 128 experts (gate/up 2048->768, down 768->2048, K in {1,2,3}), top-8 per
      token, a step = one token = 2 grouped launches
+  6  prefill: gate projection 8192 -> 28672, K=4, 512 activation rows (decode once
+     to fp16 + dense GEMM; its roofline is the matrix cores')
 
 Enough seeded copies of the weights (>= 1 GiB, four times the 256 MB Infinity
 Cache) are used round-robin that the timed reads come from HBM. Inputs are in
@@ -199,6 +201,30 @@ def setup_gemm(torch, tg, inputs, wl, dev, code_id):
                       flops=2.0 * m * n * M)
 
 
+def setup_prefill(torch, tg, inputs, wl, dev, code_id):
+    name = "gate"
+    m, n, k = wl.tensors[name]
+    M = wl.batch
+    code_bytes = m * n * k // 8
+    copies = _copies(code_bytes)
+    log(f"{wl.name}: M={M}, {code_bytes} code bytes, {copies} copies")
+    per = []
+    for c in range(copies):
+        L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=0, copy=c, code_id=code_id), dev)
+        X = tg.fp16_tensor(inputs.make_x(n, wl.seed, tensor=0, copy=c, rows=M), dev)
+        per.append((L, X))
+    Y = torch.empty(M, m, dtype=torch.float32, device=dev)
+    ws = tg.prefill_workspace(per[0][0], M, dev)
+
+    def step(i, launch):
+        L, X = per[i % copies]
+        launch(name, lambda: tg.trellis_gemm_prefill(L, X, Y, ws, torch.cuda.current_stream()))
+
+    return step, dict(code_bytes=code_bytes, copies=copies, alg_bytes={name: gemv_bytes(m, n, k, M)},
+                      names=[name], weights={name: m * n}, mfma=True, prefill=True,
+                      units=f"layer ({M} rows)", flops=2.0 * m * n * M)
+
+
 def setup_moe(torch, tg, inputs, wl, dev, code_id):
     routing = wl.routing()
     gu_arr = [wl.layer(e, w, code_id=code_id) for e in range(wl.experts) for w in ("gate", "up")]
@@ -252,7 +278,8 @@ def run_gpu(workload, steps, warmup, use_graph, code_id=0):
 
     dev = "cuda"
     wl = inputs.WORKLOADS[workload]
-    setup = {1: setup_linears, 2: setup_linears, 3: setup_linears, 4: setup_gemm, 5: setup_moe}[workload]
+    setup = {1: setup_linears, 2: setup_linears, 3: setup_linears, 4: setup_gemm, 5: setup_moe,
+             6: setup_prefill}[workload]
     step, info = setup(torch, tg, inputs, wl, dev, code_id)
     dom = max(info["names"], key=lambda k: info["alg_bytes"][k])     # kernel moving the most bytes
     stream = torch.cuda.current_stream()
@@ -310,6 +337,9 @@ def parity_spot_check(workload, code_id=0):
     if M == 1:
         y = tg.trellis_gemv(L, tg.fp16_tensor(x, "cuda"))[None, :]
         ref = ogemv.gemv_rows(arr, x, rows)[None, :]
+    elif workload == 6:
+        y = tg.trellis_gemm_prefill(L, tg.fp16_tensor(x, "cuda"))
+        ref = ogemv.gemm_rows(arr, x[:2], rows)
     else:
         y = tg.trellis_gemm_small(L, tg.fp16_tensor(x, "cuda"))
         ref = ogemv.gemm_rows(arr, x[:2], rows)
@@ -342,23 +372,25 @@ def cpu_baseline(workload, sample_blocks, code_id=0):
         ti = list(wl.tensors).index(name)
         arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
         M = wl.batch
-        X = inputs.make_x(n, wl.seed, tensor=ti, rows=M)
+        Mo = min(M, 16)                        # oracle rows timed; scaled to the M rows of a step
+        X = inputs.make_x(n, wl.seed, tensor=ti, rows=Mo) if Mo > 1 else inputs.make_x(n, wl.seed, tensor=ti)
         nb = m // 128
-        nblk = max(1, sample_blocks // M)
+        nblk = max(1, sample_blocks // Mo)
         blocks = np.linspace(0, nb - 1, min(nblk, nb)).astype(int)
         rows = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
         with threadpool_limits(limits=1):
             for _ in range(2):                 # the second (warm) pass is the one reported
                 t = time.perf_counter()
-                if M == 1:
+                if Mo == 1:
                     ogemv.gemv_rows(arr, X, rows)
                 else:
                     ogemv.gemm_rows(arr, X, rows)
                 dt = time.perf_counter() - t
         nbytes = len(rows) * n * k // 8
         sample = (f"{len(blocks)} of {nb} 128-output blocks of the {m}x{n} K={k} '{name}' tensor"
-                  f"{'' if M == 1 else f' x {M} rows'} (decode + fp64 GEMV), {dt:.1f} s")
-        rate = nbytes / dt
+                  f"{'' if M == 1 else f' x {Mo} rows'} (decode + fp64 GEMV), {dt:.1f} s"
+                  f"{'' if Mo == M else f', scaled to {M} rows'}")
+        rate = nbytes / (dt * M / Mo)
     return {"value": round(rate / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}
 
 
@@ -367,7 +399,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--code", type=int, default=0, choices=[0, 1],
                     help="code_id of every layer: 0 the three-instruction code, 1 the pair code")
     ap.add_argument("--no-graph", action="store_true")
@@ -416,6 +448,14 @@ def main(argv=None):
         tf = info["flops"] / (dom_launch_ms * 1e-3) / 1e12
         out["roofline"]["mfma"] = {"achieved_tflops": round(tf, 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
                                    "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 5)}
+    if info.get("prefill"):
+        # decode once + dense GEMM: the contraction is the roofline here
+        mf = out["roofline"].pop("mfma")
+        alu = {k: out["roofline"].pop(k) for k in ("achieved", "peak", "unit", "frac", "algorithmic_ops",
+                                                   "ops_per_weight")}
+        out["roofline"].update({"bound": "mfma", "achieved": mf["achieved_tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": mf["frac"], "algorithmic_flops": info["flops"],
+                                "alu": alu})
     if args.copy_calib_mb > 0:
         # counter calibration: a pure write (fill) and a pure read (sum) of known size
         import torch

@@ -140,6 +140,30 @@ int32_t trellis_gemm_small(const tg_layer *layer, int32_t M,
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Prefill / large batch: Y[r] = W X[r] for r < M, 1 <= M <= 65535. Every weight
+ * is decoded exactly once per call, as fp16 rows into the workspace, so the
+ * decode is amortised over all M rows (lecture, Part eleven: the prefill side
+ * of the bill); then one dense GEMM on the matrix cores (rocBLAS, fp16 inputs,
+ * fp32 accumulation and output) and the output transform in place on Y. This
+ * path always multiplies the fp16-rounded weights (TG_FLAG_ROUND_WEIGHTS has no
+ * further effect here).
+ *   X, ldx, Y, ldy : as for trellis_gemm_small (ldy < 2^31).
+ *   ws : device workspace of ws_bytes >= tg_prefill_workspace_size(layer, M):
+ *        m*n*2 bytes of decoded weights plus M*n*2 bytes of transformed inputs
+ *        (no zero-fill needed).
+ * The GEMM uses one rocBLAS handle per device, created on the first call on
+ * that device (rocBLAS allocates its own memory then) with atomics disabled,
+ * so results stay bitwise deterministic; enqueueing is serialised across host
+ * threads.
+ */
+int32_t trellis_gemm_prefill(const tg_layer *layer, int32_t M,
+                             const uint16_t *X, int64_t ldx, float *Y, int64_t ldy,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for trellis_gemm_prefill (0 if the layer / M is invalid). */
+size_t tg_prefill_workspace_size(const tg_layer *layer, int32_t M);
+
+/*
  * Randomized Hadamard transform on 128-blocks of `rows` rows of n values
  * (Deep Dive, Section 2; lecture, Part eleven):
  *   inverse == 0: out = blockdiag(H) diag(s) in      (input side)

@@ -158,3 +158,19 @@ def test_encode_argument_validation():
     assert L.trellis_encode(0, 2, 0, 0.75, A16, A16, A16, A16, need, None) == -2
     assert L.trellis_encode(4, 2, 0, 0.75, A16 + 2, A16, A16, A16, need, None) == -4
     assert L.trellis_encode(4, 2, 0, 0.75, A16, A16, A16, A16 + 16, need, None) == -4
+
+
+def test_prefill_argument_validation():
+    L = tg.lib()
+    d = _layer()
+    need = L.tg_prefill_workspace_size(ctypes.byref(d), 100)
+    assert need >= 256 * 512 * 2 + 100 * 512 * 2
+    assert L.tg_prefill_workspace_size(ctypes.byref(d), 0) == 0
+    assert L.tg_prefill_workspace_size(ctypes.byref(d), 65536) == 0
+    assert L.trellis_gemm_prefill(ctypes.byref(d), 100, A16, 512, A16, 256, 0, need, None) == -5
+    assert L.trellis_gemm_prefill(ctypes.byref(d), 100, A16, 511, A16, 256, A16, need, None) == -8
+    assert L.trellis_gemm_prefill(ctypes.byref(d), 0, A16, 512, A16, 256, A16, need, None) == -2
+    assert L.trellis_gemm_prefill(ctypes.byref(d), 100, 0, 512, A16, 256, A16, need, None) == -1
+    assert L.trellis_gemm_prefill(ctypes.byref(d), 100, A16, 512, A16, 256, A16 + 16, need, None) == -4
+    bad = _layer(k_bits=0)
+    assert L.trellis_gemm_prefill(ctypes.byref(bad), 100, A16, 512, A16, 256, A16, need, None) == -3

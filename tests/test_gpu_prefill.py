@@ -1,0 +1,89 @@
+"""GPU parity for the prefill path (decode once to fp16, dense GEMM) against the oracle."""
+import numpy as np
+import pytest
+
+from gpu_common import REL_TOL, device, rel_err, sample_rows, say
+from oracle import gemv as ogemv
+from trellis_coded_gemv_amd import binding as tg
+from trellis_coded_gemv_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(arr, X_bits, dev):
+    import torch
+    L = tg.DeviceLayer(arr, dev)
+    Y = tg.trellis_gemm_prefill(L, tg.fp16_tensor(X_bits, dev))
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+@pytest.mark.parametrize("k", range(1, 9))
+@pytest.mark.parametrize("code_id", [0, 1])
+def test_prefill_every_k(k, code_id):
+    dev = device()
+    arr = inputs.make_layer(256, 384, k, 5000 + k, code_id=code_id)
+    X = inputs.make_x(384, 5000 + k, rows=40)
+    say("prefill k", k, code_id)
+    Y = _prefill(arr, X, dev)
+    ref = ogemv.gemm(arr, X)
+    for r in range(40):
+        assert rel_err(Y[r], ref[r]) <= REL_TOL, r
+
+
+@pytest.mark.parametrize("M", [1, 2, 17, 64, 129])
+def test_prefill_batch_sizes(M):
+    dev = device()
+    arr = inputs.make_layer(384, 1152, 3, 5100 + M)
+    X = inputs.make_x(1152, 5100 + M, rows=M) if M > 1 else inputs.make_x(1152, 5100 + M)[None, :]
+    say("prefill M", M)
+    Y = _prefill(arr, X, dev)
+    ref = ogemv.gemm(arr, X)
+    for r in range(M):
+        assert rel_err(Y[r], ref[r]) <= REL_TOL, r
+
+
+def test_prefill_decoded_weights_match_the_decode_hook():
+    """The prefill's decode kernel and trellis_decode agree bit for bit: a unit input row picks out
+    one column of W_eff, checked against the oracle's effective matrix on a small layer."""
+    dev = device()
+    arr = inputs.make_layer(128, 256, 2, 5200)
+    X = np.zeros((3, 256), np.float16)
+    for r, j in enumerate((0, 77, 255)):
+        X[r, j] = 1.0
+    say("prefill impulses")
+    Y = _prefill(arr, X.view(np.uint16), dev)
+    Weff = ogemv.effective_matrix(arr)
+    for r, j in enumerate((0, 77, 255)):
+        assert rel_err(Y[r], Weff[:, j]) <= REL_TOL, j
+
+
+def test_prefill_full_size_sampled():
+    """Gate projection 8192 -> 28672 at K=4 with 256 rows: sampled outputs against the oracle."""
+    dev = device()
+    wl = inputs.CFG4
+    m, n, k = wl.tensors["gate"]
+    arr = inputs.make_layer(m, n, k, wl.seed)
+    X = inputs.make_x(n, wl.seed, rows=256)
+    say("prefill 28672x8192 K4 M256")
+    Y = _prefill(arr, X, dev)
+    assert np.isfinite(Y).all()
+    rows = sample_rows(m, seed=6, blocks=2, per_block=8)
+    pick = [0, 100, 255]
+    ref = ogemv.gemm_rows(arr, X[pick], rows)
+    for i, r in enumerate(pick):
+        assert rel_err(Y[r, rows], ref[i]) <= REL_TOL, r
+
+
+def test_prefill_matches_mfma_path_with_rounded_weights():
+    """Same rounded weights, same fp16 inputs: the two batched paths differ only in summation order."""
+    dev = device()
+    import torch
+    arr = inputs.make_layer(256, 2048, 2, 5300)
+    X = inputs.make_x(2048, 5300, rows=16)
+    Yp = _prefill(arr, X, dev)
+    L = tg.DeviceLayer(arr, dev, flags=tg.TG_FLAG_ROUND_WEIGHTS)
+    Ys = tg.trellis_gemm_small(L, tg.fp16_tensor(X, dev))
+    torch.cuda.synchronize()
+    for r in range(16):
+        assert rel_err(Yp[r], Ys.cpu().numpy()[r]) <= 1e-5, r

@@ -24,7 +24,7 @@ STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS",
 # every symbol the header declares
 EXPORTS = ("tg_abi_version", "tg_status_str", "tg_workspace_size", "trellis_gemv", "trellis_gemm_small",
            "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table",
-           "trellis_encode", "tg_encode_workspace_size")
+           "trellis_encode", "tg_encode_workspace_size", "trellis_gemm_prefill", "tg_prefill_workspace_size")
 
 
 class TgLayer(ctypes.Structure):
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         "tg_code_table": (I32, [I32, P, P]),
         "trellis_encode": (I32, [I32, I32, I32, ctypes.c_float, P, P, P, P, SZ, P]),
         "tg_encode_workspace_size": (SZ, [I32, I32, I32]),
+        "trellis_gemm_prefill": (I32, [LP, I32, P, I64, P, I64, P, SZ, P]),
+        "tg_prefill_workspace_size": (SZ, [LP, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -261,3 +263,28 @@ def trellis_encode(targets, k_bits: int, code_id: int = 0, scale: float = 1.0, c
     _check(lib().trellis_encode(n_tiles, int(k_bits), int(code_id), float(scale), _ptr(targets),
                                 _ptr(codes), _ptr(sq_err), _ptr(ws), ws.numel(), _stream(stream)), "trellis_encode")
     return codes, sq_err
+
+
+def prefill_workspace(layer: DeviceLayer, M: int, device="cuda"):
+    torch = _torch()
+    d = layer.desc()
+    n = lib().tg_prefill_workspace_size(ctypes.byref(d), int(M))
+    if n == 0:
+        raise TgError(-2, "tg_prefill_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def trellis_gemm_prefill(layer: DeviceLayer, X, Y=None, ws=None, stream=None):
+    """Y [M, m] fp32 = W X[r] for every row of X (fp16 bits, int16 [M, n]); decode once + dense GEMM."""
+    torch = _torch()
+    M = int(X.shape[0])
+    if Y is None:
+        Y = torch.empty(M, layer.m, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = prefill_workspace(layer, M, X.device)
+    d = layer.desc()
+    ldx = X.stride(0) if M > 1 else X.shape[1]
+    ldy = Y.stride(0) if M > 1 else Y.shape[1]
+    _check(lib().trellis_gemm_prefill(ctypes.byref(d), M, _ptr(X), ldx, _ptr(Y), ldy, _ptr(ws), ws.numel(),
+                                      _stream(stream)), "trellis_gemm_prefill")
+    return Y

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtrellis_gemv.so")
-SOURCES = ["api.hip", "gemv.hip", "gemm_small.hip", "misc.hip", "encode.hip"]
+SOURCES = ["api.hip", "gemv.hip", "gemm_small.hip", "misc.hip", "encode.hip", "prefill.hip"]
+ROCM_LIB = "/opt/rocm/lib"
 ARCH = "gfx950"
 
 
@@ -51,7 +52,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    # rocBLAS runs the dense GEMM of the prefill path (a plain library GEMM)
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + [
+        f"-L{ROCM_LIB}", f"-Wl,-rpath,{ROCM_LIB}", "-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

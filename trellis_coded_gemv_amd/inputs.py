@@ -110,6 +110,8 @@ CFG3 = Workload("decoder70b_layer_k2", 303, {
     "all seven linears of one 70B-shaped decoder layer, K=2, batch 1")
 CFG4 = Workload("gate_8192x28672_k4_m16", 404, {"gate": (28672, 8192, 4)}, 16,
                 "gate projection 8192->28672, K=4, 16 activation rows (MFMA path)")
+PREFILL = Workload("prefill_gate_8192x28672_k4_m512", 606, {"gate": (28672, 8192, 4)}, 512,
+                   "gate projection 8192->28672, K=4, 512 activation rows (decode once + dense GEMM)")
 
 
 @dataclass
@@ -146,4 +148,4 @@ class MoEWorkload:
 
 CFG5 = MoEWorkload()
 
-WORKLOADS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5}
+WORKLOADS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5, 6: PREFILL}
