@@ -16,6 +16,8 @@ through the C ABI. Workloads (seeded, synthetic; no trained weights):
      token, a step = one token = 2 grouped launches
   6  prefill: gate projection 8192 -> 28672, K=4, 512 activation rows (decode once
      to fp16 + dense GEMM; its roofline is the matrix cores')
+  7  the workload-5 experts as a whole MoE block per token: gate/up -> silu * mul ->
+     down -> router-weighted combine (3 launches)
 
 Enough seeded copies of the weights (>= 1 GiB, four times the 256 MB Infinity
 Cache) are used round-robin that the timed reads come from HBM. Inputs are in
@@ -225,6 +227,43 @@ def setup_prefill(torch, tg, inputs, wl, dev, code_id):
                       units=f"layer ({M} rows)", flops=2.0 * m * n * M)
 
 
+def setup_moe_block(torch, tg, inputs, wl, dev, code_id):
+    routing, rw = wl.routing(), wl.router_weights()
+    gu_arr = [wl.layer(e, w, code_id=code_id) for e in range(wl.experts) for w in ("gate", "up")]
+    dn_arr = [wl.layer(e, "down", code_id=code_id) for e in range(wl.experts)]
+    all_bytes = sum(a.code_bytes for a in gu_arr + dn_arr)
+    copies = _copies(all_bytes)
+    log(f"{wl.name} block: {all_bytes} code bytes for all experts, {copies} copies, {wl.tokens} tokens")
+    tables = []
+    for c in range(copies):
+        gu = [tg.DeviceLayer(wl.layer(e, w, copy=c, code_id=code_id), dev) for e in range(wl.experts)
+              for w in ("gate", "up")]
+        dn = [tg.DeviceLayer(wl.layer(e, "down", copy=c, code_id=code_id), dev) for e in range(wl.experts)]
+        tables.append((tg.LayerTable(gu, dev), tg.LayerTable(dn, dev)))
+    sels = [torch.tensor(routing[t], dtype=torch.int32, device=dev) for t in range(wl.tokens)]
+    wts = [torch.tensor(rw[t], dtype=torch.float32, device=dev) for t in range(wl.tokens)]
+    xs = [tg.fp16_tensor(inputs.make_x(wl.hidden, wl.seed, tensor=10_000 + t), dev) for t in range(wl.tokens)]
+    y = torch.empty(wl.hidden, dtype=torch.float32, device=dev)
+    ws = tg.moe_workspace(tables[0][0], tables[0][1], wl.top_k, dev)
+    tok_bytes = [sum(gu_arr[2 * int(e) + w].code_bytes for e in routing[t] for w in (0, 1)) +
+                 sum(dn_arr[int(e)].code_bytes for e in routing[t]) for t in range(wl.tokens)]
+
+    def step(i, launch):
+        t = i % wl.tokens
+        gu_t, dn_t = tables[(i // wl.tokens) % copies]
+        s = torch.cuda.current_stream()
+        launch("block", lambda: tg.trellis_moe_block(gu_t, dn_t, sels[t], wts[t], xs[t], y, ws, s))
+
+    mean_tok = float(np.mean(tok_bytes))
+    k2 = 2 * wl.top_k
+    # codes + x (fp16) + y (fp32) + scales (fp16) + the fp32 intermediates, each written once and read once
+    alg = {"block": mean_tok + 2 * wl.hidden + 4 * wl.hidden + 2 * (k2 * wl.inter + wl.top_k * wl.hidden) +
+           2 * 4 * (k2 * wl.inter + wl.top_k * wl.hidden)}
+    return step, dict(code_bytes=mean_tok, copies=copies, alg_bytes=alg, names=["block"],
+                      weights={"block": 3 * wl.top_k * wl.inter * wl.hidden}, mfma=False,
+                      units="token (MoE block, 3 launches)")
+
+
 def setup_moe(torch, tg, inputs, wl, dev, code_id):
     routing = wl.routing()
     gu_arr = [wl.layer(e, w, code_id=code_id) for e in range(wl.experts) for w in ("gate", "up")]
@@ -277,9 +316,9 @@ def run_gpu(workload, steps, warmup, use_graph, code_id=0):
     from trellis_coded_gemv_amd import inputs
 
     dev = "cuda"
-    wl = inputs.WORKLOADS[workload]
+    wl = workload_of(inputs, workload)
     setup = {1: setup_linears, 2: setup_linears, 3: setup_linears, 4: setup_gemm, 5: setup_moe,
-             6: setup_prefill}[workload]
+             6: setup_prefill, 7: setup_moe_block}[workload]
     step, info = setup(torch, tg, inputs, wl, dev, code_id)
     dom = max(info["names"], key=lambda k: info["alg_bytes"][k])     # kernel moving the most bytes
     stream = torch.cuda.current_stream()
@@ -313,6 +352,40 @@ def run_gpu(workload, steps, warmup, use_graph, code_id=0):
     return info, dict(region_ms=region_ms, eager_ms=eager_ms, dom=dom, dom_ms=dom_ms, timing=timing)
 
 
+def workload_of(inputs, workload):
+    """Workload 7 runs the experts of workload 5 as whole MoE blocks."""
+    return inputs.WORKLOADS[5 if workload == 7 else workload]
+
+
+def _moe_token(inputs, wl, code_id, t=0):
+    """Token t of the MoE workload: its selected experts' layers (keyed as in the tables), selection, weights, x."""
+    sel, w = wl.routing()[t], wl.router_weights()[t]
+    gu, dn = {}, {}
+    for e in sel:
+        e = int(e)
+        gu[2 * e], gu[2 * e + 1] = wl.layer(e, "gate", code_id=code_id), wl.layer(e, "up", code_id=code_id)
+        dn[e] = wl.layer(e, "down", code_id=code_id)
+    return gu, dn, sel, w, inputs.make_x(wl.hidden, wl.seed, tensor=10_000 + t)
+
+
+def moe_block_parity(inputs, wl, code_id):
+    """Token 0 through the whole block (all experts on the device, copy 0) against the oracle's block."""
+    import torch
+    from oracle import moe
+    from trellis_coded_gemv_amd import binding as tg
+
+    gu, dn, sel, w, x = _moe_token(inputs, wl, code_id)
+    gut = tg.LayerTable([tg.DeviceLayer(wl.layer(e, k, code_id=code_id), "cuda") for e in range(wl.experts)
+                         for k in ("gate", "up")], "cuda")
+    dnt = tg.LayerTable([tg.DeviceLayer(wl.layer(e, "down", code_id=code_id), "cuda") for e in range(wl.experts)],
+                        "cuda")
+    y = tg.trellis_moe_block(gut, dnt, torch.from_numpy(sel).to("cuda"), torch.from_numpy(w).to("cuda"),
+                             tg.fp16_tensor(x, "cuda"))
+    torch.cuda.synchronize()
+    ref = moe.moe_block(gu, dn, sel, w, x)
+    return float(np.abs(y.cpu().numpy() - ref).max() / np.abs(ref).max())
+
+
 def parity_spot_check(workload, code_id=0):
     """Copy 0 of the workload against the oracle on sampled outputs (after timing)."""
     import torch
@@ -320,7 +393,9 @@ def parity_spot_check(workload, code_id=0):
     from trellis_coded_gemv_amd import binding as tg
     from trellis_coded_gemv_amd import inputs
 
-    wl = inputs.WORKLOADS[workload]
+    wl = workload_of(inputs, workload)
+    if workload == 7:
+        return moe_block_parity(inputs, wl, code_id)
     if workload == 5:
         e, which = int(wl.routing()[0][0]), "gate"
         arr, x = wl.layer(e, which, code_id=code_id), inputs.make_x(wl.hidden, wl.seed, tensor=10_000)
@@ -354,8 +429,21 @@ def cpu_baseline(workload, sample_blocks, code_id=0):
     from oracle import gemv as ogemv
     from trellis_coded_gemv_amd import inputs
 
-    wl = inputs.WORKLOADS[workload]
-    if workload == 5:
+    wl = workload_of(inputs, workload)
+    if workload == 7:
+        from oracle import moe
+        dt, nbytes, ntok = 0.0, 0, 0
+        while ntok < wl.tokens and dt < 10.0:   # whole tokens, about 10 s of oracle work
+            gu, dn, sel, w, x = _moe_token(inputs, wl, code_id, ntok)
+            with threadpool_limits(limits=1):
+                t = time.perf_counter()
+                moe.moe_block(gu, dn, sel, w, x)
+                dt += time.perf_counter() - t
+            nbytes += sum(a.code_bytes for a in list(gu.values()) + list(dn.values()))
+            ntok += 1
+        sample = f"tokens 0..{ntok - 1}: the whole block over each token's {wl.top_k} experts ({nbytes} code bytes), {dt:.1f} s"
+        rate = nbytes / dt
+    elif workload == 5:
         arrs = [wl.layer(int(e), w, code_id=code_id) for e in wl.routing()[0][:2] for w in ("gate", "up", "down")]
         xs = [inputs.make_x(a.n, 1) for a in arrs]
         with threadpool_limits(limits=1):
@@ -399,7 +487,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--code", type=int, default=0, choices=[0, 1],
                     help="code_id of every layer: 0 the three-instruction code, 1 the pair code")
     ap.add_argument("--no-graph", action="store_true")
@@ -413,7 +501,7 @@ def main(argv=None):
         return 2
 
     from trellis_coded_gemv_amd import inputs
-    wl = inputs.WORKLOADS[args.workload]
+    wl = workload_of(inputs, args.workload)
     info, t = run_gpu(args.workload, args.steps, args.warmup, not args.no_graph, args.code)
     steps = args.steps
     ms_per_step = t["region_ms"] / steps
@@ -424,12 +512,12 @@ def main(argv=None):
     opw = alu_ops_per_weight(args.code, info["mfma"])
     alg_ops = info["weights"][dom] * opw
     alu_achieved = alg_ops / (dom_launch_ms * 1e-3) / 1e12
-    config = {"workload": wl.name, "units": info["units"], "code_bytes_per_step": int(info["code_bytes"]),
+    config = {"workload": wl.name + ("_block" if args.workload == 7 else ""), "units": info["units"], "code_bytes_per_step": int(info["code_bytes"]),
               "copies": info["copies"], "us_per_step": round(ms_per_step * 1e3, 3),
               "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
               "eager_us_per_step": round(t["eager_ms"] / steps * 1e3, 3),
               "code_id": args.code, "parity_max_rel_err": parity_spot_check(args.workload, args.code)}
-    if args.workload != 5:
+    if args.workload not in (5, 7):
         config.update({"tensors": {k: list(v) for k, v in wl.tensors.items()}, "batch": wl.batch})
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,

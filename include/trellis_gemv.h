@@ -201,6 +201,39 @@ int32_t trellis_gemv_grouped(const tg_layer *layers, const tg_layer *d_layers, i
 size_t tg_grouped_workspace_size(const tg_layer *layers, int32_t n_layers, int32_t n_sel);
 
 /*
+ * Mixture-of-experts block for one token over trellis-coded experts (Deep Dive,
+ * Section 4 and lecture, Part eleven: expert models, per-tensor bit widths):
+ *     y = sum_i w_i * down_{e_i}( fp16( silu(gate_{e_i}(x)) * up_{e_i}(x) ) ),
+ * silu(v) = v / (1 + exp(-v)), over the top_k selected experts e_i. Three
+ * launches: the 2*top_k gate/up GEMVs (one grouped launch, shared x), the
+ * top_k down GEMVs whose input transform forms fp16(silu(g)*u) from the first
+ * launch's fp32 rows, and the router-weighted sum in selection order.
+ *   gate_up / d_gate_up : host / device tables of n_gate_up = 2*n_down layers;
+ *                         entry 2e = gate and 2e+1 = up of expert e, each
+ *                         inter x hidden (out x in); all of one shape.
+ *   down / d_down       : host / device tables of n_down layers, hidden x inter.
+ *   d_sel               : device, top_k int32 expert ids (1 <= top_k <= min(n_down, 256));
+ *                         ids outside [0, n_down) contribute nothing.
+ *   d_weights           : device, top_k fp32 router weights.
+ *   x                   : device, hidden fp16; y : device, hidden fp32.
+ *   ws                  : device workspace, ws_bytes >= tg_moe_workspace_size(...),
+ *                         256-byte aligned and zero-filled before its first use. Every
+ *                         call leaves its arrival counters at zero again; the rest holds
+ *                         the call's intermediate rows. Calls that share a workspace
+ *                         must be ordered (one stream).
+ * All layers must share TG_FLAG_* flags. Errors: a negative tg_status (shape, table,
+ * top_k, alignment or workspace checks) with nothing launched.
+ */
+int32_t trellis_moe_block(const tg_layer *gate_up, const tg_layer *d_gate_up, int32_t n_gate_up,
+                          const tg_layer *down, const tg_layer *d_down, int32_t n_down,
+                          const int32_t *d_sel, const float *d_weights, int32_t top_k,
+                          const uint16_t *x, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for trellis_moe_block (0 if the tables / top_k are invalid). */
+size_t tg_moe_workspace_size(const tg_layer *gate_up, int32_t n_gate_up,
+                             const tg_layer *down, int32_t n_down, int32_t top_k);
+
+/*
  * Decode the whole layer to fp16 weights (test / export hook): w_out[o*n + i]
  * = W^[o, i] as fp16 patterns, bit-exact with the code's definition. Only
  * codes, k_bits, code_id and shape are used; m, n need only be positive

@@ -174,3 +174,20 @@ def test_prefill_argument_validation():
     assert L.trellis_gemm_prefill(ctypes.byref(d), 100, A16, 512, A16, 256, A16 + 16, need, None) == -4
     bad = _layer(k_bits=0)
     assert L.trellis_gemm_prefill(ctypes.byref(bad), 100, A16, 512, A16, 256, A16, need, None) == -3
+
+
+def test_moe_block_argument_validation():
+    L = tg.lib()
+    gu = (tg.TgLayer * 4)(*[_layer(m=256, n=512) for _ in range(4)])
+    dn = (tg.TgLayer * 2)(*[_layer(m=512, n=256) for _ in range(2)])
+    need = L.tg_moe_workspace_size(gu, 4, dn, 2, 2)
+    assert need > 0
+    assert L.tg_moe_workspace_size(gu, 3, dn, 2, 2) == 0            # gate/up table must be twice the down table
+    assert L.tg_moe_workspace_size(gu, 4, dn, 2, 3) == 0            # top_k above the expert count
+    bad = (tg.TgLayer * 2)(*[_layer(m=512, n=384) for _ in range(2)])
+    assert L.tg_moe_workspace_size(gu, 4, bad, 2, 2) == 0           # down must be hidden x inter
+    args = [gu, A16, 4, dn, A16, 2, A16, A16, 2, A16, A16]
+    assert L.trellis_moe_block(*args, 0, need, None) == -5
+    assert L.trellis_moe_block(*args, A16, need - 1, None) == -5
+    assert L.trellis_moe_block(gu, A16, 4, dn, A16, 2, 0, A16, 2, A16, A16, A16, need, None) == -1
+    assert L.trellis_moe_block(gu, A16, 4, dn, A16, 2, A16, A16, 0, A16, A16, A16, need, None) == -8

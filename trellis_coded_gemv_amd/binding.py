@@ -24,7 +24,8 @@ STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS",
 # every symbol the header declares
 EXPORTS = ("tg_abi_version", "tg_status_str", "tg_workspace_size", "trellis_gemv", "trellis_gemm_small",
            "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table",
-           "trellis_encode", "tg_encode_workspace_size", "trellis_gemm_prefill", "tg_prefill_workspace_size")
+           "trellis_encode", "tg_encode_workspace_size", "trellis_gemm_prefill", "tg_prefill_workspace_size",
+           "trellis_moe_block", "tg_moe_workspace_size")
 
 
 class TgLayer(ctypes.Structure):
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "tg_encode_workspace_size": (SZ, [I32, I32, I32]),
         "trellis_gemm_prefill": (I32, [LP, I32, P, I64, P, I64, P, SZ, P]),
         "tg_prefill_workspace_size": (SZ, [LP, I32]),
+        "trellis_moe_block": (I32, [LP, P, I32, LP, P, I32, P, P, I32, P, P, P, SZ, P]),
+        "tg_moe_workspace_size": (SZ, [LP, I32, LP, I32, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -288,3 +291,26 @@ def trellis_gemm_prefill(layer: DeviceLayer, X, Y=None, ws=None, stream=None):
     _check(lib().trellis_gemm_prefill(ctypes.byref(d), M, _ptr(X), ldx, _ptr(Y), ldy, _ptr(ws), ws.numel(),
                                       _stream(stream)), "trellis_gemm_prefill")
     return Y
+
+
+def moe_workspace(gate_up: "LayerTable", down: "LayerTable", top_k: int, device="cuda"):
+    torch = _torch()
+    n = lib().tg_moe_workspace_size(gate_up.host, len(gate_up), down.host, len(down), int(top_k))
+    if n == 0:
+        raise TgError(-8, "tg_moe_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def trellis_moe_block(gate_up: "LayerTable", down: "LayerTable", sel, weights, x, y=None, ws=None, stream=None):
+    """y [hidden] fp32 = sum_i w_i down_{sel_i}(fp16(silu(gate(x)) * up(x))); sel int32 / weights fp32 on device."""
+    torch = _torch()
+    top_k = int(sel.numel())
+    hidden = down.layers[0].m
+    if y is None:
+        y = torch.empty(hidden, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = moe_workspace(gate_up, down, top_k, x.device)
+    _check(lib().trellis_moe_block(gate_up.host, _ptr(gate_up.device), len(gate_up), down.host, _ptr(down.device),
+                                   len(down), _ptr(sel), _ptr(weights), top_k, _ptr(x), _ptr(y), _ptr(ws),
+                                   ws.numel(), _stream(stream)), "trellis_moe_block")
+    return y

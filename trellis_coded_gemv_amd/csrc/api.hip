@@ -209,6 +209,8 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
   a.m = L->m;
   a.n = L->n;
   a.splits = splits;
+  a.hg = nullptr;
+  a.hu = nullptr;
   return launch_status(
       launch_gemv(a, L->k_bits, L->code_id, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
 }
@@ -282,6 +284,9 @@ TG_API int32_t trellis_gemv_grouped(const tg_layer* layers, const tg_layer* d_la
   a.max_m = g.max_m;
   a.splits = g.splits;
   a.round_weights = (layers[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0;
+  a.sel_pairs = 0;
+  a.hin = nullptr;
+  a.hin_stride = 0;
   return launch_status(launch_grouped(a, g.max_m / kBlock, g.max_n, (hipStream_t)stream));
 }
 
@@ -403,4 +408,96 @@ TG_API int32_t trellis_gemm_prefill(const tg_layer* L, int32_t M, const uint16_t
     if (bs != rocblas_status_success) return TG_ERR_LAUNCH;
   }
   return launch_status(launch_prefill_out(Y, ldy, L->scales, L->sign_out, L->m, M, s));
+}
+
+namespace {
+
+struct MoeWs {
+  GroupedWs gu, dn;
+  int inter, hidden;
+  size_t gu_off, dn_off, y1, y2, total;
+};
+
+// Gate/up table: entry 2e = gate of expert e, 2e+1 = up (inter x hidden); down table:
+// entry e (hidden x inter). All experts share inter and hidden and the flags.
+int32_t moe_geometry(const tg_layer* gu, int32_t n_gu, const tg_layer* dn, int32_t n_dn, int32_t top_k, MoeWs* w) {
+  if (!gu || !dn) return TG_ERR_NULL;
+  if (n_dn < 1 || n_gu != 2 * n_dn || top_k < 1 || top_k > n_dn || top_k > 256) return TG_ERR_ARG;
+  int32_t st = grouped_geometry(gu, n_gu, 2 * top_k, &w->gu);
+  if (st != TG_OK) return st;
+  st = grouped_geometry(dn, n_dn, top_k, &w->dn);
+  if (st != TG_OK) return st;
+  w->inter = gu[0].m;
+  w->hidden = gu[0].n;
+  for (int i = 0; i < n_gu; ++i)
+    if (gu[i].m != w->inter || gu[i].n != w->hidden) return TG_ERR_SHAPE;
+  for (int i = 0; i < n_dn; ++i)
+    if (dn[i].m != w->hidden || dn[i].n != w->inter) return TG_ERR_SHAPE;
+  if (gu[0].flags != dn[0].flags) return TG_ERR_ARG;
+  w->gu_off = 0;
+  w->dn_off = round_up(w->gu.total, kAlign);
+  w->y1 = w->dn_off + round_up(w->dn.total, kAlign);
+  w->y2 = w->y1 + round_up((size_t)2 * top_k * w->inter * 4, kAlign);
+  w->total = w->y2 + round_up((size_t)top_k * w->hidden * 4, kAlign);
+  return TG_OK;
+}
+
+GroupedArgs grouped_args(const tg_layer* d_layers, int32_t n_layers, const int32_t* d_sel, int32_t n_sel,
+                         const GroupedWs& g, char* ws, float* y, int64_t y_stride, bool round) {
+  GroupedArgs a;
+  a.layers = reinterpret_cast<const LayerDev*>(d_layers);
+  a.sel = d_sel;
+  a.n_layers = n_layers;
+  a.n_sel = n_sel;
+  a.x = nullptr;
+  a.x_stride = 0;
+  a.y = y;
+  a.y_stride = y_stride;
+  a.counters = reinterpret_cast<uint32_t*>(ws + g.counters);
+  a.partials = reinterpret_cast<float*>(ws + g.partials);
+  a.max_m = g.max_m;
+  a.splits = g.splits;
+  a.round_weights = round ? 1 : 0;
+  a.sel_pairs = 0;
+  a.hin = nullptr;
+  a.hin_stride = 0;
+  return a;
+}
+
+}  // namespace
+
+TG_API size_t tg_moe_workspace_size(const tg_layer* gate_up, int32_t n_gate_up, const tg_layer* down, int32_t n_down,
+                                    int32_t top_k) {
+  MoeWs w;
+  if (moe_geometry(gate_up, n_gate_up, down, n_down, top_k, &w) != TG_OK) return 0;
+  return w.total;
+}
+
+TG_API int32_t trellis_moe_block(const tg_layer* gate_up, const tg_layer* d_gate_up, int32_t n_gate_up,
+                                 const tg_layer* down, const tg_layer* d_down, int32_t n_down, const int32_t* d_sel,
+                                 const float* d_weights, int32_t top_k, const uint16_t* x, float* y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  MoeWs w;
+  int32_t st = moe_geometry(gate_up, n_gate_up, down, n_down, top_k, &w);
+  if (st != TG_OK) return st;
+  if (!d_gate_up || !d_down || !d_sel || !d_weights || !x || !y) return TG_ERR_NULL;
+  if (misaligned(d_gate_up, 8) || misaligned(d_down, 8) || misaligned(d_sel, 4) || misaligned(d_weights, 4) ||
+      misaligned(x, 2) || misaligned(y, 4))
+    return TG_ERR_ALIGN;
+  if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
+  if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  float* Y1 = reinterpret_cast<float*>(base + w.y1);   // [2 top_k][inter]: gate, up rows per selection
+  float* Y2 = reinterpret_cast<float*>(base + w.y2);   // [top_k][hidden]
+  const bool round = (gate_up[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0;
+  GroupedArgs g1 = grouped_args(d_gate_up, n_gate_up, d_sel, 2 * top_k, w.gu, base + w.gu_off, Y1, w.inter, round);
+  g1.x = x;
+  g1.sel_pairs = 1;
+  if (launch_grouped(g1, w.gu.max_m / kBlock, w.gu.max_n, s) != hipSuccess) return TG_ERR_LAUNCH;
+  GroupedArgs g2 = grouped_args(d_down, n_down, d_sel, top_k, w.dn, base + w.dn_off, Y2, w.hidden, round);
+  g2.hin = Y1;
+  g2.hin_stride = w.inter;
+  if (launch_grouped(g2, w.dn.max_m / kBlock, w.dn.max_n, s) != hipSuccess) return TG_ERR_LAUNCH;
+  return launch_status(launch_moe_combine(Y2, w.hidden, d_sel, d_weights, top_k, n_down, w.hidden, y, s));
 }

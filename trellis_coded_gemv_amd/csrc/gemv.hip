@@ -169,7 +169,9 @@ __device__ __forceinline__ void read_xx(const uint32_t* xx_lds, int tile, uint32
 
 // One workgroup = 8 tile rows (a 128-output block) x one input chunk, with P
 // waves per tile row that take interleaved 16-tile steps of the chunk.
-template <int K, int CODE, bool ROUND, int PF, int P>
+// GATED: the input is fp16(silu(a.hg) * a.hu) (the down projection of a gated
+// expert MLP) instead of the fp16 vector a.x.
+template <int K, int CODE, bool ROUND, int PF, int P, bool GATED = false>
 __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int split, uint32_t* lds) {
   constexpr int NW = 2 * K;
   constexpr int NX = CODE == 0 ? 16 : 8;   // input words per tile column
@@ -203,7 +205,13 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   const int nbp = 2 * nsteps;                       // blocks incl. the zero padding to whole steps
   const int xb = 8 * wave + (lane >> 3), xs = lane & 7;
   const int xfirst = (blk0 + (xb < cb ? xb : cb - 1)) * kBlock + 16 * xs;
-  const X16 xraw = load_x16(a.x, a.sign_in, xfirst);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wunused-variable"
+  X16 xraw;
+  XGated16 graw;
+#pragma clang diagnostic pop
+  if constexpr (GATED) graw = load_gated16(a.hg, a.hu, a.sign_in, xfirst);
+  else xraw = load_x16(a.x, a.sign_in, xfirst);
   __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the prefetch below
 
   // Prefetch ring. Every issue is unconditional (out-of-range steps and tiles
@@ -226,6 +234,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
     const bool active = xb < nbp, live = xb < cb;
     float* sc = reinterpret_cast<float*>(xx_lds) + xb * kBlock;
     float v[16];
+    if constexpr (GATED) xraw = gated_to_x16(graw);
     x16_phase1(xraw, xfirst, v);
     if (active) {
 #pragma unroll
@@ -344,21 +353,23 @@ __global__ __launch_bounds__(64 * 8 * P) void gemv_kernel(GemvArgs a) {
   gemv_workgroup<K, CODE, ROUND, PF, P>(a, ob, bid - ob * a.splits, lds);
 }
 
-template <int CODE, bool ROUND>
+template <int CODE, bool ROUND, bool GATED>
 __device__ __forceinline__ void grouped_dispatch(const GemvArgs& a, int k_bits, int ob, int split, uint32_t* lds) {
   switch (k_bits) {
-    case 1: gemv_workgroup<1, CODE, ROUND, gemv_pf<1>(), kGemvP>(a, ob, split, lds); break;
-    case 2: gemv_workgroup<2, CODE, ROUND, gemv_pf<2>(), kGemvP>(a, ob, split, lds); break;
-    case 3: gemv_workgroup<3, CODE, ROUND, gemv_pf<3>(), kGemvP>(a, ob, split, lds); break;
-    case 4: gemv_workgroup<4, CODE, ROUND, gemv_pf<4>(), kGemvP>(a, ob, split, lds); break;
-    case 5: gemv_workgroup<5, CODE, ROUND, gemv_pf<5>(), kGemvP>(a, ob, split, lds); break;
-    case 6: gemv_workgroup<6, CODE, ROUND, gemv_pf<6>(), kGemvP>(a, ob, split, lds); break;
-    case 7: gemv_workgroup<7, CODE, ROUND, gemv_pf<7>(), kGemvP>(a, ob, split, lds); break;
-    default: gemv_workgroup<8, CODE, ROUND, gemv_pf<8>(), kGemvP>(a, ob, split, lds); break;
+    case 1: gemv_workgroup<1, CODE, ROUND, gemv_pf<1>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 2: gemv_workgroup<2, CODE, ROUND, gemv_pf<2>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 3: gemv_workgroup<3, CODE, ROUND, gemv_pf<3>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 4: gemv_workgroup<4, CODE, ROUND, gemv_pf<4>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 5: gemv_workgroup<5, CODE, ROUND, gemv_pf<5>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 6: gemv_workgroup<6, CODE, ROUND, gemv_pf<6>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 7: gemv_workgroup<7, CODE, ROUND, gemv_pf<7>(), kGemvP, GATED>(a, ob, split, lds); break;
+    default: gemv_workgroup<8, CODE, ROUND, gemv_pf<8>(), kGemvP, GATED>(a, ob, split, lds); break;
   }
 }
 
-template <bool ROUND>
+// Selection e of the launch runs layer sel[e] (or, with sel_pairs, layer
+// 2*sel[e/2] + e%2: the gate and up of the selected experts, from one id each).
+template <bool ROUND, bool GATED>
 __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g, int max_ob) {
   extern __shared__ uint32_t lds[];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -366,8 +377,9 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
   const int e = bid / per_sel;
   const int rem = bid - e * per_sel;
   const int ob = rem / g.splits, split = rem - ob * g.splits;
-  const int li = g.sel[e];
-  if (li < 0 || li >= g.n_layers) return;
+  const int sv = g.sel[g.sel_pairs ? (e >> 1) : e];
+  if (sv < 0 || sv >= (g.sel_pairs ? (g.n_layers >> 1) : g.n_layers)) return;
+  const int li = g.sel_pairs ? 2 * sv + (e & 1) : sv;
   const LayerDev L = g.layers[li];
   if (ob >= (L.m >> 7)) return;
   GemvArgs a;
@@ -382,8 +394,25 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
   a.m = L.m;
   a.n = L.n;
   a.splits = g.splits;
-  if (L.code_id == 0) grouped_dispatch<0, ROUND>(a, L.k_bits, ob, split, lds);
-  else grouped_dispatch<1, ROUND>(a, L.k_bits, ob, split, lds);
+  a.hg = GATED ? g.hin + (size_t)(2 * e) * g.hin_stride : nullptr;
+  a.hu = GATED ? g.hin + (size_t)(2 * e + 1) * g.hin_stride : nullptr;
+  if (L.code_id == 0) grouped_dispatch<0, ROUND, GATED>(a, L.k_bits, ob, split, lds);
+  else grouped_dispatch<1, ROUND, GATED>(a, L.k_bits, ob, split, lds);
+}
+
+// Router-weighted sum of the selected experts' outputs, in selection order;
+// selections outside [0, n_experts) contribute nothing.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ Y2, int64_t y2_stride,
+                                                          const int32_t* __restrict__ sel, const float* __restrict__ w,
+                                                          int top_k, int n_experts, int hidden, float* __restrict__ y) {
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= hidden) return;
+  float acc = 0.f;
+  for (int e = 0; e < top_k; ++e) {
+    const int s = sel[e];
+    if (s >= 0 && s < n_experts) acc += w[e] * Y2[(size_t)e * y2_stride + o];
+  }
+  y[o] = acc;
 }
 
 template <int K, int CODE, bool ROUND>
@@ -412,16 +441,31 @@ hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_we
   return code_id == 0 ? launch_code<0>(a, k_bits, round_weights, s) : launch_code<1>(a, k_bits, round_weights, s);
 }
 
+template <bool ROUND, bool GATED>
+static void launch_grouped_t(const GroupedArgs& g, int max_ob, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_kernel<ROUND, GATED>), dim3(grid), dim3(64 * 8 * kGemvP), lds, s, g, max_ob);
+}
+
 hipError_t launch_grouped(const GroupedArgs& g, int max_ob, int max_n, hipStream_t s) {
   const int grid = g.n_sel * max_ob * g.splits;
   if (grid == 0) return hipSuccess;
   const int max_chunk = ((max_n >> 7) + g.splits - 1) / g.splits;
-  if (g.round_weights)
-    hipLaunchKernelGGL(grouped_kernel<true>, dim3(grid), dim3(64 * 8 * kGemvP), gemv_lds_bytes(max_chunk), s, g,
-                       max_ob);
-  else
-    hipLaunchKernelGGL(grouped_kernel<false>, dim3(grid), dim3(64 * 8 * kGemvP), gemv_lds_bytes(max_chunk), s, g,
-                       max_ob);
+  const size_t lds = gemv_lds_bytes(max_chunk);
+  const bool gated = g.hin != nullptr;
+  if (g.round_weights) {
+    if (gated) launch_grouped_t<true, true>(g, max_ob, grid, lds, s);
+    else launch_grouped_t<true, false>(g, max_ob, grid, lds, s);
+  } else {
+    if (gated) launch_grouped_t<false, true>(g, max_ob, grid, lds, s);
+    else launch_grouped_t<false, false>(g, max_ob, grid, lds, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const float* Y2, int64_t y2_stride, const int32_t* sel, const float* w, int top_k,
+                              int n_experts, int hidden, float* y, hipStream_t s) {
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((hidden + 255) / 256), dim3(256), 0, s, Y2, y2_stride, sel, w, top_k,
+                     n_experts, hidden, y);
   return hipGetLastError();
 }
 

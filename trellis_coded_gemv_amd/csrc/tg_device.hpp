@@ -195,6 +195,46 @@ __device__ __forceinline__ X16 load_x16(const uint16_t* __restrict__ x, const ui
   return r;
 }
 
+// Gated-MLP input of one lane: 16 fp32 gate and up values and the sign word.
+// The vector loads are copied out component by component (.x .. .w): this
+// compiler turned a bit_cast of a subscripted vector element into a read of
+// component 0.
+struct XGated16 {
+  float g[16], u[16];
+  uint32_t sw;
+};
+
+__device__ __forceinline__ XGated16 load_gated16(const float* __restrict__ hg, const float* __restrict__ hu,
+                                                 const uint32_t* __restrict__ sign_in, int first) {
+  XGated16 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4_t vg = reinterpret_cast<const float4_t*>(hg + first)[i];
+    const float4_t vu = reinterpret_cast<const float4_t*>(hu + first)[i];
+    r.g[4 * i] = vg.x, r.g[4 * i + 1] = vg.y, r.g[4 * i + 2] = vg.z, r.g[4 * i + 3] = vg.w;
+    r.u[4 * i] = vu.x, r.u[4 * i + 1] = vu.y, r.u[4 * i + 2] = vu.z, r.u[4 * i + 3] = vu.w;
+  }
+  r.sw = sign_in[first >> 5];
+  return r;
+}
+
+// x = fp16(silu(g) * u), silu(v) = v / (1 + exp(-v)), packed as the fp16 input words.
+__device__ __forceinline__ X16 gated_to_x16(const XGated16& r) {
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const float h0 = r.g[j] / (1.f + expf(-r.g[j])) * r.u[j];
+    const float h1 = r.g[j + 1] / (1.f + expf(-r.g[j + 1])) * r.u[j + 1];
+    w[j >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h1) << 16);
+  }
+  X16 x;
+  x.lo = u32x4{w[0], w[1], w[2], w[3]};
+  x.hi = u32x4{w[4], w[5], w[6], w[7]};
+  x.sw = r.sw;
+  return x;
+}
+
 // v[j] = s[first+j] * x[first+j] / sqrt(128), then the 16-point transform over j.
 __device__ __forceinline__ void x16_phase1(const X16& r, int first, float (&v)[16]) {
   const uint32_t sb = r.sw >> (first & 16);   // bit j: sign of element first + j

@@ -28,6 +28,8 @@ struct GemvArgs {
   float* partials;      // [splits][m]   (unused when splits == 1)
   uint32_t* counters;   // [m/128]       arrival counters, zero between calls
   int32_t m, n, splits;
+  const float* hg;      // gated-MLP input mode: x = fp16(silu(hg) * hu), fp32 rows of n values
+  const float* hu;
 };
 
 // Grouped batch-1 GEMVs: the layer table lives in device memory.
@@ -50,6 +52,9 @@ struct GroupedArgs {
   float* partials;      // [n_sel][splits][max_m]
   uint32_t* counters;   // [n_sel][max_m/128]
   int32_t max_m, splits, round_weights;
+  int32_t sel_pairs;    // 1: selection e uses layer 2*sel[e/2] + e%2 (gate and up of the selected experts)
+  const float* hin;     // non-null: selection e's input is fp16(silu(hin row 2e) * hin row 2e+1)
+  int64_t hin_stride;   // floats between hin rows
 };
 
 // Small-batch MFMA path.
@@ -67,6 +72,8 @@ struct GemmArgs {
 
 hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_weights, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, int max_ob, int max_n, hipStream_t s);
+hipError_t launch_moe_combine(const float* Y2, int64_t y2_stride, const int32_t* sel, const float* w, int top_k,
+                              int n_experts, int hidden, float* y, hipStream_t s);
 hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in,
                              int k_bits, int code_id, bool round_weights, hipStream_t s);
 hipError_t launch_rht(int n, int rows, const uint16_t* in, float* out, const uint32_t* signs, bool inverse,

@@ -27,7 +27,7 @@ from typing import Dict, List, Sequence
 import numpy as np
 
 # field identifiers of the seed sequence
-F_CODES, F_SCALES, F_SIGN_IN, F_SIGN_OUT, F_X, F_KBITS, F_ROUTING = range(7)
+F_CODES, F_SCALES, F_SIGN_IN, F_SIGN_OUT, F_X, F_KBITS, F_ROUTING, F_ROUTER_W = range(8)
 
 TILE = 16            # 16 x 16 weights per trellis sequence
 RHT_BLOCK = 128      # Hadamard block along each axis
@@ -79,6 +79,13 @@ def make_x(n: int, seed: int, tensor: int = 0, copy: int = 0, rows: int = 1) -> 
 
 def draw_kbits(seed: int, tensor: int, choices: Sequence[int]) -> int:
     return int(_rng(seed, tensor, 0, F_KBITS).choice(np.asarray(choices)))
+
+
+def draw_router_weights(seed: int, tokens: int, top_k: int) -> np.ndarray:
+    """Router weights of the selected experts: softmax over top_k N(0,1) logits per token. float32 [tokens, top_k]."""
+    logits = _rng(seed, 0, 0, F_ROUTER_W).standard_normal((tokens, top_k))
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 def draw_routing(seed: int, tokens: int, experts: int, top_k: int) -> np.ndarray:
@@ -144,6 +151,9 @@ class MoEWorkload:
 
     def routing(self) -> np.ndarray:
         return draw_routing(self.seed, self.tokens, self.experts, self.top_k)
+
+    def router_weights(self) -> np.ndarray:
+        return draw_router_weights(self.seed, self.tokens, self.top_k)
 
 
 CFG5 = MoEWorkload()
