@@ -109,10 +109,13 @@ const char *tg_status_str(int32_t status);
 /*
  * Workspace bytes needed by trellis_gemv (M == 1) or trellis_gemm_small
  * (1 <= M <= 64) for this layer, or 0 if the layer / M is invalid.
- * The workspace holds split-K partial sums and per-output-block arrival
- * counters. It must be zero-filled before its first use; every completed call
- * leaves it zero-filled again, so it can be reused by later calls on the same
- * stream. 256-byte alignment is required.
+ * Layout: two counter areas of fixed size (256 KiB in all: the batch-1
+ * tickets and the small-batch arrival counters, each sized for the largest
+ * layer), then scratch (split-K partials, the small-batch input transform).
+ * It must be zero-filled before its first use. Every completed call leaves the
+ * counters at zero; the scratch may hold anything between calls. One buffer,
+ * as large as each layer needs, can therefore serve any sequence of layers and
+ * of both entry points on one stream. 256-byte alignment is required.
  */
 size_t tg_workspace_size(const tg_layer *layer, int32_t M);
 
@@ -122,6 +125,11 @@ size_t tg_workspace_size(const tg_layer *layer, int32_t M);
  *   x  : device, n fp16 patterns.
  *   y  : device, m fp32 outputs, 4-byte aligned.
  *   ws : device workspace of ws_bytes >= tg_workspace_size(layer, 1).
+ * With split-K, the workgroups of an output block hand their partial sums to
+ * one of them through the workspace; its wait for them is bounded (about a
+ * second) and, should the device ever stall a workgroup that long, the
+ * affected outputs are written as NaN and the workspace must be zero-filled
+ * again before reuse.
  */
 int32_t trellis_gemv(const tg_layer *layer, const uint16_t *x, float *y,
                      void *ws, size_t ws_bytes, void *stream);

@@ -108,6 +108,25 @@ def test_grouped_moe_config5(token):
         assert rel_err(y2[e], ogemv.gemv(dn[li], xd[e])) <= REL_TOL, (e, li)
 
 
+def test_grouped_workspace_reuse():
+    """A second call on the same workspace gives the same bits; the arrival counters are back at zero."""
+    dev = device()
+    import torch
+    wl = inputs.CFG5
+    _, _, dn, dn_table = _moe_tables(dev, wl)
+    sel = torch.tensor([3, 77, 12, 100], dtype=torch.int32, device=dev)
+    X = tg.fp16_tensor(inputs.make_x(wl.inter, 5, rows=4), dev)
+    ws = tg.grouped_workspace(dn_table, 4, dev)
+    say("grouped workspace reuse")
+    Y1 = tg.trellis_gemv_grouped(dn_table, sel, X, wl.inter, torch.zeros(4, wl.hidden, device=dev), wl.hidden, ws)
+    torch.cuda.synchronize()
+    counters = 4 * (wl.hidden // 128) * 4                # one per selection and 128-output block
+    assert int(ws[:counters].count_nonzero()) == 0
+    Y2 = tg.trellis_gemv_grouped(dn_table, sel, X, wl.inter, torch.zeros(4, wl.hidden, device=dev), wl.hidden, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+
+
 def test_grouped_out_of_range_selection_writes_nothing():
     dev = device()
     import torch

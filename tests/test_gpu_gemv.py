@@ -122,3 +122,46 @@ def test_gemv_edge_values():
     x = inputs.make_x(256, 99)
     y = _run_gemv(arr, x, dev)
     assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
+
+
+@pytest.mark.parametrize("splits", ["40", "64"])
+def test_gemv_many_splits(splits, monkeypatch):
+    """More splits than one pass of the reducer covers (8 waves x 4 slots): chunks of one and two 128-blocks."""
+    dev = device()
+    monkeypatch.setenv("TG_SPLITK", splits)
+    arr = inputs.make_layer(256, 8192, 2, 89)
+    x = inputs.make_x(8192, 89)
+    say("many splits", splits)
+    y = _run_gemv(arr, x, dev)
+    assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
+
+
+def test_workspace_shared_by_layers_and_paths():
+    """One buffer serves two layers on both paths, its scratch first filled with ones (every split-K
+    slot then looks full): each result equals the one computed on a fresh workspace, bit for bit,
+    and the counter areas are zero after every call."""
+    dev = device()
+    import torch
+    a_arr = inputs.make_layer(1024, 4096, 3, 90)
+    b_arr = inputs.make_layer(512, 8192, 2, 91)
+    A, B = tg.DeviceLayer(a_arr, dev), tg.DeviceLayer(b_arr, dev)
+    xa, xb = tg.fp16_tensor(inputs.make_x(4096, 90), dev), tg.fp16_tensor(inputs.make_x(8192, 91), dev)
+    Xa = tg.fp16_tensor(inputs.make_x(4096, 92, rows=16), dev)
+    Xb = tg.fp16_tensor(inputs.make_x(8192, 93, rows=5), dev)
+    size = max(tg.workspace(A, 16, dev).numel(), tg.workspace(B, 16, dev).numel())
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+    counters = 2 * (1 << 22) // 128 * 4        # the batch-1 and small-batch counter areas
+    ws[counters:] = 0xFF
+    say("shared workspace")
+    ref = {"ga": tg.trellis_gemm_small(A, Xa), "vb": tg.trellis_gemv(B, xb),
+           "gb": tg.trellis_gemm_small(B, Xb), "va": tg.trellis_gemv(A, xa)}
+    calls = [("va", lambda: tg.trellis_gemv(A, xa, ws=ws)), ("ga", lambda: tg.trellis_gemm_small(A, Xa, ws=ws)),
+             ("vb", lambda: tg.trellis_gemv(B, xb, ws=ws)), ("gb", lambda: tg.trellis_gemm_small(B, Xb, ws=ws)),
+             ("va", lambda: tg.trellis_gemv(A, xa, ws=ws)), ("vb", lambda: tg.trellis_gemv(B, xb, ws=ws))]
+    for name, call in calls:
+        y = call()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[name]), name
+        assert (ws[:counters] == 0).all(), name
+    rows = sample_rows(512)
+    assert rel_err(ref["vb"].cpu().numpy()[rows], ogemv.gemv_rows(b_arr, inputs.make_x(8192, 91), rows)) <= REL_TOL

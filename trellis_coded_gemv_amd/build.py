@@ -35,6 +35,9 @@ def hipcc() -> str:
 def compile_flags():
     return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # every atomic here is issued by one lane; the optimizer's wave-wide
+            # rewrite would wait for the result at once instead of where it is used
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

@@ -100,15 +100,23 @@ int gemm_splits(int m, int n, int M, int k_bits, int code_id) {
   return s;
 }
 
+// A layer's workspace: the batch-1 ticket counters and the small-batch
+// arrival counters, each in an area sized for the largest layer (so every
+// layer finds its counters at the same place), then scratch shared by both
+// paths. Every call leaves the counters it used at zero; the scratch may hold
+// anything between calls (the batch-1 path empties its own slots before use).
+// One buffer can therefore serve any sequence of layers and paths.
+constexpr size_t kCounterArea = (size_t)((1 << 22) / kBlock) * 4;
+
 struct GemvWs {
-  size_t counters, partials, total;
+  size_t counters, slots, total;
 };
 
 GemvWs gemv_ws(int m, int splits) {
   GemvWs w;
   w.counters = 0;
-  w.partials = round_up((size_t)(m / kBlock) * 4, kAlign);
-  w.total = w.partials + (splits > 1 ? round_up((size_t)splits * m * 4, kAlign) : 0);
+  w.slots = 2 * kCounterArea;
+  w.total = w.slots + (splits > 1 ? round_up((size_t)splits * m * 8, kAlign) : 0);
   return w;
 }
 
@@ -119,8 +127,8 @@ struct GemmWs {
 GemmWs gemm_ws(int m, int n, int M, int splits) {
   GemmWs w;
   const int mpad = (M + 15) / 16 * 16;
-  w.counters = 0;
-  w.xt = round_up((size_t)(m / kBlock) * 4, kAlign);
+  w.counters = kCounterArea;
+  w.xt = 2 * kCounterArea;
   w.partials = w.xt + round_up((size_t)mpad * n * 4, kAlign);
   w.total = w.partials + (splits > 1 ? round_up((size_t)splits * M * m * 4, kAlign) : 0);
   return w;
@@ -128,7 +136,7 @@ GemmWs gemm_ws(int m, int n, int M, int splits) {
 
 struct GroupedWs {
   int max_m, max_n, splits;
-  size_t counters, partials, total;
+  size_t counters, slots, total;
 };
 
 int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel, GroupedWs* g) {
@@ -153,8 +161,8 @@ int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel
   g->max_n = max_n;
   g->splits = s;
   g->counters = 0;
-  g->partials = round_up((size_t)n_sel * max_ob * 4, kAlign);
-  g->total = g->partials + round_up((size_t)n_sel * s * max_m * 4, kAlign);
+  g->slots = round_up((size_t)n_sel * max_ob * 4, kAlign);
+  g->total = g->slots + round_up((size_t)n_sel * s * max_m * 8, kAlign);
   return TG_OK;
 }
 
@@ -182,7 +190,6 @@ TG_API const char* tg_status_str(int32_t status) {
 TG_API size_t tg_workspace_size(const tg_layer* L, int32_t M) {
   if (check_layer(L) != TG_OK || M < 1 || M > 64) return 0;
   const size_t g = gemm_ws(L->m, L->n, M, gemm_splits(L->m, L->n, M, L->k_bits, L->code_id)).total;
-  if (M > 1) return g;
   const size_t v = gemv_ws(L->m, gemv_splits(L->m, L->n)).total;
   return v > g ? v : g;
 }
@@ -205,7 +212,7 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
   a.x = x;
   a.y = y;
   a.counters = reinterpret_cast<uint32_t*>((char*)ws + w.counters);
-  a.partials = reinterpret_cast<float*>((char*)ws + w.partials);
+  a.slots = reinterpret_cast<uint64_t*>((char*)ws + w.slots);
   a.m = L->m;
   a.n = L->n;
   a.splits = splits;
@@ -280,7 +287,7 @@ TG_API int32_t trellis_gemv_grouped(const tg_layer* layers, const tg_layer* d_la
   a.y = Y;
   a.y_stride = y_stride;
   a.counters = reinterpret_cast<uint32_t*>((char*)ws + g.counters);
-  a.partials = reinterpret_cast<float*>((char*)ws + g.partials);
+  a.slots = reinterpret_cast<uint64_t*>((char*)ws + g.slots);
   a.max_m = g.max_m;
   a.splits = g.splits;
   a.round_weights = (layers[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0;
@@ -454,7 +461,7 @@ GroupedArgs grouped_args(const tg_layer* d_layers, int32_t n_layers, const int32
   a.y = y;
   a.y_stride = y_stride;
   a.counters = reinterpret_cast<uint32_t*>(ws + g.counters);
-  a.partials = reinterpret_cast<float*>(ws + g.partials);
+  a.slots = reinterpret_cast<uint64_t*>(ws + g.slots);
   a.max_m = g.max_m;
   a.splits = g.splits;
   a.round_weights = round ? 1 : 0;

@@ -328,4 +328,35 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
   __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Split-K by ticket and slots (batch-1 and grouped paths). Every workgroup of
+// an output block takes a ticket when it starts; the holder of the last
+// ticket reduces. The others have all started by then and finish without
+// waiting on anything, so the reducer's wait for their partials ends. A slot
+// is one 64-bit word per partial: the fp32 bits with bit 32 set when full, 0
+// when empty. One atomic store publishes value and state together, so a
+// writer never waits for its store to land.
+constexpr uint32_t kSlotPolls = 1u << 20;   // bound of one wait: re-reads, about a second in all
+
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void put_slot(uint64_t* p, float v) {
+  __hip_atomic_store(p, (uint64_t)__builtin_bit_cast(uint32_t, v) | (1ull << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t peek_slot(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void clear_slot(uint64_t* p) {
+  __hip_atomic_store(p, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Value of a slot read; NaN if it is still empty (a wait that ran out).
+__device__ __forceinline__ float slot_value(uint64_t s) {
+  return (s >> 32) != 0u ? __builtin_bit_cast(float, (uint32_t)s) : __builtin_nanf("");
+}
+
 }  // namespace tg

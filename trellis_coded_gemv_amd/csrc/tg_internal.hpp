@@ -25,8 +25,8 @@ struct GemvArgs {
   const uint32_t* sign_out;
   const uint16_t* x;
   float* y;
-  float* partials;      // [splits][m]   (unused when splits == 1)
-  uint32_t* counters;   // [m/128]       arrival counters, zero between calls
+  uint64_t* slots;      // [m/128][splits][128] split-K slots (unused when splits == 1), empty between calls
+  uint32_t* counters;   // [m/128]       ticket counters, zero between calls
   int32_t m, n, splits;
   const float* hg;      // gated-MLP input mode: x = fp16(silu(hg) * hu), fp32 rows of n values
   const float* hu;
@@ -49,7 +49,7 @@ struct GroupedArgs {
   int64_t x_stride;
   float* y;
   int64_t y_stride;
-  float* partials;      // [n_sel][splits][max_m]
+  uint64_t* slots;      // fp32 split-K partials [n_sel][splits][max_m] (8 bytes reserved per partial)
   uint32_t* counters;   // [n_sel][max_m/128]
   int32_t max_m, splits, round_weights;
   int32_t sel_pairs;    // 1: selection e uses layer 2*sel[e/2] + e%2 (gate and up of the selected experts)
