@@ -349,7 +349,29 @@ def run_gpu(workload, steps, warmup, use_graph, code_id=0):
         t1.record(stream)
         torch.cuda.synchronize()
         dom_ms = t0.elapsed_time(t1)
-    return info, dict(region_ms=region_ms, eager_ms=eager_ms, dom=dom, dom_ms=dom_ms, timing=timing)
+    # Context only, never the metric: the same copy every step (its code words stay in the caches).
+    hot_ms = None
+    if timing == "graph replay":
+        hot_ms = graph_time_ms(torch, lambda i, launches: step(0, launches), steps, Launches())
+    return info, dict(region_ms=region_ms, eager_ms=eager_ms, dom=dom, dom_ms=dom_ms, timing=timing, hot_ms=hot_ms,
+                      stream_read_gbs=stream_read_gbs(torch))
+
+
+def stream_read_gbs(torch, nbytes=1 << 30, reps=5):
+    """Context: a plain streaming read on the same GPU in the same run (torch.sum over 1 GiB viewed as fp64, the
+    fastest read-only library kernel measured here), GB/s, best of reps."""
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps + 1):
+        a.record()
+        buf.view(torch.float64).sum()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None or ms < best else best
+    del buf
+    return round(nbytes / (best * 1e-3) / 1e9, 1)
 
 
 def workload_of(inputs, workload):
@@ -466,17 +488,23 @@ def cpu_baseline(workload, sample_blocks, code_id=0):
         nblk = max(1, sample_blocks // Mo)
         blocks = np.linspace(0, nb - 1, min(nblk, nb)).astype(int)
         rows = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
+        def one_pass():
+            if Mo == 1:
+                ogemv.gemv_rows(arr, X, rows)
+            else:
+                ogemv.gemm_rows(arr, X, rows)
         with threadpool_limits(limits=1):
-            for _ in range(2):                 # the second (warm) pass is the one reported
+            one_pass()                         # warm-up pass, not timed
+            passes, total = 0, 0.0
+            while passes < 8 and (passes == 0 or total < 10.0):   # whole passes, about 10 s in all
                 t = time.perf_counter()
-                if Mo == 1:
-                    ogemv.gemv_rows(arr, X, rows)
-                else:
-                    ogemv.gemm_rows(arr, X, rows)
-                dt = time.perf_counter() - t
+                one_pass()
+                total += time.perf_counter() - t
+                passes += 1
+        dt = total / passes
         nbytes = len(rows) * n * k // 8
         sample = (f"{len(blocks)} of {nb} 128-output blocks of the {m}x{n} K={k} '{name}' tensor"
-                  f"{'' if M == 1 else f' x {Mo} rows'} (decode + fp64 GEMV), {dt:.1f} s"
+                  f"{'' if M == 1 else f' x {Mo} rows'} (decode + fp64 GEMV), {passes} timed pass(es) of {dt:.1f} s"
                   f"{'' if Mo == M else f', scaled to {M} rows'}")
         rate = nbytes / (dt * M / Mo)
     return {"value": round(rate / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}
@@ -516,6 +544,9 @@ def main(argv=None):
               "copies": info["copies"], "us_per_step": round(ms_per_step * 1e3, 3),
               "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
               "eager_us_per_step": round(t["eager_ms"] / steps * 1e3, 3),
+              "context": {"hot_cache_us_per_step": None if t["hot_ms"] is None else round(t["hot_ms"] / steps * 1e3, 3),
+                          "stream_read_gbs": t["stream_read_gbs"],
+                          "note": "hot: copy 0 every step (caches warm); stream_read: torch.sum over 1 GiB (fp64 view)"},
               "code_id": args.code, "parity_max_rel_err": parity_spot_check(args.workload, args.code)}
     if args.workload not in (5, 7):
         config.update({"tensors": {k: list(v) for k, v in wl.tensors.items()}, "batch": wl.batch})

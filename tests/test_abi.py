@@ -191,3 +191,15 @@ def test_moe_block_argument_validation():
     assert L.trellis_moe_block(*args, A16, need - 1, None) == -5
     assert L.trellis_moe_block(gu, A16, 4, dn, A16, 2, 0, A16, 2, A16, A16, A16, need, None) == -1
     assert L.trellis_moe_block(gu, A16, 4, dn, A16, 2, A16, A16, 0, A16, A16, A16, need, None) == -8
+
+
+def test_trellis_linear_dispatch():
+    """Row counts map to the entry points the dense-linear wrapper documents."""
+    from trellis_coded_gemv_amd.binding import TrellisLinear
+    assert TrellisLinear.path_for_rows(1) == "gemv"
+    assert TrellisLinear.path_for_rows(2) == "small" and TrellisLinear.path_for_rows(64) == "small"
+    assert TrellisLinear.path_for_rows(65) == "small_chunked" and TrellisLinear.path_for_rows(191) == "small_chunked"
+    assert TrellisLinear.path_for_rows(192) == "prefill" and TrellisLinear.path_for_rows(4096) == "prefill"
+    assert TrellisLinear.path_for_rows(100, prefill_min_rows=65) == "prefill"
+    with pytest.raises(ValueError):
+        TrellisLinear.path_for_rows(0)

@@ -278,7 +278,7 @@ def prefill_workspace(layer: DeviceLayer, M: int, device="cuda"):
 
 
 def trellis_gemm_prefill(layer: DeviceLayer, X, Y=None, ws=None, stream=None):
-    """Y [M, m] fp32 = W X[r] for every row of X (fp16 bits, int16 [M, n]); decode once + dense GEMM."""
+    """Y [M, m] fp32 = W X[r] for every row of fp16 X [M, n] (row stride X.stride(0)); decode once + dense GEMM."""
     torch = _torch()
     M = int(X.shape[0])
     if Y is None:
@@ -314,3 +314,69 @@ def trellis_moe_block(gate_up: "LayerTable", down: "LayerTable", sel, weights, x
                                    len(down), _ptr(sel), _ptr(weights), top_k, _ptr(x), _ptr(y), _ptr(ws),
                                    ws.numel(), _stream(stream)), "trellis_moe_block")
     return y
+
+
+class TrellisLinear:
+    """A trellis-coded linear layer used like a dense one: y = W x over the last axis.
+
+    `forward(x)` takes fp16 activations [..., n] on the device and returns fp32 [..., m]. It
+    picks the entry point by the number of rows R (the product of the leading axes), as the
+    pages' drop-in linear does for its batch sizes ("Trellis Quantization" lecture, Part
+    eleven: small batches decode per call, prefill decodes once):
+      R == 1                 -> trellis_gemv
+      R <= 64                -> trellis_gemm_small
+      R <  prefill_min_rows  -> trellis_gemm_small on row chunks of 64
+      otherwise              -> trellis_gemm_prefill (decode once, dense GEMM)
+    The default threshold (192 rows) sits past the measured crossover of the last two on
+    the 8192 -> 28672 gate shape. Workspaces are allocated on first use of each path and kept
+    (the prefill one grows with the largest row count seen); calls are ordered on one stream.
+    """
+
+    SMALL_MAX_ROWS = 64
+
+    def __init__(self, layer: DeviceLayer, prefill_min_rows: int = 192):
+        self.layer = layer
+        self.prefill_min_rows = int(prefill_min_rows)
+        self._ws = None
+        self._prefill_ws, self._prefill_rows = None, 0
+
+    @classmethod
+    def path_for_rows(cls, rows: int, prefill_min_rows: int = 192) -> str:
+        if rows < 1:
+            raise ValueError("no rows")
+        if rows == 1:
+            return "gemv"
+        if rows <= cls.SMALL_MAX_ROWS:
+            return "small"
+        return "small_chunked" if rows < prefill_min_rows else "prefill"
+
+    def _layer_ws(self, device):
+        if self._ws is None:   # one buffer for every row count up to 64 (the split count varies with it)
+            size = max(workspace_size(self.layer, M) for M in range(1, self.SMALL_MAX_ROWS + 1))
+            self._ws = _torch().zeros(size, dtype=_torch().uint8, device=device)
+        return self._ws
+
+    def forward(self, x, stream=None):
+        torch = _torch()
+        n, m = self.layer.n, self.layer.m
+        if x.dtype != torch.float16 or x.shape[-1] != n:
+            raise ValueError(f"expected float16 activations [..., {n}], got {tuple(x.shape)} {x.dtype}")
+        lead = tuple(x.shape[:-1])
+        X = x.reshape(-1, n).contiguous()
+        rows = X.shape[0]
+        path = self.path_for_rows(rows, self.prefill_min_rows)
+        Y = torch.empty(rows, m, dtype=torch.float32, device=x.device)
+        if path == "gemv":
+            trellis_gemv(self.layer, X[0], Y[0], self._layer_ws(x.device), stream)
+        elif path == "prefill":
+            if rows > self._prefill_rows:
+                self._prefill_ws, self._prefill_rows = prefill_workspace(self.layer, rows, x.device), rows
+            trellis_gemm_prefill(self.layer, X, Y, self._prefill_ws, stream)
+        else:
+            ws = self._layer_ws(x.device)
+            for r0 in range(0, rows, self.SMALL_MAX_ROWS):
+                r1 = min(rows, r0 + self.SMALL_MAX_ROWS)
+                trellis_gemm_small(self.layer, X[r0:r1], Y[r0:r1], ws, stream)
+        return Y.reshape(lead + (m,))
+
+    __call__ = forward
