@@ -155,7 +155,7 @@ int32_t trellis_gemm_small(const tg_layer *layer, int32_t M,
  * fp32 accumulation and output) and the output transform in place on Y. This
  * path always multiplies the fp16-rounded weights (TG_FLAG_ROUND_WEIGHTS has no
  * further effect here).
- *   X, ldx, Y, ldy : as for trellis_gemm_small (ldy < 2^31).
+ *   X, ldx, Y, ldy : as for trellis_gemm_small (ldy < 2^31); m*n <= 2^38.
  *   ws : device workspace of ws_bytes >= tg_prefill_workspace_size(layer, M):
  *        m*n*2 bytes of decoded weights plus M*n*2 bytes of transformed inputs
  *        (no zero-fill needed).
@@ -198,7 +198,8 @@ int32_t rht_apply(int32_t n, int32_t rows, const uint16_t *in, float *out,
  *   ws        : device workspace, ws_bytes >= tg_grouped_workspace_size(...).
  * Every layer's n must fit the input stride (n <= x_stride when x_stride != 0)
  * and m <= y_stride. Indices in d_sel outside [0, n_layers) make the affected
- * selection write nothing.
+ * selection write nothing. n_sel * (max m / 128) * (max n / 128) must stay
+ * below 2^31 (TG_ERR_SHAPE otherwise).
  */
 int32_t trellis_gemv_grouped(const tg_layer *layers, const tg_layer *d_layers, int32_t n_layers,
                              const int32_t *d_sel, int32_t n_sel,
@@ -245,7 +246,7 @@ size_t tg_moe_workspace_size(const tg_layer *gate_up, int32_t n_gate_up,
  * Decode the whole layer to fp16 weights (test / export hook): w_out[o*n + i]
  * = W^[o, i] as fp16 patterns, bit-exact with the code's definition. Only
  * codes, k_bits, code_id and shape are used; m, n need only be positive
- * multiples of 16.
+ * multiples of 16, and m*n <= 2^38 (TG_ERR_SHAPE beyond: 512 GiB of output).
  *   w_out : device, m*n uint16.
  */
 int32_t trellis_decode(const tg_layer *layer, uint16_t *w_out, void *stream);

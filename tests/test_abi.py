@@ -203,3 +203,14 @@ def test_trellis_linear_dispatch():
     assert TrellisLinear.path_for_rows(100, prefill_min_rows=65) == "prefill"
     with pytest.raises(ValueError):
         TrellisLinear.path_for_rows(0)
+
+
+def test_huge_shapes_rejected_before_launch():
+    """Dense-output entry points cap the weight count (2^38); the grouped grid must fit 31 bits."""
+    L = tg.lib()
+    big = _layer(m=1 << 22, n=1 << 22)
+    assert L.trellis_decode(ctypes.byref(big), A16, None) == -2
+    assert L.tg_prefill_workspace_size(ctypes.byref(big), 16) == 0
+    assert L.trellis_gemm_prefill(ctypes.byref(big), 16, A16, 1 << 22, A16, 1 << 22, A16, 1 << 40, None) == -2
+    table = (tg.TgLayer * 1)(_layer(m=1 << 22, n=1 << 22))
+    assert L.tg_grouped_workspace_size(table, 1, 65536) == 0

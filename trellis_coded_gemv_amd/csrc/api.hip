@@ -24,6 +24,11 @@ static_assert(sizeof(tg_layer) == sizeof(LayerDev), "device layer table mirrors 
 static_assert(offsetof(tg_layer, codes) == offsetof(LayerDev, codes), "device layer table mirrors tg_layer");
 static_assert(offsetof(tg_layer, sign_out) == offsetof(LayerDev, sign_out), "device layer table mirrors tg_layer");
 
+// Entry points that write a dense fp16 copy of the weights (decode, prefill)
+// take at most 2^38 of them: 512 GiB, more than any device holds, and the
+// bound keeps their grids within 32 bits.
+constexpr int64_t kMaxDenseWeights = (int64_t)1 << 38;
+
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
@@ -151,6 +156,7 @@ int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel
     if (layers[i].n > max_n) max_n = layers[i].n;
   }
   const int max_ob = max_m / kBlock, max_nb = max_n / kBlock;
+  if ((int64_t)n_sel * max_ob * max_nb > INT32_MAX) return TG_ERR_SHAPE;   // the grid (splits <= max_nb) fits 31 bits
   int s = env_int("TG_SPLITK");
   if (s <= 0) s = split_for_target(max_nb, (256 + n_sel * max_ob / 2) / (n_sel * max_ob));
   const int min_s = (max_nb + kMaxChunkBlocks - 1) / kMaxChunkBlocks;
@@ -303,6 +309,7 @@ TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) 
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || L->m % kTile != 0 || L->n % kTile != 0 || L->m > (1 << 22) || L->n > (1 << 22))
     return TG_ERR_SHAPE;
+  if ((int64_t)L->m * L->n > kMaxDenseWeights) return TG_ERR_SHAPE;
   if (!L->codes || !w_out) return TG_ERR_NULL;
   if (misaligned(L->codes, 4) || misaligned(w_out, 2)) return TG_ERR_ALIGN;
   return launch_status(launch_decode(L->codes, w_out, L->m, L->n, L->k_bits, L->code_id, (hipStream_t)stream));
@@ -380,6 +387,7 @@ PrefillWs prefill_ws(int m, int n, int M) {
 
 TG_API size_t tg_prefill_workspace_size(const tg_layer* L, int32_t M) {
   if (check_layer(L) != TG_OK || M < 1 || M > 65535) return 0;
+  if ((int64_t)L->m * L->n > kMaxDenseWeights) return 0;
   return prefill_ws(L->m, L->n, M).total;
 }
 
@@ -387,7 +395,7 @@ TG_API int32_t trellis_gemm_prefill(const tg_layer* L, int32_t M, const uint16_t
                                     int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_layer(L);
   if (st != TG_OK) return st;
-  if (M < 1 || M > 65535) return TG_ERR_SHAPE;
+  if (M < 1 || M > 65535 || (int64_t)L->m * L->n > kMaxDenseWeights) return TG_ERR_SHAPE;
   if (!X || !Y) return TG_ERR_NULL;
   if (ldx < L->n || ldy < L->m || ldy > 0x7fffffff) return TG_ERR_ARG;
   if (misaligned(X, 2) || misaligned(Y, 4)) return TG_ERR_ALIGN;
