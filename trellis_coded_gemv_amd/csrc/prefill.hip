@@ -15,11 +15,14 @@
 
 namespace tg {
 
-// One wave per (input row, 128-block): the input-side transform as fp16.
-__global__ __launch_bounds__(64) void rows_rht_kernel(const uint16_t* __restrict__ X, int64_t ldx,
-                                                      const uint32_t* __restrict__ sign_in,
-                                                      uint16_t* __restrict__ Xt, int n) {
-  const int lane = threadIdx.x, row = blockIdx.y, base = blockIdx.x * kBlock;
+// Four waves per workgroup, one per (input row, 128-block): the input-side
+// transform as fp16. A wave past the row's last block leaves (no barriers).
+__global__ __launch_bounds__(256) void rows_rht_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                       const uint32_t* __restrict__ sign_in,
+                                                       uint16_t* __restrict__ Xt, int n) {
+  const int lane = threadIdx.x & 63, row = blockIdx.y, blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= (n >> 7)) return;
+  const int base = blk * kBlock;
   const XBlock xb = load_x_block(X + (size_t)row * ldx, sign_in, base, lane);
   const uint16_t b0 = xb.b0 ^ (uint16_t)(((xb.s0 >> ((base + lane) & 31)) & 1u) << 15);
   const uint16_t b1 = xb.b1 ^ (uint16_t)(((xb.s1 >> ((base + lane + 64) & 31)) & 1u) << 15);
@@ -81,18 +84,21 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
   }
 }
 
-// One wave per (output row, 128-block): scale, output transform and signs in place.
-__global__ __launch_bounds__(64) void rows_out_kernel(float* __restrict__ Y, int64_t ldy,
-                                                      const uint16_t* __restrict__ scales,
-                                                      const uint32_t* __restrict__ sign_out) {
-  const int lane = threadIdx.x, base = blockIdx.x * kBlock;
+// Four waves per workgroup, one per (output row, 128-block): scale, output
+// transform and signs in place.
+__global__ __launch_bounds__(256) void rows_out_kernel(float* __restrict__ Y, int64_t ldy,
+                                                       const uint16_t* __restrict__ scales,
+                                                       const uint32_t* __restrict__ sign_out, int m) {
+  const int lane = threadIdx.x & 63, blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= (m >> 7)) return;
+  const int base = blk * kBlock;
   float* y = Y + (size_t)blockIdx.y * ldy;
   rht_out_block(y[base + lane], y[base + lane + 64], scales, sign_out, y, base, lane);
 }
 
 hipError_t launch_prefill_rht(const uint16_t* X, int64_t ldx, const uint32_t* sign_in, uint16_t* Xt, int n, int M,
                               hipStream_t s) {
-  hipLaunchKernelGGL(rows_rht_kernel, dim3(n / kBlock, M), dim3(64), 0, s, X, ldx, sign_in, Xt, n);
+  hipLaunchKernelGGL(rows_rht_kernel, dim3((n / kBlock + 3) / 4, M), dim3(256), 0, s, X, ldx, sign_in, Xt, n);
   return hipGetLastError();
 }
 
@@ -117,7 +123,7 @@ hipError_t launch_prefill_decode(const uint32_t* codes, uint16_t* W, int m, int 
 
 hipError_t launch_prefill_out(float* Y, int64_t ldy, const uint16_t* scales, const uint32_t* sign_out, int m, int M,
                               hipStream_t s) {
-  hipLaunchKernelGGL(rows_out_kernel, dim3(m / kBlock, M), dim3(64), 0, s, Y, ldy, scales, sign_out);
+  hipLaunchKernelGGL(rows_out_kernel, dim3((m / kBlock + 3) / 4, M), dim3(256), 0, s, Y, ldy, scales, sign_out, m);
   return hipGetLastError();
 }
 
