@@ -470,16 +470,36 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
 }
 
 // Router-weighted sum of the selected experts' outputs, in selection order;
-// selections outside [0, n_experts) contribute nothing.
+// selections outside [0, n_experts) contribute nothing. The selection and
+// weights are staged in LDS once, and each thread issues the loads of eight
+// experts before it adds them (a load per expert behind its own validity test
+// would wait for each in turn).
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ Y2, int64_t y2_stride,
                                                           const int32_t* __restrict__ sel, const float* __restrict__ w,
                                                           int top_k, int n_experts, int hidden, float* __restrict__ y) {
+  __shared__ float wl[256];
+  __shared__ int32_t valid[256];
+  for (int e = threadIdx.x; e < top_k; e += 256) {
+    const int32_t s = sel[e];
+    valid[e] = s >= 0 && s < n_experts;
+    wl[e] = w[e];
+  }
+  __syncthreads();
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= hidden) return;
   float acc = 0.f;
-  for (int e = 0; e < top_k; ++e) {
-    const int s = sel[e];
-    if (s >= 0 && s < n_experts) acc += w[e] * Y2[(size_t)e * y2_stride + o];
+  for (int e0 = 0; e0 < top_k; e0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + j;
+      v[j] = (e < top_k && valid[e]) ? Y2[(size_t)e * y2_stride + o] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + j;
+      if (e < top_k && valid[e]) acc += wl[e] * v[j];
+    }
   }
   y[o] = acc;
 }

@@ -218,13 +218,21 @@ __device__ __forceinline__ XGated16 load_gated16(const float* __restrict__ hg, c
   return r;
 }
 
-// x = fp16(silu(g) * u), silu(v) = v / (1 + exp(-v)), packed as the fp16 input words.
+// x = fp16(silu(g) * u), silu(v) = v / (1 + exp(-v)), packed as the fp16 input
+// words. exp(-v) = 2^(-v log2 e) and the reciprocal use the hardware's
+// v_exp_f32 and v_rcp_f32 (relative error ~2^-22, far below the 2^-11 of the
+// fp16 rounding that follows); exp overflows to +inf for v < -88, and
+// v * rcp(inf) = -0 as silu's limit demands.
+__device__ __forceinline__ float silu_fast(float v) {
+  return v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
+}
+
 __device__ __forceinline__ X16 gated_to_x16(const XGated16& r) {
   uint32_t w[8];
 #pragma unroll
   for (int j = 0; j < 16; j += 2) {
-    const float h0 = r.g[j] / (1.f + expf(-r.g[j])) * r.u[j];
-    const float h1 = r.g[j + 1] / (1.f + expf(-r.g[j + 1])) * r.u[j + 1];
+    const float h0 = silu_fast(r.g[j]) * r.u[j];
+    const float h1 = silu_fast(r.g[j + 1]) * r.u[j + 1];
     w[j >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h0) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)h1) << 16);
   }
