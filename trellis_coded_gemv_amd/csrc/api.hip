@@ -158,7 +158,12 @@ int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel
   const int max_ob = max_m / kBlock, max_nb = max_n / kBlock;
   if ((int64_t)n_sel * max_ob * max_nb > INT32_MAX) return TG_ERR_SHAPE;   // the grid (splits <= max_nb) fits 31 bits
   int s = env_int("TG_SPLITK");
-  if (s <= 0) s = split_for_target(max_nb, (256 + n_sel * max_ob / 2) / (n_sel * max_ob));
+  if (s <= 0) {
+    // at most one workgroup per CU: a second round of a few workgroups costs a whole chunk's time
+    const int per = n_sel * max_ob;
+    s = split_for_target(max_nb, per >= 256 ? 1 : 256 / per);
+    while (s > 1 && (int64_t)s * per > 256) --s;
+  }
   const int min_s = (max_nb + kMaxChunkBlocks - 1) / kMaxChunkBlocks;
   if (s < min_s) s = min_s;
   if (s > max_nb) s = max_nb;
