@@ -43,6 +43,10 @@
 #ifndef TG_MFMA_GROUP
 #define TG_MFMA_GROUP 4
 #endif
+// Steps of code words and x~ in flight per wave.
+#ifndef TG_MFMA_PF
+#define TG_MFMA_PF 2
+#endif
 // A workgroup has 16 waves when the activations fit one 16-row MFMA block and
 // every wave still gets at least this many steps (more waves hide more
 // latency; short loops do not amortise the start-up and the deeper reduction,
@@ -53,20 +57,23 @@
 
 namespace tg {
 
-// x~ = H diag(s_in) x / sqrt(128) for every row (rows >= M are zero), stored as
-// fp16 pairs: mode 0 (x~, x~) per column, row stride n words; mode 1 the rotated
-// column pairs (x~0 - x~1, x~0 + x~1) and mode 2 the plain pairs (x~0, x~1),
-// row stride n/2 words.
+// x~ = H diag(s_in) x / sqrt(128) for every row (rows >= M are zero). Mode 0:
+// plain fp16 in tile-column order, [n/16][mpad rows][16 columns], so that the
+// 16 rows x 16 columns one MFMA step reads are 512 contiguous bytes. Modes 1
+// and 2: fp16 pairs, the rotated column pairs (x~0 - x~1, x~0 + x~1) or the
+// plain pairs (x~0, x~1), row stride n/2 words.
 __global__ __launch_bounds__(64) void xt_prep_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                       const uint32_t* __restrict__ sign_in, uint32_t* __restrict__ xt,
                                                       int n, int M, int mode) {
   const int lane = threadIdx.x, row = blockIdx.y;
   if (mode == 0) {
-    const size_t ob = (size_t)row * n + (size_t)blockIdx.x * kBlock;
     uint32_t d0 = 0u, d1 = 0u;
     if (row < M) rht_in_block_dup(X + (size_t)row * ldx, sign_in, blockIdx.x * kBlock, lane, d0, d1);
-    xt[ob + lane] = d0;
-    xt[ob + lane + 64] = d1;
+    uint16_t* xh = reinterpret_cast<uint16_t*>(xt);
+    const size_t mpad = gridDim.y;
+    const int c0 = blockIdx.x * kBlock + lane, c1 = c0 + 64;
+    xh[((size_t)(c0 >> 4) * mpad + row) * 16 + (c0 & 15)] = (uint16_t)d0;
+    xh[((size_t)(c1 >> 4) * mpad + row) * 16 + (c1 & 15)] = (uint16_t)d1;
   } else {
     uint32_t d = 0u;
     if (row < M)
@@ -146,10 +153,14 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
   const int tl = lane >> 3;                                  // tile row this lane loads
   const uint32_t* __restrict__ cptr =
       a.codes + ((size_t)(ob * 8 + tl) * n16 + (size_t)col0 * SPAN) * WPT + (lane & 7) * LW;
-  const uint32_t* __restrict__ xptr = a.xt + (size_t)jrow * xrow + 4 * g + (size_t)col0 * 16;
+  // x~ of this lane: row jrow (+16 per row block), input columns 4g..4g+3 of the step
+  const uint32_t* __restrict__ xptr = CODE == 0 ? a.xt + ((size_t)col0 * a.mpad + jrow) * 8 + 2 * g
+                                                : a.xt + (size_t)jrow * xrow + 4 * g + (size_t)col0 * 16;
+  const size_t xmb = CODE == 0 ? 128 : 16 * xrow;   // words between 16-row blocks
   const uint32_t* __restrict__ cfirst = cptr;
   const uint32_t* __restrict__ xfirst = xptr;
-  const size_t cadv = (size_t)cstep * SPAN * WPT, xadv = (size_t)cstep * 16;
+  const size_t cadv = (size_t)cstep * SPAN * WPT;
+  const size_t xadv = CODE == 0 ? (size_t)cstep * a.mpad * 8 : (size_t)cstep * 16;
 
   // Prefetch ring; out-of-range steps re-read the first step (valid addresses,
   // and every path issues the same loads so the waits stay exact).
@@ -161,7 +172,14 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
     load_column<LW>(ok ? cptr : cfirst, dst);
     const uint32_t* xq = ok ? xptr : xfirst;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) xd[mb] = *reinterpret_cast<const u32x4*>(xq + (size_t)(16 * mb) * xrow);
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (CODE == 0) {   // four fp16 values; paired up at use
+        const u32x2 v = *reinterpret_cast<const u32x2*>(xq + (size_t)mb * xmb);
+        xd[mb] = u32x4{v.x, v.y, 0u, 0u};
+      } else {
+        xd[mb] = *reinterpret_cast<const u32x4*>(xq + (size_t)mb * xmb);
+      }
+    }
     cptr += cadv;
     xptr += xadv;
     ++issued;
@@ -174,6 +192,18 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       if (i0 + p < ncol) {
+        // A operands: code 0 pairs each x~ with itself, (x~, x~) per column
+        u32x4 av[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          if constexpr (CODE == 0) {
+            const uint32_t d0 = xa[p][mb].x, d1 = xa[p][mb].y;
+            av[mb] = u32x4{__builtin_amdgcn_perm(d0, d0, 0x01000100u), __builtin_amdgcn_perm(d0, d0, 0x03020302u),
+                           __builtin_amdgcn_perm(d1, d1, 0x01000100u), __builtin_amdgcn_perm(d1, d1, 0x03020302u)};
+          } else {
+            av[mb] = xa[p][mb];
+          }
+        }
         // stage the step's words, read back the words of all 8 tile rows,
         // decode all 8 B operands, then issue the MFMAs back to back
         stage_words<LW>(slice + lane * LW, cw[p]);   // lane l's LW words sit at word l*LW
@@ -206,7 +236,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
           const half8_t bop = __builtin_bit_cast(half8_t, u32x4{bw[tt][0], bw[tt][1], bw[tt][2], bw[tt][3]});
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            acc[t0 + tt][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xa[p][mb]), bop,
+            acc[t0 + tt][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[mb]), bop,
                                                                       acc[t0 + tt][mb], 0, 0, 0);
         }
         }
@@ -219,7 +249,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
 template <int K, int CODE, bool ROUND, int MB, int MW>
 __global__ __launch_bounds__(64 * MW) void gemm_small_kernel(GemmArgs a) {
   extern __shared__ uint32_t lds[];
-  constexpr int PF = 2;
+  constexpr int PF = TG_MFMA_PF;
   using G = MfmaGeom<K, CODE>;
   constexpr int SLICE = 8 * G::SPAN * G::WPT;   // staged words per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
