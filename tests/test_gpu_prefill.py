@@ -87,3 +87,24 @@ def test_prefill_matches_mfma_path_with_rounded_weights():
     torch.cuda.synchronize()
     for r in range(16):
         assert rel_err(Yp[r], Ys.cpu().numpy()[r]) <= 1e-5, r
+
+
+@pytest.mark.parametrize("m,n,M", [(384, 1152, 129), (28672, 8192, 512)])
+def test_prefill_deterministic_and_strided(m, n, M):
+    """Two calls give bit-identical outputs (the library GEMM runs with atomics off), and an output
+    row stride wider than m leaves the gap columns untouched."""
+    import torch
+    dev = device()
+    arr = inputs.make_layer(m, n, 2, 5300 + M)
+    X = tg.fp16_tensor(inputs.make_x(n, 5300 + M, rows=M), dev)
+    L = tg.DeviceLayer(arr, dev)
+    say("prefill determinism", m, n, M)
+    Y1 = tg.trellis_gemm_prefill(L, X).clone()
+    Y2 = tg.trellis_gemm_prefill(L, X).clone()
+    wide = torch.full((M, m + 128), 7.0, dtype=torch.float32, device=dev)
+    tg.trellis_gemm_prefill(L, X, Y=wide[:, :m])
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    assert torch.isfinite(Y1).all()
+    assert torch.equal(wide[:, m:], torch.full_like(wide[:, m:], 7.0))
+    assert rel_err(wide[:, :m].cpu().numpy(), Y1.cpu().numpy()) <= REL_TOL
