@@ -46,7 +46,10 @@
  *   - Pointers named d_* or documented "device" are device pointers (hipMalloc
  *     or any allocator of device memory); the tg_layer struct itself is read on
  *     the host. The caller owns every buffer; the library never allocates,
- *     frees, or keeps a pointer after the call returns.
+ *     frees, or keeps a pointer after the call returns. One exception: the
+ *     prefill path creates one rocBLAS handle per device on its first call
+ *     there (kept until the process ends; rocBLAS manages that handle's own
+ *     device memory).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously; the library never synchronises.
  *   - Every argument is validated on the host before anything is enqueued; on
@@ -56,6 +59,11 @@
  *   - Results are bitwise deterministic for identical inputs and launch
  *     configuration.
  *   - Calls that share a workspace must not run concurrently.
+ *   - Environment (tuning aids, read on every call, including by the
+ *     workspace-size queries): TG_SPLITK=S (S > 0) forces S input chunks on
+ *     the batch-1 and grouped paths, TG_SPLITK_MFMA=S on the small-batch
+ *     path. A workspace sized under one setting can be too small under
+ *     another; the call then returns TG_ERR_WORKSPACE.
  */
 #ifndef TRELLIS_GEMV_H
 #define TRELLIS_GEMV_H
