@@ -524,7 +524,7 @@ def main(argv=None):
                     help="after timing, write (fill) and read (sum) this many MiB (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU path.",
               file=sys.stderr)
         return 2
 

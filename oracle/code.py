@@ -8,7 +8,7 @@ pins the exponent, giving two half-precision values with random signs and
 bounded magnitude; (3) add the two halves with one half-precision add.
 Step (2) is the mantissa-splice trick of [TQ] Part three.
 
-The pages print no constants for this code. Reading (listed in the design doc):
+The pages print no constants for this code. Reading where they leave it open:
 the multiplier is the blog's 0x9E3779B9 ([DD] Section 3 code) cut to its top
 24 bits, 0x9E3779, so the multiply-add is one full-rate instruction on the
 target, as [TQ] Part nine requires of step (1); the addend is the blog's
@@ -74,7 +74,7 @@ def table() -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# code_id 1, the pair code (this library's V=2 variant; readings in the design doc):
+# code_id 1, the pair code (this library's V=2 variant of the pages' vector trellis, a reading):
 # one state per two consecutive weights ([DD] Section 3: b*V bits per
 # V-dimensional step; its decode snippet yields a pair of halves per state).
 # The state goes through the same multiply-add and mask/XOR; the halves a, b

@@ -9,7 +9,7 @@ eleven; [FG] "out_scales always"):
     y~ = diag(g) W^ x~                          (g: per-output fp16 scale)
     y  = diag(s_out) blockdiag(H_128) y~
 
-Reading (listed in the design doc): the per-output scale g acts in the rotated
+Reading where the pages leave it open: the per-output scale g acts in the rotated
 domain, on y~ before the output transform.
 
 Two routes are provided and pinned against each other: the factored route

@@ -6,7 +6,7 @@ signs stored as one bit per row / column, and the rotation is undone on the
 activations at run time. [TQ] Part eleven: EXL3 rotates blocks of 128 along
 each axis rather than whole rows and columns.
 
-Readings (listed in DESIGN.md): Sylvester (natural) ordering,
+Readings where the pages leave it open: Sylvester (natural) ordering,
 H[i, j] = (-1)^popcount(i AND j) / sqrt(128); sign bit i is bit i mod 32 of
 word i // 32, set meaning -1. The two runtime equations of [DD] Section 2 are
 not inverse to each other as printed; the oracle uses

@@ -5,7 +5,7 @@
 for the token's selected experts e_i with router weights w_i. The pages name
 mixture-of-experts models and expert parallelism ([DD] Section 4; [TQ] Part
 eleven: per-tensor bit widths, experts at their own K) but not the block's
-arithmetic. Readings (listed in the design doc): each expert is a gated MLP with the
+arithmetic. Readings where the pages leave it open: each expert is a gated MLP with the
 SiLU gate, silu(v) = v / (1 + exp(-v)); the down projection's input is the
 product rounded once to binary16 (every GEMV of this library takes fp16
 inputs); the router weights are given per token and combined in selection

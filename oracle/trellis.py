@@ -14,7 +14,7 @@ V-dimensional steps ([DD] Section 3, "b*V bits per V-dimensional sub-vector"):
 with V=2 a sequence of 256 weights is 128 steps of two weights; each step
 shifts 2K bits and the state of step tau starts at stream bit 2K*tau.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * the first stream bit of a window is the state's most significant bit;
   * stream bit p of a tile is bit (31 - p mod 32) of 32-bit word p // 32
     (MSB-first inside little-endian words); a tile is 8*K words;

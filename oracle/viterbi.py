@@ -16,7 +16,7 @@ Followed passages:
     bits. [DD] Section 3 / [TQ] Part eight give the trellis itself: a step
     shifts b = V*K new bits into an L = 16 bit window.
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave it open:
   * "read off the bits in the middle" = the pass-one path's state at rotated
     step T/2, which is the window of original step 0 (its 16 bits become S_0);
   * "constrained to start and end with those bits": the second pass starts in
