@@ -121,7 +121,10 @@ const char *tg_status_str(int32_t status);
  * tickets and the small-batch arrival counters, each sized for the largest
  * layer), then scratch (split-K partials, the small-batch input transform).
  * It must be zero-filled before its first use. Every completed call leaves the
- * counters at zero; the scratch may hold anything between calls. One buffer,
+ * small-batch counters at zero and each batch-1 ticket counter on a call
+ * boundary (a multiple of 65536: the counter advances by 65536 per call, and
+ * its high 16 bits number the calls and tag the split-K slots, so slots are
+ * never cleared); the scratch may hold anything between calls. One buffer,
  * as large as each layer needs, can therefore serve any sequence of layers and
  * of both entry points on one stream. 256-byte alignment is required.
  */
@@ -136,8 +139,8 @@ size_t tg_workspace_size(const tg_layer *layer, int32_t M);
  * With split-K, the workgroups of an output block hand their partial sums to
  * one of them through the workspace; its wait for them is bounded (about a
  * second) and, should the device ever stall a workgroup that long, the
- * affected outputs are written as NaN and the workspace must be zero-filled
- * again before reuse.
+ * affected outputs are written as NaN (the workspace stays usable: a late
+ * partial carries its own call's tag).
  */
 int32_t trellis_gemv(const tg_layer *layer, const uint16_t *x, float *y,
                      void *ws, size_t ws_bytes, void *stream);
@@ -203,7 +206,10 @@ int32_t rht_apply(int32_t n, int32_t rows, const uint16_t *in, float *out,
  *   X         : device fp16 inputs; selection e reads X + e*x_stride
  *               (x_stride == 0: all selections share one input vector).
  *   Y         : device fp32 outputs; selection e writes Y + e*y_stride.
- *   ws        : device workspace, ws_bytes >= tg_grouped_workspace_size(...).
+ *   ws        : device workspace, ws_bytes >= tg_grouped_workspace_size(...),
+ *               zero-filled before its first use; every call leaves its ticket
+ *               counters on a call boundary (as for trellis_gemv), and calls
+ *               that share it must be ordered (one stream).
  * Every layer's n must fit the input stride (n <= x_stride when x_stride != 0)
  * and m <= y_stride. Indices in d_sel outside [0, n_layers) make the affected
  * selection write nothing. n_sel * (max m / 128) * (max n / 128) must stay
@@ -235,7 +241,7 @@ size_t tg_grouped_workspace_size(const tg_layer *layers, int32_t n_layers, int32
  *   x                   : device, hidden fp16; y : device, hidden fp32.
  *   ws                  : device workspace, ws_bytes >= tg_moe_workspace_size(...),
  *                         256-byte aligned and zero-filled before its first use. Every
- *                         call leaves its arrival counters at zero again; the rest holds
+ *                         call leaves its ticket counters on a call boundary; the rest holds
  *                         the call's intermediate rows. Calls that share a workspace
  *                         must be ordered (one stream).
  * All layers must share TG_FLAG_* flags. Errors: a negative tg_status (shape, table,

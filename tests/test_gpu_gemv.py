@@ -95,7 +95,8 @@ def test_gemv_deterministic_and_workspace_reuse():
     y2 = tg.trellis_gemv(L, xt, ws=ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
-    assert (ws[: 1024 // 128 * 4] == 0).all()         # arrival counters are left at zero
+    tickets = ws[: 1024 // 128 * 4].view(torch.int32)
+    assert ((tickets & 0xFFFF) == 0).all()              # ticket counters end each call at a call boundary
     rows = sample_rows(1024)
     assert rel_err(y1.cpu().numpy()[rows], ogemv.gemv_rows(arr, x, rows)) <= REL_TOL
 
@@ -136,10 +137,34 @@ def test_gemv_many_splits(splits, monkeypatch):
     assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
 
 
+def test_gemv_call_tags_wrap():
+    """70,000 calls on one workspace: the 16-bit call number in the ticket counters and slot tags
+    wraps (at 65,536 calls) without a stale partial ever being taken for a current one."""
+    import torch
+    dev = device()
+    arr = inputs.make_layer(256, 4096, 2, 94)   # 2 blocks x 8 splits: every call hands over
+    L = tg.DeviceLayer(arr, dev)
+    x = tg.fp16_tensor(inputs.make_x(4096, 94), dev)
+    ws = tg.workspace(L, 1, dev)
+    y = torch.empty(256, dtype=torch.float32, device=dev)
+    say("tag wrap: 70000 calls")
+    ref = tg.trellis_gemv(L, x, ws=ws).clone()
+    bad = torch.zeros((), dtype=torch.int32, device=dev)
+    for i in range(70_000):
+        tg.trellis_gemv(L, x, y, ws=ws)
+        if i % 4096 == 4095 or i >= 65_530:
+            bad += (~torch.eq(y, ref)).sum()
+    torch.cuda.synchronize()
+    assert int(bad) == 0
+    tickets = ws[: 2 * 4].view(torch.int32)
+    assert ((tickets & 0xFFFF) == 0).all()
+
+
 def test_workspace_shared_by_layers_and_paths():
     """One buffer serves two layers on both paths, its scratch first filled with ones (every split-K
-    slot then looks full): each result equals the one computed on a fresh workspace, bit for bit,
-    and the counter areas are zero after every call."""
+    slot then carries a tag no call uses): each result equals the one computed on a fresh workspace,
+    bit for bit; after every call the batch-1 ticket counters sit on a call boundary (low 16 bits
+    zero) and the small-batch arrival counters are zero."""
     dev = device()
     import torch
     a_arr = inputs.make_layer(1024, 4096, 3, 90)
@@ -162,6 +187,8 @@ def test_workspace_shared_by_layers_and_paths():
         y = call()
         torch.cuda.synchronize()
         assert torch.equal(y, ref[name]), name
-        assert (ws[:counters] == 0).all(), name
+        tickets = ws[: counters // 2].view(torch.int32)
+        assert ((tickets & 0xFFFF) == 0).all(), name
+        assert (ws[counters // 2: counters] == 0).all(), name
     rows = sample_rows(512)
     assert rel_err(ref["vb"].cpu().numpy()[rows], ogemv.gemv_rows(b_arr, inputs.make_x(8192, 91), rows)) <= REL_TOL

@@ -171,11 +171,9 @@ __device__ __forceinline__ void read_xx(const uint32_t* xx_lds, int tile, uint32
 // waves per tile row that take interleaved 16-tile steps of the chunk.
 // GATED: the input is fp16(silu(a.hg) * a.hu) (the down projection of a gated
 // expert MLP) instead of the fp16 vector a.x.
-// TICKET selects the split-K handoff: the reducer chosen by a ticket taken
-// at the start, partials in self-describing slots (batch-1 path); or the
-// last-arriving workgroup reducing fp32 partials (grouped path, whose short
-// chunks do better with it).
-template <int K, int CODE, bool ROUND, int PF, int P, bool GATED = false, bool TICKET = true>
+// Split-K handoff: the reducer is chosen by a ticket taken once the input has
+// arrived, and the partials travel in call-tagged slots (tg_device.hpp).
+template <int K, int CODE, bool ROUND, int PF, int P, bool GATED = false>
 __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int split, uint32_t* lds) {
   constexpr int NW = 2 * K;
   constexpr int NX = CODE == 0 ? 16 : 8;   // input words per tile column
@@ -200,16 +198,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   float* red = ybuf + 128;                                       // [P-1][128]
   uint32_t* flag = lds + nsteps * 256 + 128 * P;
 
-  // Split-K by ticket: wave 0 empties this workgroup's slots before
-  // anything else. Vector memory operations retire in issue order, so the
-  // prologue's wait for the input below also means these stores have landed,
-  // before the ticket is taken: whatever the scratch held before, a slot the
-  // reducer reads is then either empty or holds this call's partial.
-  uint64_t* slots = a.slots + (size_t)ob * a.splits * kBlock;
-  if (TICKET && a.splits > 1 && wave == 0) {
-    clear_slot(slots + (size_t)split * kBlock + lane);
-    clear_slot(slots + (size_t)split * kBlock + lane + 64);
-  }
+  uint64_t* slots = a.slots + (size_t)ob * a.splits * kBlock;   // split-K by ticket: [split][128]
 
   // This lane's part of the input chunk (8 lanes per 128-block, 16 elements
   // per lane) is fetched before the code prefetch: loads complete in order,
@@ -269,7 +258,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
     __syncthreads();   // every wave has read its exchange values
     // Split-K ticket: after the input has arrived (and with it the slot
     // clears); the answer is needed only at the end.
-    if (TICKET && a.splits > 1 && threadIdx.x == 0) ticket = take_ticket(&a.counters[ob]);
+    if (a.splits > 1 && threadIdx.x == 0) ticket = take_ticket(&a.counters[ob]);
     if (active) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -328,64 +317,56 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
     return;
   }
 
-  // Split-K. Either way the reducer sums the splits in a fixed order (wave w
-  // takes splits w, w+WAVES, ..., then wave 0 adds the per-wave sums), so the
+  // Split-K. The reducer sums the splits in a fixed order (wave w takes
+  // splits w, w+WAVES, ..., then wave 0 adds the per-wave sums), so the
   // result does not depend on which workgroup reduced.
   float v0 = 0.f, v1 = 0.f;
-  if constexpr (TICKET) {
-    // The last ticket holder reduces, with its own partial from LDS; every
-    // other workgroup publishes its 128 partials and leaves.
-    if (threadIdx.x == 0) flag[0] = ticket == (uint32_t)a.splits - 1u ? 1u : 0u;
-    if (kp == 0 && lane < 16) ybuf[orow] = d;
-    __syncthreads();
-    if (flag[0] == 0u) {
-      if (kp == 0 && lane < 16) put_slot(slots + (size_t)split * kBlock + orow, d);
-      return;
+  // The call's last ticket holder reduces, with its own partial from LDS;
+  // every workgroup publishes its 128 partials (the reducer too, so that no
+  // slot is ever more than one call old), and all but the reducer leave.
+  if (threadIdx.x == 0) {
+    flag[0] = (ticket & (kTicketCall - 1u)) == (uint32_t)a.splits - 1u ? 1u : 0u;
+    flag[1] = slot_tag(ticket);
+  }
+  if (kp == 0 && lane < 16) ybuf[orow] = d;
+  __syncthreads();
+  const uint32_t tag = flag[1];
+  if (kp == 0 && lane < 16) put_slot(slots + (size_t)split * kBlock + orow, d, tag);
+  if (flag[0] == 0u) return;
+  constexpr int J = 4;   // splits per wave whose slots are read together
+  for (int t0 = 0; t0 < a.splits; t0 += WAVES * J) {
+    // Read this wave's slots of up to J splits at once; re-read the ones that
+    // do not hold this call's partial yet, together, until all do (bounded),
+    // then add in split order.
+    uint64_t s0[J], s1[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int t = t0 + wave + j * WAVES;
+      s0[j] = s1[j] = (uint64_t)tag << 32;   // splits outside the range, and this one's own, count as ready
+      if (t < a.splits && t != split) {
+        s0[j] = peek_slot(slots + (size_t)t * kBlock + lane);
+        s1[j] = peek_slot(slots + (size_t)t * kBlock + lane + 64);
+      }
     }
-    constexpr int J = 4;   // splits per wave whose slots are read together
-    for (int t0 = 0; t0 < a.splits; t0 += WAVES * J) {
-      // Read this wave's slots of up to J splits at once; re-read the empty
-      // ones together until all are full (bounded), then add in split order.
-      uint64_t s0[J], s1[J];
+    for (uint32_t it = 0; it < kSlotPolls; ++it) {
+      bool empty = false;
+#pragma unroll
+      for (int j = 0; j < J; ++j) empty |= !slot_ready(s0[j], tag) || !slot_ready(s1[j], tag);
+      if (!empty) break;
+      __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int t = t0 + wave + j * WAVES;
-        s0[j] = s1[j] = 1ull << 32;   // splits outside the range, and this one's own, count as full
-        if (t < a.splits && t != split) {
-          s0[j] = peek_slot(slots + (size_t)t * kBlock + lane);
-          s1[j] = peek_slot(slots + (size_t)t * kBlock + lane + 64);
-        }
-      }
-      for (uint32_t it = 0; it < kSlotPolls; ++it) {
-        bool empty = false;
-#pragma unroll
-        for (int j = 0; j < J; ++j) empty |= (s0[j] >> 32) == 0u || (s1[j] >> 32) == 0u;
-        if (!empty) break;
-        __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-          const int t = t0 + wave + j * WAVES;
-          if ((s0[j] >> 32) == 0u) s0[j] = peek_slot(slots + (size_t)t * kBlock + lane);
-          if ((s1[j] >> 32) == 0u) s1[j] = peek_slot(slots + (size_t)t * kBlock + lane + 64);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int t = t0 + wave + j * WAVES;
-        if (t >= a.splits) break;
-        v0 += t == split ? ybuf[lane] : slot_value(s0[j]);
-        v1 += t == split ? ybuf[lane + 64] : slot_value(s1[j]);
+        if (!slot_ready(s0[j], tag)) s0[j] = peek_slot(slots + (size_t)t * kBlock + lane);
+        if (!slot_ready(s1[j], tag)) s1[j] = peek_slot(slots + (size_t)t * kBlock + lane + 64);
       }
     }
-  } else {
-    // fp32 partials [split][m]; the last workgroup to arrive reduces.
-    float* partials = reinterpret_cast<float*>(a.slots);
-    if (kp == 0 && lane < 16) store_partial(partials + (size_t)split * a.m + ob * kBlock + orow, d);
-    if (!arrive_is_last(&a.counters[ob], (uint32_t)a.splits, flag)) return;
-    const float* pp = partials + ob * kBlock;
-    for (int t = wave; t < a.splits; t += WAVES) {
-      v0 += load_partial(pp + (size_t)t * a.m + lane);
-      v1 += load_partial(pp + (size_t)t * a.m + lane + 64);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int t = t0 + wave + j * WAVES;
+      if (t >= a.splits) break;
+      v0 += t == split ? ybuf[lane] : slot_value(s0[j], tag);
+      v1 += t == split ? ybuf[lane + 64] : slot_value(s1[j], tag);
     }
   }
   {
@@ -403,7 +384,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
         v1 += wsum[w * kBlock + lane + 64];
       }
       rht_out_block(v0, v1, a.scales, a.sign_out, a.y, ob * kBlock, lane);
-      if (lane == 0) reset_counter(&a.counters[ob]);
+      if (lane == 0) finish_call(&a.counters[ob], (uint32_t)a.splits);
     }
   }
 }
@@ -425,14 +406,14 @@ __global__ __launch_bounds__(64 * 8 * P) void gemv_kernel(GemvArgs a) {
 template <int CODE, bool ROUND, bool GATED>
 __device__ __forceinline__ void grouped_dispatch(const GemvArgs& a, int k_bits, int ob, int split, uint32_t* lds) {
   switch (k_bits) {
-    case 1: gemv_workgroup<1, CODE, ROUND, gemv_pf<1>(), kGemvP, GATED, false>(a, ob, split, lds); break;
-    case 2: gemv_workgroup<2, CODE, ROUND, gemv_pf<2>(), kGemvP, GATED, false>(a, ob, split, lds); break;
-    case 3: gemv_workgroup<3, CODE, ROUND, gemv_pf<3>(), kGemvP, GATED, false>(a, ob, split, lds); break;
-    case 4: gemv_workgroup<4, CODE, ROUND, gemv_pf<4>(), kGemvP, GATED, false>(a, ob, split, lds); break;
-    case 5: gemv_workgroup<5, CODE, ROUND, gemv_pf<5>(), kGemvP, GATED, false>(a, ob, split, lds); break;
-    case 6: gemv_workgroup<6, CODE, ROUND, gemv_pf<6>(), kGemvP, GATED, false>(a, ob, split, lds); break;
-    case 7: gemv_workgroup<7, CODE, ROUND, gemv_pf<7>(), kGemvP, GATED, false>(a, ob, split, lds); break;
-    default: gemv_workgroup<8, CODE, ROUND, gemv_pf<8>(), kGemvP, GATED, false>(a, ob, split, lds); break;
+    case 1: gemv_workgroup<1, CODE, ROUND, gemv_pf<1>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 2: gemv_workgroup<2, CODE, ROUND, gemv_pf<2>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 3: gemv_workgroup<3, CODE, ROUND, gemv_pf<3>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 4: gemv_workgroup<4, CODE, ROUND, gemv_pf<4>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 5: gemv_workgroup<5, CODE, ROUND, gemv_pf<5>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 6: gemv_workgroup<6, CODE, ROUND, gemv_pf<6>(), kGemvP, GATED>(a, ob, split, lds); break;
+    case 7: gemv_workgroup<7, CODE, ROUND, gemv_pf<7>(), kGemvP, GATED>(a, ob, split, lds); break;
+    default: gemv_workgroup<8, CODE, ROUND, gemv_pf<8>(), kGemvP, GATED>(a, ob, split, lds); break;
   }
 }
 

@@ -337,20 +337,34 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
 }
 
 // Split-K by ticket and slots (batch-1 and grouped paths). Every workgroup of
-// an output block takes a ticket when it starts; the holder of the last
-// ticket reduces. The others have all started by then and finish without
-// waiting on anything, so the reducer's wait for their partials ends. A slot
-// is one 64-bit word per partial: the fp32 bits with bit 32 set when full, 0
-// when empty. One atomic store publishes value and state together, so a
-// writer never waits for its store to land.
-constexpr uint32_t kSlotPolls = 1u << 20;   // bound of one wait: re-reads, about a second in all
+// an output block takes a ticket once its input has arrived; the holder of the
+// last ticket of the call reduces. The others have all started by then and
+// finish without waiting on anything, so the reducer's wait for their
+// partials ends. The ticket counter advances by kTicketCall per call (the
+// reducer tops it up), so a ticket's low 16 bits rank the workgroups of the
+// call and its high 16 bits number the call. A slot is one 64-bit word per
+// partial: the fp32 bits, and above them a tag, the call number + 1. Every
+// workgroup of the block, the reducer included, writes its slots in every
+// call, so a slot holds either this call's partial or the previous call's
+// (a different tag): nothing is cleared, and one atomic store publishes value
+// and tag together, so a writer never waits for its store to land. A zeroed
+// workspace starts at call 0 with no slot tagged.
+constexpr uint32_t kSlotPolls = 1u << 20;     // bound of one wait: re-reads, about a second in all
+constexpr uint32_t kTicketCall = 1u << 16;    // tickets per call (splits < 2^16)
 
 __device__ __forceinline__ uint32_t take_ticket(uint32_t* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void put_slot(uint64_t* p, float v) {
-  __hip_atomic_store(p, (uint64_t)__builtin_bit_cast(uint32_t, v) | (1ull << 32), __ATOMIC_RELAXED,
+// The reducer, holder of the call's last ticket: move the counter to the next call.
+__device__ __forceinline__ void finish_call(uint32_t* counter, uint32_t splits) {
+  __hip_atomic_fetch_add(counter, kTicketCall - splits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t slot_tag(uint32_t ticket) { return (ticket >> 16) + 1u; }
+
+__device__ __forceinline__ void put_slot(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, (uint64_t)__builtin_bit_cast(uint32_t, v) | ((uint64_t)tag << 32), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -358,13 +372,11 @@ __device__ __forceinline__ uint64_t peek_slot(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void clear_slot(uint64_t* p) {
-  __hip_atomic_store(p, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+__device__ __forceinline__ bool slot_ready(uint64_t s, uint32_t tag) { return (uint32_t)(s >> 32) == tag; }
 
-// Value of a slot read; NaN if it is still empty (a wait that ran out).
-__device__ __forceinline__ float slot_value(uint64_t s) {
-  return (s >> 32) != 0u ? __builtin_bit_cast(float, (uint32_t)s) : __builtin_nanf("");
+// Value of a slot read; NaN if it does not hold this call's partial (a wait that ran out).
+__device__ __forceinline__ float slot_value(uint64_t s, uint32_t tag) {
+  return slot_ready(s, tag) ? __builtin_bit_cast(float, (uint32_t)s) : __builtin_nanf("");
 }
 
 }  // namespace tg

@@ -25,8 +25,8 @@ struct GemvArgs {
   const uint32_t* sign_out;
   const uint16_t* x;
   float* y;
-  uint64_t* slots;      // [m/128][splits][128] split-K slots (unused when splits == 1), empty between calls
-  uint32_t* counters;   // [m/128]       ticket counters, zero between calls
+  uint64_t* slots;      // [m/128][splits][128] call-tagged split-K slots (unused when splits == 1)
+  uint32_t* counters;   // [m/128] ticket counters, on a call boundary (multiple of 2^16) between calls
   int32_t m, n, splits;
   const float* hg;      // gated-MLP input mode: x = fp16(silu(hg) * hu), fp32 rows of n values
   const float* hu;
@@ -49,8 +49,8 @@ struct GroupedArgs {
   int64_t x_stride;
   float* y;
   int64_t y_stride;
-  uint64_t* slots;      // fp32 split-K partials [n_sel][splits][max_m] (8 bytes reserved per partial)
-  uint32_t* counters;   // [n_sel][max_m/128]
+  uint64_t* slots;      // per selection [max_m/128][splits][128] call-tagged split-K slots
+  uint32_t* counters;   // [n_sel][max_m/128] ticket counters
   int32_t max_m, splits, round_weights;
   int32_t sel_pairs;    // 1: selection e uses layer 2*sel[e/2] + e%2 (gate and up of the selected experts)
   const float* hin;     // non-null: selection e's input is fp16(silu(hin row 2e) * hin row 2e+1)
