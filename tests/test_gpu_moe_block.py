@@ -48,9 +48,14 @@ def test_moe_block_pair_code_and_invalid_ids():
     x = inputs.make_x(wl.hidden, 77)
     say("moe block pair code")
     ws = tg.moe_workspace(gut, dnt, 4, dev)
+    # The workspace's last region holds the down projections, one row per selection; the rows of
+    # the invalid selections are never written, so fill that region with NaN bit patterns first:
+    # they must be dropped, not multiplied by a zero weight.
+    ws[ws.numel() - 4 * wl.hidden * 4:] = 0xFF
     for _ in range(2):                      # the workspace is reused across calls
         y = tg.trellis_moe_block(gut, dnt, torch.from_numpy(sel).to(dev), torch.from_numpy(w).to(dev),
                                  tg.fp16_tensor(x, dev), ws=ws)
         torch.cuda.synchronize()
         ref = moe.moe_block(gu, dn, [4, 0], [0.4, 0.2], x)
+        assert np.isfinite(y.cpu().numpy()).all()
         assert rel_err(y.cpu().numpy(), ref) <= REL_TOL

@@ -451,35 +451,32 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
 }
 
 // Router-weighted sum of the selected experts' outputs, in selection order;
-// selections outside [0, n_experts) contribute nothing. The selection and
-// weights are staged in LDS once, and each thread issues the loads of eight
-// experts before it adds them (a load per expert behind its own validity test
-// would wait for each in turn).
+// selections outside [0, n_experts) contribute nothing. Every row of Y2 is a
+// valid address (one per selection), so each thread loads eight experts' rows
+// together with their selection and weight (uniform, scalar loads) in one
+// round of memory latency, and an invalid selection's row -- never written,
+// so possibly not a number -- is dropped by a select, not multiplied by zero.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ Y2, int64_t y2_stride,
                                                           const int32_t* __restrict__ sel, const float* __restrict__ w,
                                                           int top_k, int n_experts, int hidden, float* __restrict__ y) {
-  __shared__ float wl[256];
-  __shared__ int32_t valid[256];
-  for (int e = threadIdx.x; e < top_k; e += 256) {
-    const int32_t s = sel[e];
-    valid[e] = s >= 0 && s < n_experts;
-    wl[e] = w[e];
-  }
-  __syncthreads();
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= hidden) return;
   float acc = 0.f;
   for (int e0 = 0; e0 < top_k; e0 += 8) {
-    float v[8];
+    float v[8], wt[8];
+    int32_t sv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int e = e0 + j;
-      v[j] = (e < top_k && valid[e]) ? Y2[(size_t)e * y2_stride + o] : 0.f;
+      const int e = e0 + j < top_k ? e0 + j : top_k - 1;   // past the end: re-read the last, unused
+      sv[j] = sel[e];
+      wt[j] = w[e];
+      v[j] = Y2[(size_t)e * y2_stride + o];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int e = e0 + j;
-      if (e < top_k && valid[e]) acc += wl[e] * v[j];
+      const bool ok = e0 + j < top_k && sv[j] >= 0 && sv[j] < n_experts;
+      const float t = wt[j] * v[j];
+      acc = ok ? acc + t : acc;
     }
   }
   y[o] = acc;
