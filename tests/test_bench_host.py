@@ -22,3 +22,18 @@ def test_algorithmic_bytes():
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_recorded_traffic_only_for_the_sources_it_was_taken_on(monkeypatch):
+    """profiles/traffic.json is tied to a hash of the kernel sources: the bench reports measured HBM
+    traffic while that hash matches, and null once any kernel source has changed."""
+    import json
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    assert len(rec["csrc_sha"]) == 16 and bench.kernel_source_hash() == bench.kernel_source_hash()
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["csrc_sha"])
+    down = rec["workloads"]["2"]["down"]
+    assert bench.recorded_traffic(2, "down") == down["hbm_bytes_per_launch"]
+    assert down["hbm_bytes_per_launch"] == down["fetch_bytes_per_launch"] + down["write_bytes_per_launch"]
+    assert bench.recorded_traffic(2, "no such launch") is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.recorded_traffic(2, "down") is None
