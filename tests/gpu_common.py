@@ -6,7 +6,7 @@ import pytest
 
 from trellis_coded_gemv_amd import binding as tg
 
-# spec bar for fp32-accumulated outputs: max |y_gpu - y_ref| / max |y_ref| <= 1e-3
+# Parity bar for fp32-accumulated outputs: max |y_gpu - y_ref| / max |y_ref| <= 1e-3
 REL_TOL = 1e-3
 
 
