@@ -108,9 +108,11 @@ int gemm_splits(int m, int n, int M, int k_bits, int code_id) {
 // A layer's workspace: the batch-1 ticket counters and the small-batch
 // arrival counters, each in an area sized for the largest layer (so every
 // layer finds its counters at the same place), then scratch shared by both
-// paths. Every call leaves the counters it used at zero; the scratch may hold
-// anything between calls (the batch-1 path empties its own slots before use).
-// One buffer can therefore serve any sequence of layers and paths.
+// paths. A batch-1 call leaves its ticket counters on a call boundary (a
+// multiple of 2^16) and a small-batch call leaves its arrival counters at
+// zero; the scratch may hold anything between calls (batch-1 slots carry the
+// call's tag, so stale contents are never taken for a partial). One buffer can
+// therefore serve any sequence of layers and paths.
 constexpr size_t kCounterArea = (size_t)((1 << 22) / kBlock) * 4;
 
 struct GemvWs {

@@ -25,8 +25,10 @@
 // the chunk, so the MFMA accumulators of a wave stay put for the whole loop
 // and the x~ operand of a column (prepared once per call by xt_prep_kernel,
 // read from L2) is loaded once for 8 tiles. The waves are summed through LDS
-// at the end; split-K partials and the
-// last-arriving-workgroup epilogue are as in the batch-1 kernel.
+// at the end. With split K, every workgroup stores its fp32 partials to the
+// workspace with device-scope stores and bumps the block's arrival counter;
+// the last to arrive sums the splits in a fixed order, applies scale, output
+// FWHT and signs, and resets the counter to zero.
 //
 // Pair code (code_id 1): a state covers two input columns, so one tile row of
 // 16 weights needs only 8 code words (k = 16) and one MFMA spans two adjacent

@@ -30,17 +30,18 @@
 // Walsh-Hadamard transform, 1/sqrt(128)) into LDS as fp16 pairs, eight lanes
 // per block with one fp32 exchange through LDS and no lane shuffles. Epilogue: lane -> wave reduction by lane shuffles,
 // then either a direct output transform (1 split) or fp32 split-K partials in
-// the workspace; the last-arriving workgroup of a block sums them in a fixed
-// order and applies scale, output FWHT and signs. No waiting on other
-// workgroups anywhere: every workgroup runs to completion independently.
+// call-tagged workspace slots. The workgroup that took the block's last ticket
+// of the call (tickets are taken once the input has arrived, so every other
+// workgroup of the block is already running and finishes without waiting)
+// waits for those slots, sums them in a fixed order and applies scale, output
+// FWHT and signs. No other workgroup waits on anything.
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
 namespace tg {
 
-// Prefetch depth in steps (each step is 8K bytes per lane).
-// Prefetch depth in steps. Kept even so the x~ double buffer alternates
-// statically inside the unrolled loop.
+// Prefetch depth in steps (each step is 8K bytes per lane). Kept even so the
+// x~ double buffer alternates statically inside the unrolled loop.
 #ifndef TG_GEMV_PF_SMALL_K
 #define TG_GEMV_PF_SMALL_K 2
 #endif
@@ -256,8 +257,9 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
     }
     x16_phase2(e, o);
     __syncthreads();   // every wave has read its exchange values
-    // Split-K ticket: after the input has arrived (and with it the slot
-    // clears); the answer is needed only at the end.
+    // Split-K ticket: taken once the input has arrived (issued earlier, the
+    // atomic would hold back the loads queued behind it); the answer is
+    // needed only at the end.
     if (a.splits > 1 && threadIdx.x == 0) ticket = take_ticket(&a.counters[ob]);
     if (active) {
 #pragma unroll
