@@ -117,16 +117,21 @@ const char *tg_status_str(int32_t status);
 /*
  * Workspace bytes needed by trellis_gemv (M == 1) or trellis_gemm_small
  * (1 <= M <= 64) for this layer, or 0 if the layer / M is invalid.
- * Layout: two counter areas of fixed size (256 KiB in all: the batch-1
- * tickets and the small-batch arrival counters, each sized for the largest
- * layer), then scratch (split-K partials, the small-batch input transform).
- * It must be zero-filled before its first use. Every completed call leaves the
+ * Layout, at the same offsets for every layer: two counter areas (256 KiB in
+ * all: the batch-1 tickets and the small-batch arrival counters, each sized
+ * for the largest layer), the batch-1 split-K slots (2 MiB), then the
+ * small-batch scratch (input transform, split-K partials). It must be
+ * zero-filled before its first use. Every completed call leaves the
  * small-batch counters at zero and each batch-1 ticket counter on a call
- * boundary (a multiple of 65536: the counter advances by 65536 per call, and
- * its high 16 bits number the calls and tag the split-K slots, so slots are
- * never cleared); the scratch may hold anything between calls. One buffer,
- * as large as each layer needs, can therefore serve any sequence of layers and
- * of both entry points on one stream. 256-byte alignment is required.
+ * boundary (a multiple of 65536: the counter advances by 65536 per call).
+ * A batch-1 slot carries the number of its call on its output block and the
+ * layer's split count, so slots are never cleared: a slot left by another
+ * layer or an earlier call is never taken for this call's partial, unless
+ * 65535 or more calls with other split counts ran on that output block since
+ * the last call with this split count. The small-batch scratch may hold
+ * anything between calls. One buffer, as large as each layer needs, can
+ * therefore serve any sequence of layers and of both entry points on one
+ * stream. 256-byte alignment is required.
  */
 size_t tg_workspace_size(const tg_layer *layer, int32_t M);
 
@@ -140,7 +145,10 @@ size_t tg_workspace_size(const tg_layer *layer, int32_t M);
  * one of them through the workspace; its wait for them is bounded (about a
  * second) and, should the device ever stall a workgroup that long, the
  * affected outputs are written as NaN (the workspace stays usable: a late
- * partial carries its own call's tag).
+ * partial carries its own call's tag). A layer whose input must be cut into
+ * more chunks than the slot area holds ((m/128) * chunks > 2048; some 2^31
+ * weights and more, since a chunk spans at most 8192 inputs) returns
+ * TG_ERR_SHAPE.
  */
 int32_t trellis_gemv(const tg_layer *layer, const uint16_t *x, float *y,
                      void *ws, size_t ws_bytes, void *stream);
@@ -243,7 +251,10 @@ size_t tg_grouped_workspace_size(const tg_layer *layers, int32_t n_layers, int32
  *                         256-byte aligned and zero-filled before its first use. Every
  *                         call leaves its ticket counters on a call boundary; the rest holds
  *                         the call's intermediate rows. Calls that share a workspace
- *                         must be ordered (one stream).
+ *                         must be ordered (one stream); a workspace used before with
+ *                         other table shapes or another top_k must be zero-filled again
+ *                         (the intermediate rows sit where another shape keeps its
+ *                         split-K slots).
  * All layers must share TG_FLAG_* flags. Errors: a negative tg_status (shape, table,
  * top_k, alignment or workspace checks) with nothing launched.
  */

@@ -206,9 +206,13 @@ def test_trellis_linear_dispatch():
 
 
 def test_huge_shapes_rejected_before_launch():
-    """Dense-output entry points cap the weight count (2^38); the grouped grid must fit 31 bits."""
+    """Dense-output entry points cap the weight count (2^38); the grouped grid must fit 31 bits; a
+    batch-1 layer whose input chunks overflow the workspace's slot area (2048 block-chunk pairs) is
+    refused, while the same layer's small-batch workspace size is still defined."""
     L = tg.lib()
     big = _layer(m=1 << 22, n=1 << 22)
+    assert L.trellis_gemv(ctypes.byref(big), A16, A16, A16, 1 << 40, None) == -2
+    assert L.tg_workspace_size(ctypes.byref(big), 16) > 0
     assert L.trellis_decode(ctypes.byref(big), A16, None) == -2
     assert L.tg_prefill_workspace_size(ctypes.byref(big), 16) == 0
     assert L.trellis_gemm_prefill(ctypes.byref(big), 16, A16, 1 << 22, A16, 1 << 22, A16, 1 << 40, None) == -2

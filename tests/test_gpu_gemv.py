@@ -192,3 +192,44 @@ def test_workspace_shared_by_layers_and_paths():
         assert (ws[counters // 2: counters] == 0).all(), name
     rows = sample_rows(512)
     assert rel_err(ref["vb"].cpu().numpy()[rows], ogemv.gemv_rows(b_arr, inputs.make_x(8192, 91), rows)) <= REL_TOL
+
+
+def test_stale_slots_never_carry_the_expected_tag():
+    """Two layers with 8 and 16 splits share one buffer, so a slot address belongs to different output
+    blocks (and ticket counters) in turn. Read off the device around every batch-1 call: before it,
+    no slot of the call's layout holds the tag the call waits for (its block's call number and its
+    split count); after it, every slot of the layout holds exactly that tag, and y equals the result
+    on a fresh workspace. The sequence is one where a tag of the call number alone would match a
+    stale slot, which is asserted too, so the check does not rest on the reducer happening to read
+    after the writers."""
+    dev = device()
+    import torch
+    a_arr, b_arr = inputs.make_layer(1024, 4096, 3, 94), inputs.make_layer(512, 8192, 2, 95)
+    A, B = tg.DeviceLayer(a_arr, dev), tg.DeviceLayer(b_arr, dev)
+    xa, xb = tg.fp16_tensor(inputs.make_x(4096, 94), dev), tg.fp16_tensor(inputs.make_x(8192, 95), dev)
+    ref = {"a": tg.trellis_gemv(A, xa), "b": tg.trellis_gemv(B, xb)}
+    ws = torch.zeros(max(tg.workspace(A, 1, dev).numel(), tg.workspace(B, 1, dev).numel()),
+                     dtype=torch.uint8, device=dev)
+    counter_area = (1 << 22) // 128 * 4
+    slot_off = 2 * counter_area                  # the slot area follows both counter areas
+    say("stale slot tags")
+    call_tag_alone_would_match = False
+    for name in "ababa":
+        L, x, ob = (A, xa, 8) if name == "a" else (B, xb, 4)
+        pre = ws.clone()
+        y = tg.trellis_gemv(L, x, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[name]), name
+        post_slots = ws[slot_off:].view(torch.int64)
+        S = int((post_slots[0] >> 32) & 0xFFFF)   # the split count the call wrote
+        assert S in (8, 16), S
+        tickets = pre[:counter_area].view(torch.int32)[:ob].to(torch.int64) & 0xFFFFFFFF
+        expect = ((tickets & 0xFFFF0000) | S).view(ob, 1)
+        n_slots = ob * S * 128
+        after = ((post_slots[:n_slots] >> 32) & 0xFFFFFFFF).view(ob, S * 128)
+        before = ((pre[slot_off:].view(torch.int64)[:n_slots] >> 32) & 0xFFFFFFFF).view(ob, S * 128)
+        assert (after == expect).all(), name
+        assert not (before == expect).any(), name
+        old_rule = (tickets >> 16).view(ob, 1) + 1  # a tag of the call number + 1 alone
+        call_tag_alone_would_match |= bool(((before >> 16) + 1 == old_rule).logical_and(before != 0).any())
+    assert call_tag_alone_would_match

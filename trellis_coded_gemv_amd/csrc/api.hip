@@ -29,6 +29,13 @@ static_assert(offsetof(tg_layer, sign_out) == offsetof(LayerDev, sign_out), "dev
 // bound keeps their grids within 32 bits.
 constexpr int64_t kMaxDenseWeights = (int64_t)1 << 38;
 
+// Batch-1 split-K slots in a layer workspace: room for kSlotPairs (output
+// block, split) pairs of 128 64-bit slots, 2 MiB at a fixed offset. The split
+// choice below uses about 256 pairs; only a layer that needs many input chunks
+// to fit the LDS (some 2^31 weights and more) needs more, and is refused.
+constexpr int kSlotPairs = 2048;
+constexpr size_t kSlotArea = (size_t)kSlotPairs * kBlock * 8;
+
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
@@ -79,6 +86,8 @@ int gemv_splits(int m, int n) {
     const int target = (256 + ob / 2) / ob;
     s = split_for_target(nb, target < max_s ? target : max_s);
   }
+  const int cap = kSlotPairs / ob;               // (block, split) pairs the slot area holds
+  if (s > cap) s = cap;
   const int min_s = (nb + kMaxChunkBlocks - 1) / kMaxChunkBlocks;
   if (s < min_s) s = min_s;
   if (s > nb) s = nb;
@@ -105,14 +114,15 @@ int gemm_splits(int m, int n, int M, int k_bits, int code_id) {
   return s;
 }
 
-// A layer's workspace: the batch-1 ticket counters and the small-batch
-// arrival counters, each in an area sized for the largest layer (so every
-// layer finds its counters at the same place), then scratch shared by both
-// paths. A batch-1 call leaves its ticket counters on a call boundary (a
-// multiple of 2^16) and a small-batch call leaves its arrival counters at
-// zero; the scratch may hold anything between calls (batch-1 slots carry the
-// call's tag, so stale contents are never taken for a partial). One buffer can
-// therefore serve any sequence of layers and paths.
+// A layer's workspace, at fixed offsets for every layer: the batch-1 ticket
+// counters and the small-batch arrival counters, each in an area sized for the
+// largest layer; the batch-1 split-K slots, in an area of kSlotPairs (block,
+// split) pairs; then the small-batch scratch (input transform, partials). A
+// batch-1 call leaves its ticket counters on a call boundary (a multiple of
+// 2^16) and a small-batch call leaves its arrival counters at zero. The slots
+// carry their call's number and split count, and the small-batch scratch never
+// reaches the slot area, so no stale word is ever taken for a partial. One
+// buffer can therefore serve any sequence of layers and paths.
 constexpr size_t kCounterArea = (size_t)((1 << 22) / kBlock) * 4;
 
 struct GemvWs {
@@ -127,6 +137,10 @@ GemvWs gemv_ws(int m, int splits) {
   return w;
 }
 
+// A batch-1 split that the slot area cannot hold (layers of more than about
+// 2^31 weights, whose chunks must be many to fit the LDS).
+bool gemv_slots_overflow(int m, int splits) { return splits > 1 && (int64_t)splits * (m / kBlock) > kSlotPairs; }
+
 struct GemmWs {
   size_t counters, xt, partials, total;
 };
@@ -135,7 +149,7 @@ GemmWs gemm_ws(int m, int n, int M, int splits) {
   GemmWs w;
   const int mpad = (M + 15) / 16 * 16;
   w.counters = kCounterArea;
-  w.xt = 2 * kCounterArea;
+  w.xt = 2 * kCounterArea + kSlotArea;
   w.partials = w.xt + round_up((size_t)mpad * n * 4, kAlign);
   w.total = w.partials + (splits > 1 ? round_up((size_t)splits * M * m * 4, kAlign) : 0);
   return w;
@@ -214,6 +228,7 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
   if (!x || !y) return TG_ERR_NULL;
   if (misaligned(x, 2) || misaligned(y, 4)) return TG_ERR_ALIGN;
   const int splits = gemv_splits(L->m, L->n);
+  if (gemv_slots_overflow(L->m, splits)) return TG_ERR_SHAPE;
   const GemvWs w = gemv_ws(L->m, splits);
   if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
   if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;

@@ -328,7 +328,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   // slot is ever more than one call old), and all but the reducer leave.
   if (threadIdx.x == 0) {
     flag[0] = (ticket & (kTicketCall - 1u)) == (uint32_t)a.splits - 1u ? 1u : 0u;
-    flag[1] = slot_tag(ticket);
+    flag[1] = slot_tag(ticket, (uint32_t)a.splits);
   }
   if (kp == 0 && lane < 16) ybuf[orow] = d;
   __syncthreads();

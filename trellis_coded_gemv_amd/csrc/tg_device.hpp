@@ -343,12 +343,17 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
 // partials ends. The ticket counter advances by kTicketCall per call (the
 // reducer tops it up), so a ticket's low 16 bits rank the workgroups of the
 // call and its high 16 bits number the call. A slot is one 64-bit word per
-// partial: the fp32 bits, and above them a tag, the call number + 1. Every
-// workgroup of the block, the reducer included, writes its slots in every
-// call, so a slot holds either this call's partial or the previous call's
-// (a different tag): nothing is cleared, and one atomic store publishes value
-// and tag together, so a writer never waits for its store to land. A zeroed
-// workspace starts at call 0 with no slot tagged.
+// partial: the fp32 bits, and above them a tag, the call number and the split
+// count (slot_tag). Slot (counter c, split s, lane i) sits at (c*S + s)*128 + i
+// for S splits, so the same address under another split count belongs to
+// another block and counter, and is never taken for this call's: its tag has
+// another split count. Under the same split count the address belongs to this
+// counter, whose earlier calls carry earlier call numbers (equal only after
+// 2^16 calls of other split counts on the block in between). Every workgroup
+// of the block, the reducer included, writes its slots in every call, so
+// nothing is cleared, and one atomic store publishes value and tag together:
+// a writer never waits for its store to land. A zeroed workspace starts at
+// call 0 with no slot tagged (a tag's split count is at least 2).
 constexpr uint32_t kSlotPolls = 1u << 20;     // bound of one wait: re-reads, about a second in all
 constexpr uint32_t kTicketCall = 1u << 16;    // tickets per call (splits < 2^16)
 
@@ -361,7 +366,9 @@ __device__ __forceinline__ void finish_call(uint32_t* counter, uint32_t splits) 
   __hip_atomic_fetch_add(counter, kTicketCall - splits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint32_t slot_tag(uint32_t ticket) { return (ticket >> 16) + 1u; }
+__device__ __forceinline__ uint32_t slot_tag(uint32_t ticket, uint32_t splits) {
+  return (ticket & ~(kTicketCall - 1u)) | splits;
+}
 
 __device__ __forceinline__ void put_slot(uint64_t* p, float v, uint32_t tag) {
   __hip_atomic_store(p, (uint64_t)__builtin_bit_cast(uint32_t, v) | ((uint64_t)tag << 32), __ATOMIC_RELAXED,
