@@ -137,6 +137,33 @@ def test_gemv_many_splits(splits, monkeypatch):
     assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
 
 
+
+def test_gemv_slot_area_full_beside_small_batch(monkeypatch):
+    """A 32768 x 4096 layer with a forced 16 splits is held to the slot area's 2048 (block, split)
+    pairs (256 blocks x 8 splits): its slots fill the area exactly. Batch-1 and 16-row calls then
+    alternate on one buffer; each result equals the one on a fresh workspace, bit for bit, so the
+    small-batch scratch and the full slot area do not overlap."""
+    dev = device()
+    import torch
+    monkeypatch.setenv("TG_SPLITK", "16")
+    arr = inputs.make_layer(32768, 4096, 2, 96)
+    L = tg.DeviceLayer(arr, dev)
+    x = inputs.make_x(4096, 96)
+    xt = tg.fp16_tensor(x, dev)
+    X = tg.fp16_tensor(inputs.make_x(4096, 97, rows=16), dev)
+    say("slot area full", 32768, 4096)
+    ref_v, ref_g = tg.trellis_gemv(L, xt), tg.trellis_gemm_small(L, X)
+    ws = tg.workspace(L, 16, dev)
+    for _ in range(2):
+        assert torch.equal(tg.trellis_gemv(L, xt, ws=ws), ref_v)
+        assert torch.equal(tg.trellis_gemm_small(L, X, ws=ws), ref_g)
+    torch.cuda.synchronize()
+    slots = ws[2 * (1 << 22) // 128 * 4:].view(torch.int64)
+    assert (((slots[: 2048 * 128] >> 32) & 0xFFFF) == 8).all()   # 8 splits in every pair's tag
+    rows = sample_rows(32768)
+    assert rel_err(ref_v.cpu().numpy()[rows], ogemv.gemv_rows(arr, x, rows)) <= REL_TOL
+
+
 def test_gemv_call_tags_wrap():
     """70,000 calls on one workspace: the 16-bit call number in the ticket counters and slot tags
     wraps (at 65,536 calls) without a stale partial ever being taken for a current one."""
