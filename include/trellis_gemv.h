@@ -217,7 +217,11 @@ int32_t rht_apply(int32_t n, int32_t rows, const uint16_t *in, float *out,
  *   ws        : device workspace, ws_bytes >= tg_grouped_workspace_size(...),
  *               zero-filled before its first use; every call leaves its ticket
  *               counters on a call boundary (as for trellis_gemv), and calls
- *               that share it must be ordered (one stream).
+ *               that share it must be ordered (one stream). Its first n_sel *
+ *               (largest m / 128) words are ticket counters and its split-K slots
+ *               follow, so a workspace used before with another n_sel or largest
+ *               m must be zero-filled again (one geometry's slots lie where
+ *               another keeps its counters).
  * Every layer's n must fit the input stride (n <= x_stride when x_stride != 0)
  * and m <= y_stride. Indices in d_sel outside [0, n_layers) make the affected
  * selection write nothing. n_sel * (max m / 128) * (max n / 128) must stay
