@@ -48,7 +48,6 @@ import math
 import os
 import sys
 import time
-from collections import defaultdict
 
 import numpy as np
 

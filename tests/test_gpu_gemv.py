@@ -1,5 +1,4 @@
 """GPU parity: batch-1 trellis GEMV and the randomized Hadamard transform against the oracle."""
-import os
 
 import numpy as np
 import pytest
