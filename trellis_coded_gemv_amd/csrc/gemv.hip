@@ -215,6 +215,10 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   X16 xraw;
   XGated16 graw;
 #pragma clang diagnostic pop
+  // Waves whose lanes all lie past the chunk's blocks (uniform) skip the
+  // transform below but still issue these loads, so that every path keeps
+  // the same loads in flight and the waits on the prefetch stay exact.
+  const bool xwave = 8 * wave < nbp;
   if constexpr (GATED) graw = load_gated16(a.hg, a.hu, a.sign_in, xfirst);
   else xraw = load_x16(a.x, a.sign_in, xfirst);
   __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the prefetch below
@@ -239,23 +243,25 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   {
     const bool active = xb < nbp, live = xb < cb;
     float* sc = reinterpret_cast<float*>(xx_lds) + xb * kBlock;
-    float v[16];
-    if constexpr (GATED) xraw = gated_to_x16(graw);
-    x16_phase1(xraw, xfirst, v);
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        reinterpret_cast<float4_t*>(sc + 16 * xs)[i] = float4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-    }
-    __builtin_amdgcn_wave_barrier();
     float e[8], o[8];
+    if (xwave) {
+      float v[16];
+      if constexpr (GATED) xraw = gated_to_x16(graw);
+      x16_phase1(xraw, xfirst, v);
+      if (active) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float2 t = active ? *reinterpret_cast<const float2*>(sc + 16 * j + 2 * xs) : float2{0.f, 0.f};
-      e[j] = live ? t.x : 0.f;
-      o[j] = live ? t.y : 0.f;
+        for (int i = 0; i < 4; ++i)
+          reinterpret_cast<float4_t*>(sc + 16 * xs)[i] = float4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 t = active ? *reinterpret_cast<const float2*>(sc + 16 * j + 2 * xs) : float2{0.f, 0.f};
+        e[j] = live ? t.x : 0.f;
+        o[j] = live ? t.y : 0.f;
+      }
+      x16_phase2(e, o);
     }
-    x16_phase2(e, o);
     __syncthreads();   // every wave has read its exchange values
     // Split-K ticket: taken once the input has arrived (issued earlier, the
     // atomic would hold back the loads queued behind it); the answer is
