@@ -17,7 +17,8 @@ Two routes are provided and pinned against each other: the factored route
 W_eff = diag(s_out) H diag(g) W^ H diag(s_in) and multiplies once. The
 batched and grouped forms run the single-vector routine row by row and expert
 by expert. Further pins: the all-zero stream has a closed-form output, a
-naive triple loop agrees on a small layer, unit impulses read out columns.
+naive Python loop over every element agrees on the 256x256 layer
+(tests/test_oracle_gemv.py), unit impulses read out columns.
 """
 from __future__ import annotations
 

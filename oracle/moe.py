@@ -11,9 +11,13 @@ product rounded once to binary16 (every GEMV of this library takes fp16
 inputs); the router weights are given per token and combined in selection
 order. Every GEMV is the oracle's single-vector routine (gemv.py).
 
-Pins (tests/test_oracle_moe.py): silu's closed forms and symmetry; a single
-expert with weight 1 equals the chain of single GEMVs; the block is linear in
-the router weights and invariant to reordering the selection.
+Pins (tests/test_oracle_moe.py): silu's closed forms and symmetry; a closed
+form of the whole block on all-zero streams (every projection is then non-zero
+only at outputs 0 mod 128, so h and y follow by hand, with silu from SciPy's
+logistic function and binary16 rounding from NumPy's cast), which fails if gate
+and up are swapped, if silu acts on up, or if h is not rounded to binary16 once;
+the block is linear in the router weights and invariant to reordering the
+selection.
 """
 from __future__ import annotations
 

@@ -16,3 +16,12 @@ def golden_rows(name):
     """Non-comment, non-empty lines of a golden fixture, split on whitespace."""
     with open(os.path.join(GOLDEN, name)) as f:
         return [ln.split() for ln in f if ln.strip() and not ln.lstrip().startswith("#")]
+
+
+def hand_code(state):
+    """Weight value of a trellis state from the hand-derived golden fixture (not the oracle)."""
+    import numpy as np
+    for row in golden_rows("code_hand_values.txt"):
+        if int(row[0], 16) == state:
+            return float(np.array([int(row[7], 16)], np.uint16).view(np.float16)[0])
+    raise KeyError(state)

@@ -191,3 +191,33 @@ def test_pair_code_tile_layout():
     expect = np.tile(_bits([e0, o0]), (m, n // 2))
     expect[16 * R:16 * R + 16, 16 * C:16 * C + 16] = np.tile(_bits([e1, o1]), (16, 8))
     assert np.array_equal(W, expect)
+
+
+def test_naive_triple_loop_small_layer():
+    """The 256x256 K=2 layer by plain Python loops over every element: signs and the
+    (-1)^popcount(i & j) / sqrt(128) Hadamard entries on the input side, the scaled
+    product with the decoded weights, then the Hadamard entries and signs on the output
+    side -- against the oracle's NumPy route."""
+    wl = inputs.CFG1
+    m, n, k = wl.tensors["linear"]
+    L = inputs.make_layer(m, n, k, wl.seed)
+    x = inputs.make_x(n, wl.seed)
+    W = gemv.weight_matrix(L).tolist()
+    xv = [float(v) for v in x.view(np.float16)]
+    g = [float(v) for v in L.scales.view(np.float16)]
+    sin = [-1.0 if (int(L.sign_in[i // 32]) >> (i % 32)) & 1 else 1.0 for i in range(n)]
+    sout = [-1.0 if (int(L.sign_out[o // 32]) >> (o % 32)) & 1 else 1.0 for o in range(m)]
+    r = 1.0 / 128 ** 0.5
+    xt = [0.0] * n
+    for i in range(n):
+        b = i - i % 128
+        xt[i] = sum((-1.0 if bin((i % 128) & j).count("1") % 2 else 1.0) * sin[b + j] * xv[b + j]
+                    for j in range(128)) * r
+    yt = [g[o] * sum(W[o][i] * xt[i] for i in range(n)) for o in range(m)]
+    y = [0.0] * m
+    for o in range(m):
+        b = o - o % 128
+        y[o] = sout[o] * r * sum((-1.0 if bin((o % 128) & j).count("1") % 2 else 1.0) * yt[b + j]
+                                 for j in range(128))
+    ref = gemv.gemv(L, x)
+    assert np.allclose(ref, y, rtol=1e-12, atol=1e-12 * np.abs(ref).max())

@@ -146,3 +146,21 @@ def test_pair_steps_single_bits(k):
         s = trellis.walk_states(trellis.stream_bits(_tile_from_bits(bits), k), k, v=2)
         d = (p - 2 * k * tau) % nb
         assert (s == np.where(d <= 15, 1 << (15 - np.minimum(d, 15)), 0)).all(), p
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 8])
+def test_broken_circle_rejected(k):
+    """closes_circle is False once the first state, or a low bit of the last state, no longer
+    follows the circle (the tail-biting closure of the lecture, Part eight)."""
+    b = trellis.stream_bits(_random_tiles(k, 32, 50 + k), k)
+    s = trellis.walk_states(b, k)
+    assert trellis.closes_circle(s, b, k).all()
+    first = s.copy()
+    first[:, 0] ^= 1                    # the bit the closing step shifts in last
+    assert not trellis.closes_circle(first, b, k).any()
+    last = s.copy()
+    last[:, -1] ^= 1 << (15 - k) if k < 16 else 1   # a bit the closing step keeps
+    assert not trellis.closes_circle(last, b, k).any()
+    tail = b.copy()
+    tail[:, 15] ^= 1                    # the stream's bit 15 closes the circle
+    assert not trellis.closes_circle(s, tail, k).any()
