@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the trellis-coded GEMV hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--code 0]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 input-side randomized Hadamard transform, trellis decode of every weight,
@@ -9,8 +9,9 @@ dot products, split-K reduction, per-output scale and output-side transform,
 through the C ABI. Workloads (seeded, synthetic; no trained weights):
 
   1  one 256x256 linear, K=2, batch 1
-  2  Llama-3-8B-shaped MLP down-projection 14336 -> 4096, K=3, batch 1 (default)
-  3  the seven linears of a 70B-shaped decoder layer, K=2, batch 1 (a step = 7 GEMVs)
+  2  Llama-3-8B-shaped MLP down-projection 14336 -> 4096, K=3, batch 1
+  3  the seven linears of a 70B-shaped decoder layer, K=2, batch 1 (a step = 7 GEMVs;
+     the default: the largest batch-1 workload)
   4  gate projection 8192 -> 28672, K=4, 16 activation rows (MFMA path)
   5  MoE: 128 experts (gate/up 2048->768, down 768->2048, K in {1,2,3}), top-8 per
      token, a step = one token = 2 grouped launches
@@ -20,25 +21,27 @@ through the C ABI. Workloads (seeded, synthetic; no trained weights):
      down -> router-weighted combine (3 launches)
 
 Enough seeded copies of the weights (>= 1 GiB, four times the 256 MB Infinity
-Cache) are used round-robin that the timed reads come from HBM. Inputs are in
-device memory before the timed region starts.
+Cache) are used round-robin, and every timed step uses a copy that at least
+1 GiB of other copies were read after, so the timed reads come from HBM.
+Inputs are in device memory before the timed region starts.
 
 Prints ONE JSON line: value = compressed-weight GB/s over the timed region (K
 steps between two synchronisations, HIP events on the launch stream, steps
-replayed from a captured HIP graph), the roofline of the dominant kernel, and
-the CPU oracle timed on a bounded sample of the same workload on the host.
+replayed from a captured HIP graph), the roofline of the dominant kernel, the
+CPU oracle timed on a bounded sample of the same workload on every host core
+of the process's affinity mask, and short measurements of workloads 2, 4 and 5
+as context.
 
-The dominant kernel (the launch moving the most bytes) is timed alone: the same
-K steps restricted to its launches, replayed from their own graph, give its mean
-launch duration. The decode is bound by VALU arithmetic, so the roofline is an
-ALU one: algorithmic lane-operations per launch (decoded weights x the minimum
-VALU operations per weight the code needs on gfx950: window extract,
-multiply-add, and-or, dot2 = 4 for code 0; 2 for the pair code, one state per
-two weights; one fewer per state on the MFMA path, whose dot products run on
-the matrix cores) over the launch duration, against 256 CUs x 4 SIMDs x 16
-lanes x 2.4 GHz = 39.3 T lane-operations/s. The same launch's HBM view
-(algorithmic bytes / duration against 8 TB/s) and the measured HBM traffic
-(rocprofv3 FETCH_SIZE + WRITE_SIZE, profiles/traffic.json) are reported with it.
+Roofline. The dominant launch (the one moving the most bytes) is timed alone:
+the same K steps restricted to its launches, replayed from their own graph,
+give its mean launch duration. `achieved` = its algorithmic bytes (codes + x
+fp16 + y fp32 + scales fp16 + sign bits) / that duration, against the 8 TB/s
+HBM peak. The decode is bound by VALU issue in practice, so the line also
+carries an ALU view: decoded weights per second of that launch against the
+decode-only ceiling (tg_decode_ceiling: the batch-1 loop on code words held
+in LDS), measured in the same run. `traffic` is the measured HBM bytes of one
+launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, profiles/traffic.json) while the
+kernel sources match the ones it was taken on.
 """
 from __future__ import annotations
 
@@ -57,22 +60,16 @@ if ROOT not in sys.path:
 
 METRIC = "batch-1 trellis GEMV: compressed-weight HBM GB/s (% of peak) + µs/layer"
 HBM_PEAK_GBS = 8000.0
-ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12      # VALU lane-operations per second, in T (39.32)
 MFMA_F16_PEAK_TFLOPS = 2500.0
 CACHE_DEFEAT_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DEFAULT_WORKLOAD = 3
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: counter-derived traffic is only reported for the kernels it was taken on."""
-    import hashlib
-    d = os.path.join(ROOT, "trellis_coded_gemv_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
-    return h.hexdigest()[:16]
+    """Hash of the library sources (the library reports the same value as tg_build_id())."""
+    from trellis_coded_gemv_amd.build import source_hash
+    return source_hash()
 
 
 def recorded_traffic(workload: int, kernel: str, code_id: int = 0):
@@ -92,12 +89,6 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def alu_ops_per_weight(code_id: int, mfma: bool) -> float:
-    """Minimum VALU lane-operations per decoded weight (see the module docstring)."""
-    per_state = 3 if mfma else 4          # window extract, multiply-add, and-or (+ dot2 on the VALU path)
-    return per_state / (2 if code_id == 1 else 1)
-
-
 def gemv_bytes(m: int, n: int, k: int, M: int = 1) -> int:
     """Algorithmic bytes of one layer call: codes + x (fp16) + y (fp32) + scales (fp16) + sign bits."""
     return m * n * k // 8 + 2 * n * M + 4 * m * M + 2 * m + (n + m) // 8
@@ -114,25 +105,46 @@ class Launches:
             fn()
 
 
-def graph_time_ms(torch, step, steps, launches):
-    """Capture `steps` steps into one HIP graph, replay it once between two events; return ms."""
+def timed_steps_ms(torch, step, first, steps, copies, launches, use_graph):
+    """Time `steps` steps starting at step index `first`. Returns (ms, how).
+
+    Graph mode captures the steps into one HIP graph and replays it once untimed; then,
+    if the steps use fewer copies than there are, eager steps over the other copies run
+    (so each timed copy was last read before at least 1 GiB of other copies), and a
+    second replay is timed between two events on the launch stream.
+    """
     stream = torch.cuda.current_stream()
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(stream)
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for i in range(steps):
-                step(i, launches)
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def flush():
+        for j in range(max(0, copies - steps)):
+            step(first + steps + j, launches)
+
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    step(first + i, launches)
+        torch.cuda.synchronize()
+        g.replay()
+        flush()
+        torch.cuda.synchronize()
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b), "graph replay"
+    flush()
+    torch.cuda.synchronize()
     a.record(stream)
-    g.replay()
+    for i in range(steps):
+        step(first + i, launches)
     b.record(stream)
     torch.cuda.synchronize()
-    return a.elapsed_time(b)
+    return a.elapsed_time(b), "eager launches"
 
 
 # ---------------------------------------------------------------------------
@@ -303,7 +315,9 @@ def setup_moe(torch, tg, inputs, wl, dev, code_id):
                       mfma=False, units="token (24 GEMVs, 2 launches)")
 
 
-def run_gpu(workload, steps, warmup, use_graph, code_id=0):
+
+
+def run_gpu(workload, steps, warmup, use_graph, code_id=0, hot=True):
     """Time `steps` steps of the workload. Returns (info, timings).
 
     region_ms: the timed region (all launches of K steps, graph replay unless disabled).
@@ -320,40 +334,26 @@ def run_gpu(workload, steps, warmup, use_graph, code_id=0):
              6: setup_prefill, 7: setup_moe_block}[workload]
     step, info = setup(torch, tg, inputs, wl, dev, code_id)
     dom = max(info["names"], key=lambda k: info["alg_bytes"][k])     # kernel moving the most bytes
-    stream = torch.cuda.current_stream()
+    copies = info["copies"]
     for i in range(warmup):
         step(i, Launches())
     torch.cuda.synchronize()
-
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        step(i, Launches())
-    t1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = t0.elapsed_time(t1)
-
-    region_ms, dom_ms, timing = eager_ms, None, "eager launches"
+    eager_ms, _ = timed_steps_ms(torch, step, warmup, steps, copies, Launches(), False)
+    region_ms, timing = eager_ms, "eager launches"
+    dom_ms = None
     if use_graph:
         try:
-            region_ms = graph_time_ms(torch, step, steps, Launches())
-            dom_ms = graph_time_ms(torch, step, steps, Launches(only=dom))
-            timing = "graph replay"
+            region_ms, timing = timed_steps_ms(torch, step, warmup, steps, copies, Launches(), True)
+            dom_ms, _ = timed_steps_ms(torch, step, warmup, steps, copies, Launches(only=dom), True)
         except Exception as e:  # noqa: BLE001 - keep the eager number
             log("graph replay unavailable:", repr(e))
     if dom_ms is None:
-        t0.record(stream)
-        for i in range(steps):
-            step(i, Launches(only=dom))
-        t1.record(stream)
-        torch.cuda.synchronize()
-        dom_ms = t0.elapsed_time(t1)
+        dom_ms, _ = timed_steps_ms(torch, step, warmup, steps, copies, Launches(only=dom), False)
     # Context only, never the metric: the same copy every step (its code words stay in the caches).
     hot_ms = None
-    if timing == "graph replay":
-        hot_ms = graph_time_ms(torch, lambda i, launches: step(0, launches), steps, Launches())
-    return info, dict(region_ms=region_ms, eager_ms=eager_ms, dom=dom, dom_ms=dom_ms, timing=timing, hot_ms=hot_ms,
-                      stream_read_gbs=stream_read_gbs(torch))
+    if hot and timing == "graph replay":
+        hot_ms, _ = timed_steps_ms(torch, lambda i, launches: step(0, launches), 0, steps, 1, Launches(), True)
+    return info, dict(region_ms=region_ms, eager_ms=eager_ms, dom=dom, dom_ms=dom_ms, timing=timing, hot_ms=hot_ms)
 
 
 def stream_read_gbs(torch, nbytes=1 << 30, reps=5):
@@ -373,6 +373,28 @@ def stream_read_gbs(torch, nbytes=1 << 30, reps=5):
     return round(nbytes / (best * 1e-3) / 1e9, 1)
 
 
+def decode_ceiling(k_bits, code_id):
+    """Decoded weights per second of the decode-only probe (the batch-1 loop on LDS-resident code words):
+    the best of 256, 512 and 1024 workgroups of 8 waves (2, 4 and 8 waves per SIMD)."""
+    import torch
+    from trellis_coded_gemv_amd import binding as tg
+    steps = 256
+    best = None
+    for wgs in (256, 512, 1024):
+        out = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+        tg.decode_ceiling(k_bits, code_id, wgs, steps, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            tg.decode_ceiling(k_bits, code_id, wgs, steps, out)
+        b.record()
+        torch.cuda.synchronize()
+        rate = 5 * wgs * 512 * 64 * steps / (a.elapsed_time(b) * 1e-3)
+        best = rate if best is None or rate > best else best
+    return best
+
+
 def workload_of(inputs, workload):
     """Workload 7 runs the experts of workload 5 as whole MoE blocks."""
     return inputs.WORKLOADS[5 if workload == 7 else workload]
@@ -389,124 +411,162 @@ def _moe_token(inputs, wl, code_id, t=0):
     return gu, dn, sel, w, inputs.make_x(wl.hidden, wl.seed, tensor=10_000 + t)
 
 
-def moe_block_parity(inputs, wl, code_id):
-    """Token 0 through the whole block (all experts on the device, copy 0) against the oracle's block."""
-    import torch
-    from oracle import moe
-    from trellis_coded_gemv_amd import binding as tg
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, on a bounded sample of the workload, on every core of the
+# process's affinity mask (one worker process per core, forked before the GPU is touched).
+# ---------------------------------------------------------------------------
 
-    gu, dn, sel, w, x = _moe_token(inputs, wl, code_id)
-    gut = tg.LayerTable([tg.DeviceLayer(wl.layer(e, k, code_id=code_id), "cuda") for e in range(wl.experts)
-                         for k in ("gate", "up")], "cuda")
-    dnt = tg.LayerTable([tg.DeviceLayer(wl.layer(e, "down", code_id=code_id), "cuda") for e in range(wl.experts)],
-                        "cuda")
-    y = tg.trellis_moe_block(gut, dnt, torch.from_numpy(sel).to("cuda"), torch.from_numpy(w).to("cuda"),
-                             tg.fp16_tensor(x, "cuda"))
-    torch.cuda.synchronize()
-    ref = moe.moe_block(gu, dn, sel, w, x)
-    return float(np.abs(y.cpu().numpy() - ref).max() / np.abs(ref).max())
+_CPU_JOB = {}
 
 
-def parity_spot_check(workload, code_id=0):
-    """Copy 0 of the workload against the oracle on sampled outputs (after timing)."""
-    import torch
+def _cpu_item(item):
+    """One unit of oracle work: (kind, key, ...). Returns (code bytes, oracle output)."""
     from oracle import gemv as ogemv
-    from trellis_coded_gemv_amd import binding as tg
-    from trellis_coded_gemv_amd import inputs
-
-    wl = workload_of(inputs, workload)
-    if workload == 7:
-        return moe_block_parity(inputs, wl, code_id)
-    if workload == 5:
-        e, which = int(wl.routing()[0][0]), "gate"
-        arr, x = wl.layer(e, which, code_id=code_id), inputs.make_x(wl.hidden, wl.seed, tensor=10_000)
-        rows, M = np.arange(0, wl.inter, 5), 1
-    else:
-        name = list(wl.tensors)[-1]
-        m, n, k = wl.tensors[name]
-        ti = list(wl.tensors).index(name)
-        arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
-        M = wl.batch
-        x = inputs.make_x(n, wl.seed, tensor=ti, rows=M)
-        rows = np.concatenate([np.arange(0, 128, 7), np.arange(m - 128, m, 11)])
-    L = tg.DeviceLayer(arr, "cuda")
-    if M == 1:
-        y = tg.trellis_gemv(L, tg.fp16_tensor(x, "cuda"))[None, :]
-        ref = ogemv.gemv_rows(arr, x, rows)[None, :]
-    elif workload == 6:
-        y = tg.trellis_gemm_prefill(L, tg.fp16_tensor(x, "cuda"))
-        ref = ogemv.gemm_rows(arr, x[:2], rows)
-    else:
-        y = tg.trellis_gemm_small(L, tg.fp16_tensor(x, "cuda"))
-        ref = ogemv.gemm_rows(arr, x[:2], rows)
-    torch.cuda.synchronize()
-    y = y.cpu().numpy()[: ref.shape[0], rows]
-    return float(np.abs(y - ref).max() / np.abs(ref).max())
-
-
-def cpu_baseline(workload, sample_blocks, code_id=0):
-    """The oracle, untuned, on a bounded sample of the workload, scaled to the same unit (GB/s of codes)."""
-    from threadpoolctl import threadpool_limits
-    from oracle import gemv as ogemv
-    from trellis_coded_gemv_amd import inputs
-
-    wl = workload_of(inputs, workload)
-    if workload == 7:
+    kind = item[0]
+    if kind == "block":                      # one 128-output block of a tensor, all its activation rows
+        _, name, b = item
+        arr, X = _CPU_JOB["layers"][name]
+        rows = np.arange(128 * b, 128 * b + 128)
+        y = ogemv.gemv_rows(arr, X, rows) if X.ndim == 1 else ogemv.gemm_rows(arr, X, rows)
+        return 128 * arr.n * arr.k_bits // 8, y
+    if kind == "token":                      # a whole MoE block (workload 7) or its 24 GEMVs (workload 5)
         from oracle import moe
-        dt, nbytes, ntok = 0.0, 0, 0
-        while ntok < wl.tokens and dt < 10.0:   # whole tokens, about 10 s of oracle work
-            gu, dn, sel, w, x = _moe_token(inputs, wl, code_id, ntok)
-            with threadpool_limits(limits=1):
-                t = time.perf_counter()
-                moe.moe_block(gu, dn, sel, w, x)
-                dt += time.perf_counter() - t
-            nbytes += sum(a.code_bytes for a in list(gu.values()) + list(dn.values()))
-            ntok += 1
-        sample = f"tokens 0..{ntok - 1}: the whole block over each token's {wl.top_k} experts ({nbytes} code bytes), {dt:.1f} s"
-        rate = nbytes / dt
-    elif workload == 5:
-        arrs = [wl.layer(int(e), w, code_id=code_id) for e in wl.routing()[0][:2] for w in ("gate", "up", "down")]
-        xs = [inputs.make_x(a.n, 1) for a in arrs]
-        with threadpool_limits(limits=1):
-            t = time.perf_counter()
-            for a, x in zip(arrs, xs):
-                ogemv.gemv(a, x)
-            dt = time.perf_counter() - t
-        nbytes = sum(a.code_bytes for a in arrs)
-        sample = f"gate/up/down of 2 experts (6 full GEMVs, {nbytes} code bytes), {dt:.1f} s"
-        rate = nbytes / dt
+        _, t = item
+        gu, dn, sel, w, x, xd = _CPU_JOB["tokens"][t]
+        nbytes = sum(a.code_bytes for a in list(gu.values()) + list(dn.values()))
+        if _CPU_JOB["block"]:
+            return nbytes, moe.moe_block(gu, dn, sel, w, x)
+        ys = [ogemv.gemv(gu[2 * int(e) + k], x) for e in sel for k in (0, 1)]
+        ys += [ogemv.gemv(dn[int(e)], xd[i]) for i, e in enumerate(sel)]
+        return nbytes, ys[0]
+    raise ValueError(kind)
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(workload, code_id=0, blocks_per_tensor=32, tokens=16, max_workers=16):
+    """Time the oracle on a sample of the workload with one process per core of the affinity mask
+    (at most max_workers). Returns (baseline record, oracle outputs for the parity spot check)."""
+    import multiprocessing as mp
+    from trellis_coded_gemv_amd import inputs
+
+    wl = workload_of(inputs, workload)
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, max_workers))
+    _CPU_JOB.clear()
+    if workload in (5, 7):
+        _CPU_JOB["block"] = workload == 7
+        _CPU_JOB["tokens"] = {}
+        for t in range(min(tokens, wl.tokens)):
+            gu, dn, sel, w, x = _moe_token(inputs, wl, code_id, t)
+            xd = inputs.make_x(wl.inter, wl.seed, tensor=20_000 + t, rows=wl.top_k)
+            _CPU_JOB["tokens"][t] = (gu, dn, sel, w, x, xd)
+        items = [("token", t) for t in _CPU_JOB["tokens"]]
+        what = f"{len(items)} tokens, {'the whole block' if workload == 7 else 'their 24 expert GEMVs'} each"
+        scale = 1.0
     else:
-        name = max(wl.tensors, key=lambda k: wl.tensors[k][0] * wl.tensors[k][1])
-        m, n, k = wl.tensors[name]
-        ti = list(wl.tensors).index(name)
+        _CPU_JOB["layers"] = {}
+        items = []
+        Mo = min(wl.batch, 16)               # oracle rows per block; the rate is scaled to the step's rows
+        for ti, (name, (m, n, k)) in enumerate(wl.tensors.items()):
+            arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
+            X = inputs.make_x(n, wl.seed, tensor=ti, rows=Mo)
+            _CPU_JOB["layers"][name] = (arr, X)
+            nb = m // 128
+            blocks = np.unique(np.linspace(0, nb - 1, min(blocks_per_tensor, nb)).astype(int))
+            items += [("block", name, int(b)) for b in blocks]
+        what = (f"{len(items)} 128-output blocks over the tensors {', '.join(wl.tensors)}"
+                f" (decode + fp64 GEMV{'' if Mo == 1 else f' of {Mo} rows, scaled to {wl.batch}'})")
+        scale = wl.batch / Mo
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(_cpu_item, items[:workers], chunksize=1)     # warm-up: workers started, code paged in
+        t0 = time.perf_counter()
+        res = pool.map(_cpu_item, items, chunksize=1)
+        dt = time.perf_counter() - t0
+    nbytes = sum(r[0] for r in res)
+    rate = nbytes / (dt * scale)
+    rec = {"value": round(rate / 1e9, 6), "unit": "GB/s", "cores": workers, "kind": "oracle",
+           "sample": f"{what}: {nbytes} code bytes in {dt:.1f} s wall on {workers} worker processes",
+           "affinity_cores": affinity, "cpu_count": os.cpu_count(), "cpu_model": _cpu_model()}
+    refs = {item: r[1] for item, r in zip(items, res)}
+    _CPU_JOB.clear()
+    return rec, refs
+
+
+def parity_spot_check(workload, code_id, refs):
+    """Copy 0 of the workload on the GPU against the oracle outputs the CPU baseline computed
+    (a few of its sampled blocks or tokens); max |dy| / max |y_ref| over them."""
+    import torch
+    from trellis_coded_gemv_amd import binding as tg
+    from trellis_coded_gemv_amd import inputs
+
+    wl = workload_of(inputs, workload)
+    errs = []
+    if workload in (5, 7):
+        t = 0
+        ref = refs[("token", t)]
+        gu, dn, sel, w, x = _moe_token(inputs, wl, code_id, t)
+        if workload == 7:
+            gut = tg.LayerTable([tg.DeviceLayer(wl.layer(e, k, code_id=code_id), "cuda") for e in range(wl.experts)
+                                 for k in ("gate", "up")], "cuda")
+            dnt = tg.LayerTable([tg.DeviceLayer(wl.layer(e, "down", code_id=code_id), "cuda")
+                                 for e in range(wl.experts)], "cuda")
+            y = tg.trellis_moe_block(gut, dnt, torch.from_numpy(sel).to("cuda"), torch.from_numpy(w).to("cuda"),
+                                     tg.fp16_tensor(x, "cuda"))
+        else:
+            y = tg.trellis_gemv(tg.DeviceLayer(gu[2 * int(sel[0])], "cuda"), tg.fp16_tensor(x, "cuda"))
+        torch.cuda.synchronize()
+        return float(np.abs(y.cpu().numpy() - ref).max() / np.abs(ref).max())
+    by_tensor = {}
+    for item, y in refs.items():
+        by_tensor.setdefault(item[1], []).append((item[2], y))
+    for ti, (name, (m, n, k)) in enumerate(wl.tensors.items()):
         arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
-        M = wl.batch
-        Mo = min(M, 16)                        # oracle rows timed; scaled to the M rows of a step
-        X = inputs.make_x(n, wl.seed, tensor=ti, rows=Mo) if Mo > 1 else inputs.make_x(n, wl.seed, tensor=ti)
-        nb = m // 128
-        nblk = max(1, sample_blocks // Mo)
-        blocks = np.linspace(0, nb - 1, min(nblk, nb)).astype(int)
-        rows = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
-        def one_pass():
-            if Mo == 1:
-                ogemv.gemv_rows(arr, X, rows)
-            else:
-                ogemv.gemm_rows(arr, X, rows)
-        with threadpool_limits(limits=1):
-            one_pass()                         # warm-up pass, not timed
-            passes, total = 0, 0.0
-            while passes < 8 and (passes == 0 or total < 10.0):   # whole passes, about 10 s in all
-                t = time.perf_counter()
-                one_pass()
-                total += time.perf_counter() - t
-                passes += 1
-        dt = total / passes
-        nbytes = len(rows) * n * k // 8
-        sample = (f"{len(blocks)} of {nb} 128-output blocks of the {m}x{n} K={k} '{name}' tensor"
-                  f"{'' if M == 1 else f' x {Mo} rows'} (decode + fp64 GEMV), {passes} timed pass(es) of {dt:.1f} s"
-                  f"{'' if Mo == M else f', scaled to {M} rows'}")
-        rate = nbytes / (dt * M / Mo)
-    return {"value": round(rate / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}
+        Mo = min(wl.batch, 16)
+        X = inputs.make_x(n, wl.seed, tensor=ti, rows=Mo)
+        L = tg.DeviceLayer(arr, "cuda")
+        if wl.batch == 1:
+            Y = tg.trellis_gemv(L, tg.fp16_tensor(X, "cuda"))[None, :]
+        elif workload == 6:
+            Y = tg.trellis_gemm_prefill(L, tg.fp16_tensor(X, "cuda"))
+        else:
+            Y = tg.trellis_gemm_small(L, tg.fp16_tensor(X, "cuda"))
+        torch.cuda.synchronize()
+        Y = Y.cpu().numpy()
+        for b, ref in by_tensor.get(name, []):
+            ref = np.atleast_2d(ref)
+            got = Y[:, 128 * b:128 * b + 128]
+            errs.append(float(np.abs(got - ref).max() / np.abs(ref).max()))
+    return max(errs) if errs else None
+
+
+def measure(workload, code_id, steps, warmup, use_graph, hot=True):
+    """One workload's timing record (no CPU baseline)."""
+    from trellis_coded_gemv_amd import inputs
+    wl = workload_of(inputs, workload)
+    info, t = run_gpu(workload, steps, warmup, use_graph, code_id, hot)
+    ms_per_step = t["region_ms"] / steps
+    value = info["code_bytes"] / (ms_per_step * 1e-3) / 1e9
+    dom = t["dom"]
+    dom_launch_ms = t["dom_ms"] / steps
+    rec = {"workload": wl.name + ("_block" if workload == 7 else ""), "code_id": code_id, "units": info["units"],
+           "us_per_step": round(ms_per_step * 1e3, 3), "gbs": round(value, 2),
+           "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
+           "dominant": dom, "dominant_launch_us": round(dom_launch_ms * 1e3, 3)}
+    if "flops" in info:
+        tf = info["flops"] / (dom_launch_ms * 1e-3) / 1e12
+        rec["mfma_tflops"] = round(tf, 2)
+        rec["mfma_frac_of_dense_f16_peak"] = round(tf / MFMA_F16_PEAK_TFLOPS, 5)
+    return info, t, rec, value, ms_per_step, dom_launch_ms
 
 
 def main(argv=None):
@@ -514,11 +574,14 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--code", type=int, default=0, choices=[0, 1],
                     help="code_id of every layer: 0 the three-instruction code, 1 the pair code")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=32, help="oracle sample size in 128-output blocks (0: skip)")
+    ap.add_argument("--cpu-blocks", type=int, default=32,
+                    help="oracle sample: 128-output blocks per tensor (tokens for workloads 5/7); 0 skips it")
+    ap.add_argument("--context", default="2,4,5",
+                    help="comma-separated workloads also measured briefly as context ('' for none)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="after timing, write (fill) and read (sum) this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -527,65 +590,79 @@ def main(argv=None):
               file=sys.stderr)
         return 2
 
+    # the CPU baseline runs first: its worker processes are forked before anything touches the GPU
+    cpu, refs = (None, None)
+    if args.cpu_blocks > 0:
+        log("cpu baseline (oracle) ...")
+        cpu, refs = cpu_baseline(args.workload, args.code, blocks_per_tensor=args.cpu_blocks,
+                                 tokens=min(args.cpu_blocks, 16))
+        log("cpu baseline:", cpu["value"], "GB/s on", cpu["cores"], "workers")
+
+    import torch
+    from trellis_coded_gemv_amd import binding as tg
     from trellis_coded_gemv_amd import inputs
     wl = workload_of(inputs, args.workload)
-    info, t = run_gpu(args.workload, args.steps, args.warmup, not args.no_graph, args.code)
     steps = args.steps
-    ms_per_step = t["region_ms"] / steps
-    value = info["code_bytes"] / (ms_per_step * 1e-3) / 1e9
+    info, t, rec, value, ms_per_step, dom_launch_ms = measure(args.workload, args.code, steps, args.warmup,
+                                                              not args.no_graph)
     dom = t["dom"]
-    dom_launch_ms = t["dom_ms"] / steps
     achieved = info["alg_bytes"][dom] / (dom_launch_ms * 1e-3) / 1e9
-    opw = alu_ops_per_weight(args.code, info["mfma"])
-    alg_ops = info["weights"][dom] * opw
-    alu_achieved = alg_ops / (dom_launch_ms * 1e-3) / 1e12
-    config = {"workload": wl.name + ("_block" if args.workload == 7 else ""), "units": info["units"], "code_bytes_per_step": int(info["code_bytes"]),
-              "copies": info["copies"], "us_per_step": round(ms_per_step * 1e3, 3),
-              "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
+    config = {"workload": rec["workload"], "units": info["units"], "code_bytes_per_step": int(info["code_bytes"]),
+              "copies": info["copies"], "us_per_step": rec["us_per_step"],
+              "pct_of_hbm_peak": rec["pct_of_hbm_peak"], "timing": t["timing"],
               "eager_us_per_step": round(t["eager_ms"] / steps * 1e3, 3),
-              "context": {"hot_cache_us_per_step": None if t["hot_ms"] is None else round(t["hot_ms"] / steps * 1e3, 3),
-                          "stream_read_gbs": t["stream_read_gbs"],
-                          "note": "hot: copy 0 every step (caches warm); stream_read: torch.sum over 1 GiB (fp64 view)"},
-              "code_id": args.code, "parity_max_rel_err": parity_spot_check(args.workload, args.code)}
+              "code_id": args.code, "build_id": tg.build_id()}
     if args.workload not in (5, 7):
         config.update({"tensors": {k: list(v) for k, v in wl.tensors.items()}, "batch": wl.batch})
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload, dom, args.code),
+            "algorithmic_bytes": int(info["alg_bytes"][dom]), "launch_us": round(dom_launch_ms * 1e3, 3)}
+    if not info["mfma"]:
+        k_dom = wl.tensors[dom][2] if args.workload not in (5, 7) else 2
+        ceil = decode_ceiling(k_dom, args.code)
+        wps = info["weights"][dom] / (dom_launch_ms * 1e-3)
+        roof["alu"] = {"achieved": round(wps / 1e9, 2), "ceiling": round(ceil / 1e9, 2), "unit": "G weights/s",
+                       "frac": round(wps / ceil, 4), "ceiling_kernel": f"tg_decode_ceiling(k_bits={k_dom}, "
+                                                                    f"code_id={args.code})"}
+    if "flops" in info:
+        tf = info["flops"] / (dom_launch_ms * 1e-3) / 1e12
+        roof["mfma"] = {"achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 5)}
+    if info.get("prefill"):
+        # decode once + dense GEMM: the contraction is the roofline here
+        mf = roof.pop("mfma")
+        hbm = {k: roof.pop(k) for k in ("achieved", "peak", "unit", "frac", "algorithmic_bytes")}
+        roof.update({"bound": "mfma", "achieved": mf["achieved"], "peak": mf["peak"], "unit": "TFLOP/s",
+                     "frac": mf["frac"], "algorithmic_flops": info["flops"], "hbm": hbm})
+    config["context"] = {
+        "hot_cache_us_per_step": None if t["hot_ms"] is None else round(t["hot_ms"] / steps * 1e3, 3),
+        "stream_read_gbs": stream_read_gbs(torch),
+        "note": "hot: copy 0 every step (caches warm); stream_read: torch.sum over 1 GiB (fp64 view)"}
+    if refs is not None:
+        config["parity_max_rel_err"] = parity_spot_check(args.workload, args.code, refs)
+    others = []
+    for w in [int(v) for v in args.context.split(",") if v.strip()]:
+        if w == args.workload:
+            continue
+        log("context workload", w)
+        _, _, r, _, _, _ = measure(w, args.code, min(steps, 50), 5, not args.no_graph, hot=False)
+        others.append(r)
+    config["other_workloads"] = others
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic", "config": config,
-        "roofline": {"bound": "alu", "kernel": dom, "achieved": round(alu_achieved, 3), "peak": round(ALU_PEAK_TOPS, 3),
-                     "unit": "T lane-ops/s", "frac": round(alu_achieved / ALU_PEAK_TOPS, 4),
-                     "traffic": recorded_traffic(args.workload, dom, args.code),
-                     "algorithmic_ops": int(alg_ops), "ops_per_weight": opw,
-                     "launch_us": round(dom_launch_ms * 1e3, 3),
-                     "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(achieved / HBM_PEAK_GBS, 4),
-                             "algorithmic_bytes": int(info["alg_bytes"][dom])}},
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic", "config": config, "roofline": roof,
     }
-    if "flops" in info:
-        tf = info["flops"] / (dom_launch_ms * 1e-3) / 1e12
-        out["roofline"]["mfma"] = {"achieved_tflops": round(tf, 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
-                                   "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 5)}
-    if info.get("prefill"):
-        # decode once + dense GEMM: the contraction is the roofline here
-        mf = out["roofline"].pop("mfma")
-        alu = {k: out["roofline"].pop(k) for k in ("achieved", "peak", "unit", "frac", "algorithmic_ops",
-                                                   "ops_per_weight")}
-        out["roofline"].update({"bound": "mfma", "achieved": mf["achieved_tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
-                                "unit": "TFLOP/s", "frac": mf["frac"], "algorithmic_flops": info["flops"],
-                                "alu": alu})
     if args.copy_calib_mb > 0:
         # counter calibration: a pure write (fill) and a pure read (sum) of known size
-        import torch
         buf = torch.empty(args.copy_calib_mb << 18, dtype=torch.float32, device="cuda")
         for _ in range(3):
             buf.fill_(1.0)
             buf.sum()
         torch.cuda.synchronize()
         out["config"]["calibration_bytes"] = buf.numel() * 4
-    if args.cpu_blocks > 0:
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_blocks, args.code)
-    out["config"]["csrc_sha"] = kernel_source_hash()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 

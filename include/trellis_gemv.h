@@ -51,7 +51,8 @@
  *     there (kept until the process ends; rocBLAS manages that handle's own
  *     device memory).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *     Work is enqueued asynchronously; the library never synchronises.
+ *     Work is enqueued asynchronously; the library never synchronises (except
+ *     tg_workspace_status, which has to wait for the word it reads).
  *   - Every argument is validated on the host before anything is enqueued; on
  *     error a negative tg_status is returned and nothing is enqueued. A failed
  *     launch returns TG_ERR_LAUNCH. No exception crosses the ABI.
@@ -59,11 +60,12 @@
  *   - Results are bitwise deterministic for identical inputs and launch
  *     configuration.
  *   - Calls that share a workspace must not run concurrently.
- *   - Environment (tuning aids, read on every call, including by the
- *     workspace-size queries): TG_SPLITK=S (S > 0) forces S input chunks on
- *     the batch-1 and grouped paths, TG_SPLITK_MFMA=S on the small-batch
- *     path. A workspace sized under one setting can be too small under
- *     another; the call then returns TG_ERR_WORKSPACE.
+ *   - The workspaces of trellis_gemv, trellis_gemm_small, trellis_gemv_grouped
+ *     and trellis_moe_block start with a 256-byte header whose first 32-bit
+ *     word is the status word: sticky TG_STATUS_* bits the kernels set and
+ *     tg_workspace_status() reads (zero-filling a workspace clears it).
+ *   - The library reads no environment variables; the only tuning input is a
+ *     layer's `splits` field, which the workspace-size queries see as well.
  */
 #ifndef TRELLIS_GEMV_H
 #define TRELLIS_GEMV_H
@@ -75,7 +77,7 @@
 extern "C" {
 #endif
 
-#define TG_ABI_VERSION 1
+#define TG_ABI_VERSION 2
 
 typedef enum tg_status {
   TG_OK = 0,
@@ -89,6 +91,10 @@ typedef enum tg_status {
   TG_ERR_ARG = -8         /* any other invalid argument (stride, flags, index range)   */
 } tg_status;
 
+/* Status word bits (sticky; see tg_workspace_status). */
+#define TG_STATUS_SPLITK_TIMEOUT 1u  /* a split-K reducer's bounded wait (about a second) ran out;
+                                        the outputs of that block were written as NaN */
+
 /* Layer flags. */
 #define TG_FLAG_ROUND_WEIGHTS 1  /* GEMV paths round each weight to fp16 before the product
                                     (the default adds the two fp16 halves inside the fp32
@@ -101,7 +107,10 @@ typedef struct tg_layer {
   int32_t k_bits;            /* bits per weight K, 1..8 (lecture, Part eleven)              */
   int32_t code_id;           /* 0 = the three-instruction code; 1 = the pair code            */
   int32_t flags;             /* TG_FLAG_*                                                  */
-  int32_t reserved;          /* must be 0                                                  */
+  int32_t splits;            /* input chunks (split-K) of the batch-1, grouped and          *
+                              * small-batch paths: 0 = the library's choice; S > 0 forces  *
+                              * S (a tuning aid; clamped to what the path supports); at   *
+                              * most 65535. Layers of one grouped table share it.          */
   const uint32_t *codes;     /* device, (m/16)*(n/16)*8*K words, 16-byte aligned            */
   const uint16_t *scales;    /* device, m fp16 patterns, 2-byte aligned                     */
   const uint32_t *sign_in;   /* device, ceil(n/32) words                                   */
@@ -111,13 +120,29 @@ typedef struct tg_layer {
 /* ABI version of the loaded library (TG_ABI_VERSION it was built with). */
 int32_t tg_abi_version(void);
 
+/* Identifier of the sources the library was built from (a hash of its HIP sources and this
+ * header, set at build time), so a binding can refuse a library older than its sources. */
+const char *tg_build_id(void);
+
+/*
+ * Read a workspace's status word (TG_STATUS_* bits set by kernels that used it since it
+ * was last cleared): enqueues a 4-byte device-to-host copy on `stream` and waits for the
+ * stream, so every call enqueued before it has finished. clear != 0 then enqueues a reset
+ * of the word to zero (only when it was non-zero). Not for use inside graph capture.
+ *   ws     : device workspace of trellis_gemv, trellis_gemm_small, trellis_gemv_grouped
+ *            or trellis_moe_block, 256-byte aligned.
+ *   status : host, receives the word.
+ * Returns TG_OK, or TG_ERR_LAUNCH if the runtime reports an error.
+ */
+int32_t tg_workspace_status(void *ws, int32_t clear, uint32_t *status, void *stream);
+
 /* Human-readable name of a status code. Never NULL. */
 const char *tg_status_str(int32_t status);
 
 /*
  * Workspace bytes needed by trellis_gemv (M == 1) or trellis_gemm_small
  * (1 <= M <= 64) for this layer, or 0 if the layer / M is invalid.
- * Layout, at the same offsets for every layer: two counter areas (256 KiB in
+ * Layout, at the same offsets for every layer: the 256-byte header, two counter areas (256 KiB in
  * all: the batch-1 tickets and the small-batch arrival counters, each sized
  * for the largest layer), the batch-1 split-K slots (2 MiB), then the
  * small-batch scratch (input transform, split-K partials). It must be
@@ -217,15 +242,17 @@ int32_t rht_apply(int32_t n, int32_t rows, const uint16_t *in, float *out,
  *   ws        : device workspace, ws_bytes >= tg_grouped_workspace_size(...),
  *               zero-filled before its first use; every call leaves its ticket
  *               counters on a call boundary (as for trellis_gemv), and calls
- *               that share it must be ordered (one stream). Its first n_sel *
- *               (largest m / 128) words are ticket counters and its split-K slots
- *               follow, so a workspace used before with another n_sel or largest
- *               m must be zero-filled again (one geometry's slots lie where
- *               another keeps its counters).
+ *               that share it must be ordered (one stream). After the 256-byte
+ *               header, n_sel * (largest m / 128) words are ticket counters and
+ *               the split-K slots follow, so a workspace used before with another
+ *               n_sel or largest m must be zero-filled again (one geometry's slots
+ *               lie where another keeps its counters).
  * Every layer's n must fit the input stride (n <= x_stride when x_stride != 0)
  * and m <= y_stride. Indices in d_sel outside [0, n_layers) make the affected
  * selection write nothing. n_sel * (max m / 128) * (max n / 128) must stay
- * below 2^31 (TG_ERR_SHAPE otherwise).
+ * below 2^31 (TG_ERR_SHAPE otherwise). The launch's split count S comes from
+ * the widest layer of the table (or the layers' common `splits` field); a
+ * selected layer with fewer than S 128-blocks of input runs one chunk per block.
  */
 int32_t trellis_gemv_grouped(const tg_layer *layers, const tg_layer *d_layers, int32_t n_layers,
                              const int32_t *d_sel, int32_t n_sel,
@@ -273,7 +300,11 @@ size_t tg_moe_workspace_size(const tg_layer *gate_up, int32_t n_gate_up,
 
 /*
  * Decode the whole layer to fp16 weights (test / export hook): w_out[o*n + i]
- * = W^[o, i] as fp16 patterns, bit-exact with the code's definition. Only
+ * = W^[o, i] as fp16 patterns, bit-exact with the code's definition: every
+ * weight's state is the 16-bit window of its tile's circular stream at bit K*t
+ * (lecture, Part eight: random access into the bitshift trellis, 16x16 tiles,
+ * tail-biting), put through the computed code (lecture, Part nine; code_id 1:
+ * Deep Dive, Section 3, a V = 2 step per state). Only
  * codes, k_bits, code_id and shape are used; m, n need only be positive
  * multiples of 16, and m*n <= 2^38 (TG_ERR_SHAPE beyond: 512 GiB of output).
  *   w_out : device, m*n uint16.
@@ -281,12 +312,30 @@ size_t tg_moe_workspace_size(const tg_layer *gate_up, int32_t n_gate_up,
 int32_t trellis_decode(const tg_layer *layer, uint16_t *w_out, void *stream);
 
 /*
- * The whole code as a table, for every state S < 65536:
+ * The whole computed code as a table (test / export hook; lecture, Part nine:
+ * each state's weight is a function of the 16-bit state alone, so the code has
+ * exactly 2^16 entries), for every state S < 65536:
  *   code_id 0: out[S] = fp16 pattern of the weight for state S  (65536 entries);
  *   code_id 1: out[2S], out[2S+1] = the state's weight pair      (131072 entries).
  *   out : device, 2-byte aligned.
  */
 int32_t tg_code_table(int32_t code_id, uint16_t *out, void *stream);
+
+/*
+ * Decode-only rate probe (measurement hook): runs the batch-1 kernel's per-step
+ * loop -- x~ words from LDS, the quad rotate, window extraction, computed code
+ * and fused dot product of 64 weights per lane -- on code words held in LDS, so
+ * no HBM traffic is involved. Its rate is the VALU ceiling of trellis_gemv for
+ * this K and code (lecture, Part three: the decode's integer-instruction budget
+ * per weight; Part eleven: the same decode is compute-bound on data-centre
+ * cards). workgroups of 512 threads (8 waves) each run `steps` steps, i.e.
+ * decode workgroups * 512 * 64 * steps weights.
+ *   k_bits     : 1..8;  code_id : 0 or 1.
+ *   workgroups : 1..65535;  steps : 1..2^20.
+ *   out        : device, workgroups * 512 fp32 (one per thread, keeps the work live).
+ */
+int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t workgroups, int32_t steps, float *out,
+                          void *stream);
 
 /*
  * Tail-biting Viterbi encoder (offline conversion; lecture, Part seven: the

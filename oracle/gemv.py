@@ -82,21 +82,25 @@ def gemv_dense(layer, x_bits: np.ndarray) -> np.ndarray:
 
 
 def gemv_rows(layer, x_bits: np.ndarray, rows) -> np.ndarray:
-    """y at the listed output indices only, decoding just the 128-row blocks they fall in."""
+    """y at the listed output indices only, decoding just the 128-row blocks they fall in.
+
+    x_bits is one vector [n] (result [len(rows)]) or a batch [M, n] (result [M, len(rows)]);
+    each 128-row block is decoded once and applied to every vector of the batch.
+    """
     rows = np.asarray(rows)
     x = fp16.value(x_bits)
     xt = hadamard.rht_forward(x, layer.sign_in)
     g = scales(layer)
-    out = np.empty(len(rows))
+    s_out = hadamard.signs(layer.sign_out, layer.m)
+    out = np.empty(x.shape[:-1] + (len(rows),))
     for blk in np.unique(rows // hadamard.BLOCK):
         tr = np.arange(blk * 8, blk * 8 + 8)                      # 8 tile rows = 128 outputs
         W = weight_matrix(layer, tr)
         o = slice(blk * hadamard.BLOCK, (blk + 1) * hadamard.BLOCK)
-        yt = g[o] * (W @ xt)
-        s = hadamard.signs(layer.sign_out, layer.m)[o]
-        yb = s * hadamard.apply_blocks(yt)
+        yt = g[o] * (xt @ W.T)                                    # W^ x~ for every vector
+        yb = s_out[o] * hadamard.apply_blocks(yt)
         sel = rows // hadamard.BLOCK == blk
-        out[sel] = yb[rows[sel] % hadamard.BLOCK]
+        out[..., sel] = yb[..., rows[sel] % hadamard.BLOCK]
     return out
 
 
@@ -109,7 +113,7 @@ def gemm(layer, X_bits: np.ndarray, W: np.ndarray = None) -> np.ndarray:
 
 def gemm_rows(layer, X_bits: np.ndarray, rows) -> np.ndarray:
     """Batched form at sampled output indices. X [M, n] -> [M, len(rows)]."""
-    return np.stack([gemv_rows(layer, X_bits[i], rows) for i in range(X_bits.shape[0])])
+    return gemv_rows(layer, np.asarray(X_bits).reshape(-1, layer.n), rows)
 
 
 def grouped(layers, sel, X_bits: np.ndarray, shared_x: bool) -> list:

@@ -31,12 +31,37 @@ def rel_err(y, ref):
     return float(np.abs(y - ref).max() / np.abs(ref).max())
 
 
-def sample_rows(m, seed=0, blocks=3, per_block=16):
-    """Output indices from the first, last and a random 128-block (the oracle decodes only those)."""
+def sample_rows(m, seed=0, per_block=2):
+    """Output indices to check against the oracle: per_block random outputs in every 128-output block
+    (each block has its own split-K handoff; the oracle decodes only the tile rows it needs)."""
     rng = np.random.default_rng(seed)
-    nb = m // 128
-    chosen = sorted({0, nb - 1, int(rng.integers(0, nb))})[:blocks]
-    rows = []
-    for b in chosen:
-        rows += list(128 * b + np.sort(rng.choice(128, per_block, replace=False)))
-    return np.array(sorted(set(rows)))
+    rows = [128 * b + np.sort(rng.choice(128, per_block, replace=False)) for b in range(m // 128)]
+    return np.concatenate(rows)
+
+
+def _refs_module():
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "make_full_size_refs.py")
+    spec = importlib.util.spec_from_file_location("make_full_size_refs", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+_REFS = {}
+
+
+def full_size_case(key):
+    """(layer arrays, x bits, sampled output rows, checked activation rows or None, oracle y [rows x outputs])
+    of a full-size case whose oracle outputs tests/golden/make_full_size_refs.py stored."""
+    import json
+    mod = _refs_module()
+    if not _REFS:
+        z = np.load(mod.OUT, allow_pickle=False)
+        _REFS.update({k: z[k] for k in z.files})
+    meta = json.loads(str(_REFS["meta"]))
+    assert meta[key] == json.loads(json.dumps(mod.CASES[key])), f"stale reference for {key}: regenerate"
+    arr, X, rows, pick = mod.case_inputs(key)
+    assert np.array_equal(_REFS[key + "/rows"], rows)
+    return arr, X, rows, pick, _REFS[key + "/y"]

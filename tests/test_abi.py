@@ -23,7 +23,7 @@ def _declared_functions():
 
 
 def _layer(**kw):
-    d = dict(m=256, n=512, k_bits=2, code_id=0, flags=0, reserved=0, codes=A16, scales=A16, sign_in=A16,
+    d = dict(m=256, n=512, k_bits=2, code_id=0, flags=0, splits=0, codes=A16, scales=A16, sign_in=A16,
              sign_out=A16)
     d.update(kw)
     return tg.TgLayer(**d)
@@ -35,7 +35,9 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(tg.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.tg_abi_version() == 1
+    assert L.tg_abi_version() == 2
+    from trellis_coded_gemv_amd.build import source_hash
+    assert L.tg_build_id().decode() == source_hash()
 
 
 def test_struct_layout_matches_header():
@@ -52,7 +54,7 @@ def test_status_strings():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(k_bits=0), -3), (dict(k_bits=9), -3), (dict(m=100), -2), (dict(n=0), -2), (dict(m=-128), -2),
-    (dict(code_id=2), -6), (dict(code_id=-1), -6), (dict(flags=4), -8), (dict(reserved=1), -8), (dict(codes=0), -1),
+    (dict(code_id=2), -6), (dict(code_id=-1), -6), (dict(flags=4), -8), (dict(splits=-1), -8), (dict(splits=65536), -8), (dict(codes=0), -1),
     (dict(sign_out=0), -1), (dict(codes=A16 + 8), -4), (dict(scales=A16 + 1), -4), (dict(sign_in=A4 + 2), -4)])
 def test_gemv_layer_validation(kw, status):
     d = _layer(**kw)
@@ -218,3 +220,25 @@ def test_huge_shapes_rejected_before_launch():
     assert L.trellis_gemm_prefill(ctypes.byref(big), 16, A16, 1 << 22, A16, 1 << 22, A16, 1 << 40, None) == -2
     table = (tg.TgLayer * 1)(_layer(m=1 << 22, n=1 << 22))
     assert L.tg_grouped_workspace_size(table, 1, 65536) == 0
+
+
+def test_status_query_and_splits_validation():
+    L = tg.lib()
+    word = ctypes.c_uint32(7)
+    assert L.tg_workspace_status(None, 0, ctypes.byref(word), None) == -1
+    assert L.tg_workspace_status(A16, 0, None, None) == -1
+    assert L.tg_workspace_status(A16 + 16, 0, ctypes.byref(word), None) == -4
+    mixed = (tg.TgLayer * 2)(_layer(), _layer(splits=4))
+    assert L.tg_grouped_workspace_size(mixed, 2, 4) == 0          # a table shares one splits value
+    same = (tg.TgLayer * 2)(_layer(splits=4), _layer(splits=4))
+    assert L.tg_grouped_workspace_size(same, 2, 4) > 0
+
+
+def test_decode_ceiling_validation():
+    L = tg.lib()
+    assert L.tg_decode_ceiling(0, 0, 1, 1, A16, None) == -3
+    assert L.tg_decode_ceiling(2, 2, 1, 1, A16, None) == -6
+    assert L.tg_decode_ceiling(2, 0, 0, 1, A16, None) == -8
+    assert L.tg_decode_ceiling(2, 0, 1, 0, A16, None) == -8
+    assert L.tg_decode_ceiling(2, 0, 1, 1, 0, None) == -1
+    assert L.tg_decode_ceiling(2, 0, 1, 1, A16 + 2, None) == -4

@@ -8,10 +8,23 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_alu_roofline_constants():
-    assert abs(bench.ALU_PEAK_TOPS - 256 * 4 * 16 * 2.4e9 / 1e12) < 1e-9
-    assert bench.alu_ops_per_weight(0, False) == 4.0 and bench.alu_ops_per_weight(1, False) == 2.0
-    assert bench.alu_ops_per_weight(0, True) == 3.0 and bench.alu_ops_per_weight(1, True) == 1.5
+def test_headline_is_the_largest_batch1_workload():
+    """The bench's default workload is the 70B-shaped decoder layer (the largest batch-1 configuration),
+    whose roofline is the HBM one: 8 TB/s."""
+    from trellis_coded_gemv_amd import inputs
+    assert bench.DEFAULT_WORKLOAD == 3 and inputs.WORKLOADS[3].name == "decoder70b_layer_k2"
+    batch1 = [w for w in (1, 2, 3) if inputs.WORKLOADS[w].batch == 1]
+    codes = {w: sum(m * n * k // 8 for m, n, k in inputs.WORKLOADS[w].tensors.values()) for w in batch1}
+    assert max(codes, key=codes.get) == 3 and codes[3] == 213909504
+    assert bench.HBM_PEAK_GBS == 8000.0
+
+
+def test_cpu_baseline_uses_every_core_of_the_mask():
+    """The oracle sample runs one worker process per core of the affinity mask (at most 16)."""
+    rec, refs = bench.cpu_baseline(1, blocks_per_tensor=2, max_workers=16)
+    assert rec["cores"] == min(len(os.sched_getaffinity(0)), 16)
+    assert rec["affinity_cores"] == len(os.sched_getaffinity(0)) and rec["cpu_count"] == os.cpu_count()
+    assert rec["kind"] == "oracle" and rec["value"] > 0 and len(refs) == 2
 
 
 def test_algorithmic_bytes():
@@ -31,9 +44,11 @@ def test_recorded_traffic_only_for_the_sources_it_was_taken_on(monkeypatch):
     rec = json.load(open(bench.TRAFFIC_FILE))
     assert len(rec["csrc_sha"]) == 16 and bench.kernel_source_hash() == bench.kernel_source_hash()
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["csrc_sha"])
-    down = rec["workloads"]["2"]["down"]
-    assert bench.recorded_traffic(2, "down") == down["hbm_bytes_per_launch"]
+    key = sorted(rec["workloads"])[0]
+    kern = sorted(rec["workloads"][key])[0]
+    down = rec["workloads"][key][kern]
+    assert bench.recorded_traffic(int(key.split("/")[0]), kern) == down["hbm_bytes_per_launch"]
     assert down["hbm_bytes_per_launch"] == down["fetch_bytes_per_launch"] + down["write_bytes_per_launch"]
     assert bench.recorded_traffic(2, "no such launch") is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
-    assert bench.recorded_traffic(2, "down") is None
+    assert bench.recorded_traffic(int(key.split("/")[0]), kern) is None

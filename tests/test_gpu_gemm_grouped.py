@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from gpu_common import REL_TOL, device, rel_err, sample_rows, say
+from gpu_common import REL_TOL, device, full_size_case, rel_err, say
 from oracle import gemv as ogemv
 from trellis_coded_gemv_amd import binding as tg
 from trellis_coded_gemv_amd import inputs
@@ -61,16 +61,11 @@ def test_gemm_small_matches_gemv_row_by_row():
 def test_gemm_small_config4_sampled():
     """Gate projection 8192->28672 at K=4 with 16 activation rows, in the bench's launch configuration."""
     dev = device()
-    wl = inputs.CFG4
-    m, n, k = wl.tensors["gate"]
-    arr = inputs.make_layer(m, n, k, wl.seed)
-    X = inputs.make_x(n, wl.seed, rows=wl.batch)
+    arr, X, rows, _, ref = full_size_case("w4_gate_c0")
     say("gemm_small cfg4")
     Y = _gemm(arr, X, dev)
     assert np.isfinite(Y).all()
-    rows = sample_rows(m, seed=4, blocks=2, per_block=8)
-    ref = ogemv.gemm_rows(arr, X, rows)
-    for r in range(wl.batch):
+    for r in range(X.shape[0]):
         assert rel_err(Y[r, rows], ref[r]) <= REL_TOL, r
 
 
@@ -122,7 +117,7 @@ def test_grouped_workspace_reuse():
     Y1 = tg.trellis_gemv_grouped(dn_table, sel, X, wl.inter, torch.zeros(4, wl.hidden, device=dev), wl.hidden, ws)
     torch.cuda.synchronize()
     counters = 4 * (wl.hidden // 128) * 4                # one per selection and 128-output block
-    assert int((ws[:counters].view(torch.int32) & 0xFFFF).count_nonzero()) == 0
+    assert int((ws[256: 256 + counters].view(torch.int32) & 0xFFFF).count_nonzero()) == 0
     Y2 = tg.trellis_gemv_grouped(dn_table, sel, X, wl.inter, torch.zeros(4, wl.hidden, device=dev), wl.hidden, ws)
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
@@ -157,3 +152,26 @@ def test_gemm_small_long_chunks(M, code_id):
     ref = ogemv.gemm(arr, X)
     for r in range(M):
         assert rel_err(Y[r], ref[r]) <= REL_TOL, r
+
+
+@pytest.mark.parametrize("n_sel", [2, 8])
+def test_grouped_mixed_shapes(n_sel):
+    """One table mixing a 768x2048 and a 2048x768 layer (the launch's split count comes from the
+    wider input; the narrower layer runs one chunk per 128-block), every output checked."""
+    dev = device()
+    import torch
+    arrays = [inputs.make_layer(768, 2048, 2, 3400), inputs.make_layer(2048, 768, 3, 3401),
+              inputs.make_layer(768, 2048, 1, 3402, code_id=1), inputs.make_layer(2048, 768, 2, 3403)]
+    table = tg.LayerTable([tg.DeviceLayer(a, dev) for a in arrays], dev)
+    sel = np.array([(1, 0, 3, 2)[e % 4] for e in range(n_sel)], np.int32)
+    X = inputs.make_x(2048, 3404, rows=n_sel)
+    say("grouped mixed shapes", n_sel, list(sel))
+    Y = torch.full((n_sel, 2048), float("nan"), dtype=torch.float32, device=dev)
+    tg.trellis_gemv_grouped(table, torch.from_numpy(sel).to(dev), tg.fp16_tensor(X, dev), 2048, Y, 2048)
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    ref = ogemv.grouped(arrays, sel, X, shared_x=False)
+    for e, li in enumerate(sel):
+        m = arrays[li].m
+        assert rel_err(y[e, :m], ref[e]) <= REL_TOL, (e, li)
+        assert np.isnan(y[e, m:]).all()          # nothing past the layer's outputs is written

@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from gpu_common import REL_TOL, device, rel_err, sample_rows, say
+from gpu_common import REL_TOL, device, full_size_case, rel_err, sample_rows, say
 from oracle import gemv as ogemv
 from oracle import hadamard as ohad
 from trellis_coded_gemv_amd import binding as tg
@@ -11,10 +11,12 @@ from trellis_coded_gemv_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
+HDR = 256                                  # workspace header (status word) before the counter areas
 
-def _run_gemv(arr, x_bits, dev, flags=0, ws=None):
+
+def _run_gemv(arr, x_bits, dev, flags=0, ws=None, splits=0):
     torch = pytest.importorskip("torch")
-    L = tg.DeviceLayer(arr, dev, flags=flags)
+    L = tg.DeviceLayer(arr, dev, flags=flags, splits=splits)
     x = tg.fp16_tensor(x_bits, dev)
     y = tg.trellis_gemv(L, x, ws=ws)
     torch.cuda.synchronize()
@@ -67,16 +69,11 @@ def test_gemv_config1_full():
 def test_gemv_config_sampled(cfg, tensor):
     """Full-size workload tensors in the launch configuration the bench times; oracle on sampled outputs."""
     dev = device()
-    wl = inputs.WORKLOADS[cfg]
-    m, n, k = wl.tensors[tensor]
-    idx = list(wl.tensors).index(tensor)
-    arr = inputs.make_layer(m, n, k, wl.seed, tensor=idx)
-    x = inputs.make_x(n, wl.seed, tensor=idx)
-    say("gemv config", cfg, tensor, m, n, k)
+    arr, x, rows, _, ref = full_size_case(f"w{cfg}_{tensor}_c0")
+    say("gemv config", cfg, tensor, arr.m, arr.n, arr.k_bits)
     y = _run_gemv(arr, x, dev)
     assert np.isfinite(y).all()
-    rows = sample_rows(m, seed=idx)
-    err = rel_err(y[rows], ogemv.gemv_rows(arr, x, rows))
+    err = rel_err(y[rows], ref[0])
     say("rel err", err)
     assert err <= REL_TOL
 
@@ -94,21 +91,20 @@ def test_gemv_deterministic_and_workspace_reuse():
     y2 = tg.trellis_gemv(L, xt, ws=ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
-    tickets = ws[: 1024 // 128 * 4].view(torch.int32)
+    tickets = ws[HDR: HDR + 1024 // 128 * 4].view(torch.int32)
     assert ((tickets & 0xFFFF) == 0).all()              # ticket counters end each call at a call boundary
     rows = sample_rows(1024)
     assert rel_err(y1.cpu().numpy()[rows], ogemv.gemv_rows(arr, x, rows)) <= REL_TOL
 
 
 @pytest.mark.parametrize("splits", ["1", "3", "7", "32"])
-def test_gemv_split_counts(splits, monkeypatch):
-    """Every split count (forced through the tuning override) gives the same answer within tolerance."""
+def test_gemv_split_counts(splits):
+    """Every split count (forced through the layer's splits field) gives the same answer within tolerance."""
     dev = device()
-    monkeypatch.setenv("TG_SPLITK", splits)
     arr = inputs.make_layer(256, 4096, 2, 88)
     x = inputs.make_x(4096, 88)
     say("splits", splits)
-    y = _run_gemv(arr, x, dev)
+    y = _run_gemv(arr, x, dev, splits=int(splits))
     assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
 
 
@@ -125,28 +121,26 @@ def test_gemv_edge_values():
 
 
 @pytest.mark.parametrize("splits", ["40", "64"])
-def test_gemv_many_splits(splits, monkeypatch):
+def test_gemv_many_splits(splits):
     """More splits than one pass of the reducer covers (8 waves x 4 slots): chunks of one and two 128-blocks."""
     dev = device()
-    monkeypatch.setenv("TG_SPLITK", splits)
     arr = inputs.make_layer(256, 8192, 2, 89)
     x = inputs.make_x(8192, 89)
     say("many splits", splits)
-    y = _run_gemv(arr, x, dev)
+    y = _run_gemv(arr, x, dev, splits=int(splits))
     assert rel_err(y, ogemv.gemv(arr, x)) <= REL_TOL
 
 
 
-def test_gemv_slot_area_full_beside_small_batch(monkeypatch):
+def test_gemv_slot_area_full_beside_small_batch():
     """A 32768 x 4096 layer with a forced 16 splits is held to the slot area's 2048 (block, split)
     pairs (256 blocks x 8 splits): its slots fill the area exactly. Batch-1 and 16-row calls then
     alternate on one buffer; each result equals the one on a fresh workspace, bit for bit, so the
     small-batch scratch and the full slot area do not overlap."""
     dev = device()
     import torch
-    monkeypatch.setenv("TG_SPLITK", "16")
     arr = inputs.make_layer(32768, 4096, 2, 96)
-    L = tg.DeviceLayer(arr, dev)
+    L = tg.DeviceLayer(arr, dev, splits=16)
     x = inputs.make_x(4096, 96)
     xt = tg.fp16_tensor(x, dev)
     X = tg.fp16_tensor(inputs.make_x(4096, 97, rows=16), dev)
@@ -157,10 +151,10 @@ def test_gemv_slot_area_full_beside_small_batch(monkeypatch):
         assert torch.equal(tg.trellis_gemv(L, xt, ws=ws), ref_v)
         assert torch.equal(tg.trellis_gemm_small(L, X, ws=ws), ref_g)
     torch.cuda.synchronize()
-    slots = ws[2 * (1 << 22) // 128 * 4:].view(torch.int64)
+    slots = ws[HDR + 2 * (1 << 22) // 128 * 4:].view(torch.int64)
     assert (((slots[: 2048 * 128] >> 32) & 0xFFFF) == 8).all()   # 8 splits in every pair's tag
-    rows = sample_rows(32768)
-    assert rel_err(ref_v.cpu().numpy()[rows], ogemv.gemv_rows(arr, x, rows)) <= REL_TOL
+    _, _, rows, _, ref = full_size_case("slots_32768x4096_c0")
+    assert rel_err(ref_v.cpu().numpy()[rows], ref[0]) <= REL_TOL
 
 
 def test_gemv_call_tags_wrap():
@@ -182,7 +176,7 @@ def test_gemv_call_tags_wrap():
             bad += (~torch.eq(y, ref)).sum()
     torch.cuda.synchronize()
     assert int(bad) == 0
-    tickets = ws[: 2 * 4].view(torch.int32)
+    tickets = ws[HDR: HDR + 2 * 4].view(torch.int32)
     assert ((tickets & 0xFFFF) == 0).all()
 
 
@@ -201,7 +195,7 @@ def test_workspace_shared_by_layers_and_paths():
     Xb = tg.fp16_tensor(inputs.make_x(8192, 93, rows=5), dev)
     size = max(tg.workspace(A, 16, dev).numel(), tg.workspace(B, 16, dev).numel())
     ws = torch.zeros(size, dtype=torch.uint8, device=dev)
-    counters = 2 * (1 << 22) // 128 * 4        # the batch-1 and small-batch counter areas
+    counters = HDR + 2 * (1 << 22) // 128 * 4  # end of the batch-1 and small-batch counter areas
     ws[counters:] = 0xFF
     say("shared workspace")
     ref = {"ga": tg.trellis_gemm_small(A, Xa), "vb": tg.trellis_gemv(B, xb),
@@ -213,9 +207,10 @@ def test_workspace_shared_by_layers_and_paths():
         y = call()
         torch.cuda.synchronize()
         assert torch.equal(y, ref[name]), name
-        tickets = ws[: counters // 2].view(torch.int32)
+        half = (counters - HDR) // 2
+        tickets = ws[HDR: HDR + half].view(torch.int32)
         assert ((tickets & 0xFFFF) == 0).all(), name
-        assert (ws[counters // 2: counters] == 0).all(), name
+        assert (ws[HDR + half: counters] == 0).all(), name
     rows = sample_rows(512)
     assert rel_err(ref["vb"].cpu().numpy()[rows], ogemv.gemv_rows(b_arr, inputs.make_x(8192, 91), rows)) <= REL_TOL
 
@@ -237,7 +232,7 @@ def test_stale_slots_never_carry_the_expected_tag():
     ws = torch.zeros(max(tg.workspace(A, 1, dev).numel(), tg.workspace(B, 1, dev).numel()),
                      dtype=torch.uint8, device=dev)
     counter_area = (1 << 22) // 128 * 4
-    slot_off = 2 * counter_area                  # the slot area follows both counter areas
+    slot_off = HDR + 2 * counter_area            # the slot area follows the header and both counter areas
     say("stale slot tags")
     call_tag_alone_would_match = False
     for name in "ababa":
@@ -249,7 +244,7 @@ def test_stale_slots_never_carry_the_expected_tag():
         post_slots = ws[slot_off:].view(torch.int64)
         S = int((post_slots[0] >> 32) & 0xFFFF)   # the split count the call wrote
         assert S in (8, 16), S
-        tickets = pre[:counter_area].view(torch.int32)[:ob].to(torch.int64) & 0xFFFFFFFF
+        tickets = pre[HDR: HDR + counter_area].view(torch.int32)[:ob].to(torch.int64) & 0xFFFFFFFF
         expect = ((tickets & 0xFFFF0000) | S).view(ob, 1)
         n_slots = ob * S * 128
         after = ((post_slots[:n_slots] >> 32) & 0xFFFFFFFF).view(ob, S * 128)
@@ -259,3 +254,18 @@ def test_stale_slots_never_carry_the_expected_tag():
         old_rule = (tickets >> 16).view(ob, 1) + 1  # a tag of the call number + 1 alone
         call_tag_alone_would_match |= bool(((before >> 16) + 1 == old_rule).logical_and(before != 0).any())
     assert call_tag_alone_would_match
+
+
+def test_workspace_status_word():
+    """Calls that finish normally leave the status word at zero; the query reads the word and clears it."""
+    dev = device()
+    import torch
+    arr = inputs.make_layer(256, 4096, 2, 98)
+    L = tg.DeviceLayer(arr, dev)
+    ws = tg.workspace(L, 1, dev)
+    say("status word")
+    tg.trellis_gemv(L, tg.fp16_tensor(inputs.make_x(4096, 98), dev), ws=ws)
+    assert tg.workspace_status(ws) == 0
+    ws[:4] = torch.tensor([tg.TG_STATUS_SPLITK_TIMEOUT, 0, 0, 0], dtype=torch.uint8, device=dev)
+    assert tg.workspace_status(ws, clear=True) == tg.TG_STATUS_SPLITK_TIMEOUT
+    assert tg.workspace_status(ws) == 0

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from gpu_common import REL_TOL, device, rel_err, sample_rows, say
+from gpu_common import REL_TOL, device, full_size_case, rel_err, say
 from oracle import code as ocode
 from oracle import gemv as ogemv
 from trellis_coded_gemv_amd import binding as tg
@@ -17,9 +17,9 @@ def _layer(m, n, k, seed, tensor=0):
     return inputs.make_layer(m, n, k, seed, tensor=tensor, code_id=PAIR)
 
 
-def _gemv(arr, x_bits, dev, flags=0):
+def _gemv(arr, x_bits, dev, flags=0, splits=0):
     import torch
-    L = tg.DeviceLayer(arr, dev, flags=flags)
+    L = tg.DeviceLayer(arr, dev, flags=flags, splits=splits)
     y = tg.trellis_gemv(L, tg.fp16_tensor(x_bits, dev))
     torch.cuda.synchronize()
     return y.cpu().numpy()
@@ -76,27 +76,21 @@ def test_pair_gemv_small_shapes(k, m, n, flags):
 def test_pair_gemv_full_size_sampled(cfg, tensor):
     """Full-size workload shapes in the bench's launch configuration, oracle on sampled outputs."""
     dev = device()
-    wl = inputs.WORKLOADS[cfg]
-    m, n, k = wl.tensors[tensor]
-    idx = list(wl.tensors).index(tensor)
-    arr = _layer(m, n, k, wl.seed, tensor=idx)
-    x = inputs.make_x(n, wl.seed, tensor=idx)
-    say("pair gemv config", cfg, tensor, m, n, k)
+    arr, x, rows, _, ref = full_size_case(f"w{cfg}_{tensor}_c1")
+    say("pair gemv config", cfg, tensor, arr.m, arr.n, arr.k_bits)
     y = _gemv(arr, x, dev)
-    rows = sample_rows(m, seed=idx)
-    err = rel_err(y[rows], ogemv.gemv_rows(arr, x, rows))
+    err = rel_err(y[rows], ref[0])
     say("rel err", err)
     assert err <= REL_TOL
 
 
 @pytest.mark.parametrize("splits", ["1", "3", "7"])
-def test_pair_gemv_split_counts(splits, monkeypatch):
+def test_pair_gemv_split_counts(splits):
     dev = device()
-    monkeypatch.setenv("TG_SPLITK", splits)
     arr = _layer(256, 4096, 2, 4200)
     x = inputs.make_x(4096, 4200)
     say("pair splits", splits)
-    assert rel_err(_gemv(arr, x, dev), ogemv.gemv(arr, x)) <= REL_TOL
+    assert rel_err(_gemv(arr, x, dev, splits=int(splits)), ogemv.gemv(arr, x)) <= REL_TOL
 
 
 def test_pair_gemv_zero_stream_and_zero_input():
@@ -138,15 +132,10 @@ def test_pair_gemm_small_every_k(k, n, flags):
 def test_pair_gemm_full_size_sampled():
     """Gate projection 8192->28672 at K=4, 16 activation rows, pair code."""
     dev = device()
-    wl = inputs.CFG4
-    m, n, k = wl.tensors["gate"]
-    arr = _layer(m, n, k, wl.seed)
-    X = inputs.make_x(n, wl.seed, rows=wl.batch)
+    arr, X, rows, _, ref = full_size_case("w4_gate_c1")
     say("pair gemm 28672x8192 K4 M16")
     Y = _gemm(arr, X, dev)
-    rows = sample_rows(m, seed=4, blocks=2, per_block=8)
-    ref = ogemv.gemm_rows(arr, X, rows)
-    for r in range(wl.batch):
+    for r in range(X.shape[0]):
         assert rel_err(Y[r, rows], ref[r]) <= REL_TOL, r
 
 

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from gpu_common import REL_TOL, device, rel_err, sample_rows, say
+from gpu_common import REL_TOL, device, full_size_case, rel_err, say
 from oracle import gemv as ogemv
 from trellis_coded_gemv_amd import binding as tg
 from trellis_coded_gemv_amd import inputs
@@ -61,16 +61,10 @@ def test_prefill_decoded_weights_match_the_decode_hook():
 def test_prefill_full_size_sampled():
     """Gate projection 8192 -> 28672 at K=4 with 256 rows: sampled outputs against the oracle."""
     dev = device()
-    wl = inputs.CFG4
-    m, n, k = wl.tensors["gate"]
-    arr = inputs.make_layer(m, n, k, wl.seed)
-    X = inputs.make_x(n, wl.seed, rows=256)
+    arr, X, rows, pick, ref = full_size_case("prefill_gate_m256_c0")
     say("prefill 28672x8192 K4 M256")
     Y = _prefill(arr, X, dev)
     assert np.isfinite(Y).all()
-    rows = sample_rows(m, seed=6, blocks=2, per_block=8)
-    pick = [0, 100, 255]
-    ref = ogemv.gemm_rows(arr, X[pick], rows)
     for i, r in enumerate(pick):
         assert rel_err(Y[r, rows], ref[i]) <= REL_TOL, r
 

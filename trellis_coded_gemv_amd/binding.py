@@ -17,12 +17,15 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrellis_gemv.so")
 
 TG_FLAG_ROUND_WEIGHTS = 1
+TG_STATUS_SPLITK_TIMEOUT = 1
+ABI_VERSION = 2
 
 STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS", -4: "TG_ERR_ALIGN",
           -5: "TG_ERR_WORKSPACE", -6: "TG_ERR_CODE_ID", -7: "TG_ERR_LAUNCH", -8: "TG_ERR_ARG"}
 
 # every symbol the header declares
-EXPORTS = ("tg_abi_version", "tg_status_str", "tg_workspace_size", "trellis_gemv", "trellis_gemm_small",
+EXPORTS = ("tg_abi_version", "tg_build_id", "tg_workspace_status", "tg_status_str", "tg_workspace_size",
+           "trellis_gemv", "trellis_gemm_small", "tg_decode_ceiling",
            "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table",
            "trellis_encode", "tg_encode_workspace_size", "trellis_gemm_prefill", "tg_prefill_workspace_size",
            "trellis_moe_block", "tg_moe_workspace_size")
@@ -31,7 +34,7 @@ EXPORTS = ("tg_abi_version", "tg_status_str", "tg_workspace_size", "trellis_gemv
 class TgLayer(ctypes.Structure):
     """Mirror of tg_layer."""
     _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("k_bits", ctypes.c_int32),
-                ("code_id", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("code_id", ctypes.c_int32), ("flags", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("sign_in", ctypes.c_void_p), ("sign_out", ctypes.c_void_p)]
 
@@ -46,17 +49,27 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load the HIP library (once). Raises if it is not built."""
+    """Load the HIP library (once). Raises if it is not built, or was built from other sources
+    than the ones in this tree (its tg_build_id differs from their hash)."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m trellis_coded_gemv_amd.build`")
+    from .build import source_hash
     L = ctypes.CDLL(LIB_PATH)
+    L.tg_build_id.restype = ctypes.c_char_p
+    L.tg_build_id.argtypes = []
+    built, want = L.tg_build_id().decode(), source_hash()
+    if built != want:
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (build id {built}, sources {want}): "
+                           "rebuild it with `python -m trellis_coded_gemv_amd.build`")
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     LP = ctypes.POINTER(TgLayer)
     sig = {
         "tg_abi_version": (I32, []),
+        "tg_build_id": (ctypes.c_char_p, []),
+        "tg_workspace_status": (I32, [P, I32, ctypes.POINTER(ctypes.c_uint32), P]),
         "tg_status_str": (ctypes.c_char_p, [I32]),
         "tg_workspace_size": (SZ, [LP, I32]),
         "trellis_gemv": (I32, [LP, P, P, P, SZ, P]),
@@ -66,6 +79,7 @@ def lib() -> ctypes.CDLL:
         "tg_grouped_workspace_size": (SZ, [LP, I32, I32]),
         "trellis_decode": (I32, [LP, P, P]),
         "tg_code_table": (I32, [I32, P, P]),
+        "tg_decode_ceiling": (I32, [I32, I32, I32, I32, P, P]),
         "trellis_encode": (I32, [I32, I32, I32, ctypes.c_float, P, P, P, P, SZ, P]),
         "tg_encode_workspace_size": (SZ, [I32, I32, I32]),
         "trellis_gemm_prefill": (I32, [LP, I32, P, I64, P, I64, P, SZ, P]),
@@ -77,6 +91,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
+    if L.tg_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.tg_abi_version()}, the binding expects {ABI_VERSION}")
     _lib = L
     return L
 
@@ -112,17 +128,17 @@ def _stream(stream) -> Optional[int]:
 class DeviceLayer:
     """A layer's arrays in device memory plus its tg_layer descriptor."""
 
-    def __init__(self, arrays, device="cuda", flags: int = 0):
+    def __init__(self, arrays, device="cuda", flags: int = 0, splits: int = 0):
         torch = _torch()
         self.m, self.n, self.k_bits = int(arrays.m), int(arrays.n), int(arrays.k_bits)
-        self.code_id, self.flags = int(getattr(arrays, "code_id", 0)), int(flags)
+        self.code_id, self.flags, self.splits = int(getattr(arrays, "code_id", 0)), int(flags), int(splits)
         self.codes = torch.from_numpy(np.ascontiguousarray(arrays.codes).view(np.int32)).to(device)
         self.scales = torch.from_numpy(np.ascontiguousarray(arrays.scales).view(np.int16)).to(device)
         self.sign_in = torch.from_numpy(np.ascontiguousarray(arrays.sign_in).view(np.int32)).to(device)
         self.sign_out = torch.from_numpy(np.ascontiguousarray(arrays.sign_out).view(np.int32)).to(device)
 
     def desc(self) -> TgLayer:
-        return TgLayer(self.m, self.n, self.k_bits, self.code_id, self.flags, 0,
+        return TgLayer(self.m, self.n, self.k_bits, self.code_id, self.flags, self.splits,
                        self.codes.data_ptr(), self.scales.data_ptr(),
                        self.sign_in.data_ptr(), self.sign_out.data_ptr())
 
@@ -135,6 +151,17 @@ def fp16_tensor(bits: np.ndarray, device="cuda"):
     """Host uint16 fp16 patterns -> device float16 tensor (same bits)."""
     torch = _torch()
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.float16)).to(device)
+
+
+def build_id() -> str:
+    return lib().tg_build_id().decode()
+
+
+def workspace_status(ws, clear: bool = False, stream=None) -> int:
+    """The workspace's status word (TG_STATUS_* bits); waits for the stream."""
+    word = ctypes.c_uint32(0)
+    _check(lib().tg_workspace_status(_ptr(ws), int(clear), ctypes.byref(word), _stream(stream)), "tg_workspace_status")
+    return int(word.value)
 
 
 def workspace_size(layer: DeviceLayer, M: int = 1) -> int:
@@ -229,6 +256,16 @@ def trellis_decode(layer: DeviceLayer, out=None, stream=None):
         out = torch.empty(layer.m, layer.n, dtype=torch.int16, device=layer.codes.device)
     d = layer.desc()
     _check(lib().trellis_decode(ctypes.byref(d), _ptr(out), _stream(stream)), "trellis_decode")
+    return out
+
+
+def decode_ceiling(k_bits: int, code_id: int, workgroups: int, steps: int, out=None, stream=None):
+    """Launch the decode-only rate probe; returns its fp32 output [workgroups * 512]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(workgroups * 512, dtype=torch.float32, device="cuda")
+    _check(lib().tg_decode_ceiling(k_bits, code_id, workgroups, steps, _ptr(out), _stream(stream)),
+           "tg_decode_ceiling")
     return out
 
 

@@ -32,8 +32,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def source_hash() -> str:
+    """Hash of the library's sources (HIP files and the C header); the library reports it as tg_build_id()."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".hpp"))]
+    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+              if f.endswith(".h")]
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def compile_flags():
     return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
+            f"-DTG_BUILD_ID=\"{source_hash()}\"",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # every atomic here is issued by one lane; the optimizer's wave-wide
             # rewrite would wait for the result at once instead of where it is used

@@ -14,6 +14,10 @@
 
 #define TG_API extern "C" __attribute__((visibility("default")))
 
+#ifndef TG_BUILD_ID
+#define TG_BUILD_ID "unversioned"
+#endif
+
 namespace {
 
 using namespace tg;
@@ -40,18 +44,13 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
 
-int env_int(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
-
 int32_t check_layer(const tg_layer* L) {
   if (!L) return TG_ERR_NULL;
   if (L->code_id != 0 && L->code_id != 1) return TG_ERR_CODE_ID;
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || (L->m % kBlock) != 0 || (L->n % kBlock) != 0) return TG_ERR_SHAPE;
   if (L->m > (1 << 22) || L->n > (1 << 22)) return TG_ERR_SHAPE;
-  if ((L->flags & ~TG_FLAG_ROUND_WEIGHTS) != 0 || L->reserved != 0) return TG_ERR_ARG;
+  if ((L->flags & ~TG_FLAG_ROUND_WEIGHTS) != 0 || L->splits < 0 || L->splits > 65535) return TG_ERR_ARG;
   if (!L->codes || !L->scales || !L->sign_in || !L->sign_out) return TG_ERR_NULL;
   if (misaligned(L->codes, 16) || misaligned(L->scales, 2) || misaligned(L->sign_in, 4) ||
       misaligned(L->sign_out, 4))
@@ -63,7 +62,8 @@ int32_t check_layer(const tg_layer* L) {
 // (one 128-output block x one chunk each) measured best on 256 CUs for every
 // workload shape; chunks are kept equal and a whole number of 16-tile steps
 // (two 128-blocks), since a half step costs the decode work of a full one.
-// The chunk also has to fit the LDS budget. TG_SPLITK overrides (tuning aid).
+// The chunk also has to fit the LDS budget. A layer's `splits` field, when
+// positive, forces the count (a tuning aid; still clamped to what fits).
 int split_for_target(int nb, int target) {
   const int steps = nb / 2;                      // whole steps along the input
   if (steps < 1) return 1;
@@ -76,9 +76,9 @@ int split_for_target(int nb, int target) {
   return best;
 }
 
-int gemv_splits(int m, int n) {
+int gemv_splits(int m, int n, int forced) {
   const int ob = m / kBlock, nb = n / kBlock;
-  int s = env_int("TG_SPLITK");
+  int s = forced;
   if (s <= 0) {
     // chunks of a single step lose to two-step chunks: the split-K handoff
     // costs more than the extra parallelism gains (1024 x 8192: 8.9 vs 7.3 us)
@@ -100,10 +100,10 @@ int gemv_splits(int m, int n) {
 // to 1/8 of the code bytes; a chunk keeps at least 8 MFMA steps (one per
 // wave): 8 tile columns for code 0, 16 for the pair code, whose MFMA spans two
 // tiles.
-int gemm_splits(int m, int n, int M, int k_bits, int code_id) {
+int gemm_splits(int m, int n, int M, int k_bits, int code_id, int forced) {
   const int ob = m / kBlock;
   const int nsub = n / (code_id == 0 ? kBlock : 2 * kBlock);
-  int s = env_int("TG_SPLITK_MFMA");
+  int s = forced;
   if (s <= 0) {
     s = (256 + ob / 2) / ob;                                     // about 256 workgroups
     const int cap = (int)((int64_t)n * k_bits / (512 * M));    // partial traffic <= 1/8 of the code bytes
@@ -114,7 +114,8 @@ int gemm_splits(int m, int n, int M, int k_bits, int code_id) {
   return s;
 }
 
-// A layer's workspace, at fixed offsets for every layer: the batch-1 ticket
+// A layer's workspace, at fixed offsets for every layer: the header (its first
+// word is the status word, see tg_workspace_status), the batch-1 ticket
 // counters and the small-batch arrival counters, each in an area sized for the
 // largest layer; the batch-1 split-K slots, in an area of kSlotPairs (block,
 // split) pairs; then the small-batch scratch (input transform, partials). A
@@ -131,8 +132,8 @@ struct GemvWs {
 
 GemvWs gemv_ws(int m, int splits) {
   GemvWs w;
-  w.counters = 0;
-  w.slots = 2 * kCounterArea;
+  w.counters = kWsHeader;
+  w.slots = kWsHeader + 2 * kCounterArea;
   w.total = w.slots + (splits > 1 ? round_up((size_t)splits * m * 8, kAlign) : 0);
   return w;
 }
@@ -148,8 +149,8 @@ struct GemmWs {
 GemmWs gemm_ws(int m, int n, int M, int splits) {
   GemmWs w;
   const int mpad = (M + 15) / 16 * 16;
-  w.counters = kCounterArea;
-  w.xt = 2 * kCounterArea + kSlotArea;
+  w.counters = kWsHeader + kCounterArea;
+  w.xt = kWsHeader + 2 * kCounterArea + kSlotArea;
   w.partials = w.xt + round_up((size_t)mpad * n * 4, kAlign);
   w.total = w.partials + (splits > 1 ? round_up((size_t)splits * M * m * 4, kAlign) : 0);
   return w;
@@ -167,13 +168,13 @@ int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel
   for (int i = 0; i < n_layers; ++i) {
     const int32_t st = check_layer(&layers[i]);
     if (st != TG_OK) return st;
-    if (layers[i].flags != flags) return TG_ERR_ARG;
+    if (layers[i].flags != flags || layers[i].splits != layers[0].splits) return TG_ERR_ARG;
     if (layers[i].m > max_m) max_m = layers[i].m;
     if (layers[i].n > max_n) max_n = layers[i].n;
   }
   const int max_ob = max_m / kBlock, max_nb = max_n / kBlock;
   if ((int64_t)n_sel * max_ob * max_nb > INT32_MAX) return TG_ERR_SHAPE;   // the grid (splits <= max_nb) fits 31 bits
-  int s = env_int("TG_SPLITK");
+  int s = layers[0].splits;
   if (s <= 0) {
     // at most one workgroup per CU: a second round of a few workgroups costs a whole chunk's time
     const int per = n_sel * max_ob;
@@ -187,8 +188,8 @@ int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel
   g->max_m = max_m;
   g->max_n = max_n;
   g->splits = s;
-  g->counters = 0;
-  g->slots = round_up((size_t)n_sel * max_ob * 4, kAlign);
+  g->counters = kWsHeader;
+  g->slots = kWsHeader + round_up((size_t)n_sel * max_ob * 4, kAlign);
   g->total = g->slots + round_up((size_t)n_sel * s * max_m * 8, kAlign);
   return TG_OK;
 }
@@ -198,6 +199,20 @@ int32_t launch_status(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_LA
 }  // namespace
 
 TG_API int32_t tg_abi_version(void) { return TG_ABI_VERSION; }
+
+TG_API const char* tg_build_id(void) { return TG_BUILD_ID; }
+
+TG_API int32_t tg_workspace_status(void* ws, int32_t clear, uint32_t* status, void* stream) {
+  if (!ws || !status) return TG_ERR_NULL;
+  if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess) return TG_ERR_LAUNCH;
+  if (hipStreamSynchronize(s) != hipSuccess) return TG_ERR_LAUNCH;
+  *status = word;
+  if (clear && word != 0u && hipMemsetAsync(ws, 0, sizeof(word), s) != hipSuccess) return TG_ERR_LAUNCH;
+  return TG_OK;
+}
 
 TG_API const char* tg_status_str(int32_t status) {
   switch (status) {
@@ -216,8 +231,8 @@ TG_API const char* tg_status_str(int32_t status) {
 
 TG_API size_t tg_workspace_size(const tg_layer* L, int32_t M) {
   if (check_layer(L) != TG_OK || M < 1 || M > 64) return 0;
-  const size_t g = gemm_ws(L->m, L->n, M, gemm_splits(L->m, L->n, M, L->k_bits, L->code_id)).total;
-  const size_t v = gemv_ws(L->m, gemv_splits(L->m, L->n)).total;
+  const size_t g = gemm_ws(L->m, L->n, M, gemm_splits(L->m, L->n, M, L->k_bits, L->code_id, L->splits)).total;
+  const size_t v = gemv_ws(L->m, gemv_splits(L->m, L->n, L->splits)).total;
   return v > g ? v : g;
 }
 
@@ -227,7 +242,7 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
   if (st != TG_OK) return st;
   if (!x || !y) return TG_ERR_NULL;
   if (misaligned(x, 2) || misaligned(y, 4)) return TG_ERR_ALIGN;
-  const int splits = gemv_splits(L->m, L->n);
+  const int splits = gemv_splits(L->m, L->n, L->splits);
   if (gemv_slots_overflow(L->m, splits)) return TG_ERR_SHAPE;
   const GemvWs w = gemv_ws(L->m, splits);
   if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
@@ -241,6 +256,7 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
   a.y = y;
   a.counters = reinterpret_cast<uint32_t*>((char*)ws + w.counters);
   a.slots = reinterpret_cast<uint64_t*>((char*)ws + w.slots);
+  a.status = reinterpret_cast<uint32_t*>(ws);
   a.m = L->m;
   a.n = L->n;
   a.splits = splits;
@@ -258,7 +274,7 @@ TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* 
   if (!X || !Y) return TG_ERR_NULL;
   if (ldx < L->n || ldy < L->m) return TG_ERR_ARG;
   if (misaligned(X, 2) || misaligned(Y, 4)) return TG_ERR_ALIGN;
-  const int splits = gemm_splits(L->m, L->n, M, L->k_bits, L->code_id);
+  const int splits = gemm_splits(L->m, L->n, M, L->k_bits, L->code_id, L->splits);
   const GemmWs w = gemm_ws(L->m, L->n, M, splits);
   if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
   if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
@@ -316,6 +332,7 @@ TG_API int32_t trellis_gemv_grouped(const tg_layer* layers, const tg_layer* d_la
   a.y_stride = y_stride;
   a.counters = reinterpret_cast<uint32_t*>((char*)ws + g.counters);
   a.slots = reinterpret_cast<uint64_t*>((char*)ws + g.slots);
+  a.status = reinterpret_cast<uint32_t*>(ws);
   a.max_m = g.max_m;
   a.splits = g.splits;
   a.round_weights = (layers[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0;
@@ -335,6 +352,16 @@ TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) 
   if (!L->codes || !w_out) return TG_ERR_NULL;
   if (misaligned(L->codes, 4) || misaligned(w_out, 2)) return TG_ERR_ALIGN;
   return launch_status(launch_decode(L->codes, w_out, L->m, L->n, L->k_bits, L->code_id, (hipStream_t)stream));
+}
+
+TG_API int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t workgroups, int32_t steps, float* out,
+                                 void* stream) {
+  if (code_id != 0 && code_id != 1) return TG_ERR_CODE_ID;
+  if (k_bits < 1 || k_bits > 8) return TG_ERR_KBITS;
+  if (workgroups < 1 || workgroups > 65535 || steps < 1 || steps > (1 << 20)) return TG_ERR_ARG;
+  if (!out) return TG_ERR_NULL;
+  if (misaligned(out, 4)) return TG_ERR_ALIGN;
+  return launch_status(launch_decode_ceiling(k_bits, code_id, workgroups, steps, out, (hipStream_t)stream));
 }
 
 TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
@@ -470,7 +497,7 @@ int32_t moe_geometry(const tg_layer* gu, int32_t n_gu, const tg_layer* dn, int32
     if (gu[i].m != w->inter || gu[i].n != w->hidden) return TG_ERR_SHAPE;
   for (int i = 0; i < n_dn; ++i)
     if (dn[i].m != w->hidden || dn[i].n != w->inter) return TG_ERR_SHAPE;
-  if (gu[0].flags != dn[0].flags) return TG_ERR_ARG;
+  if (gu[0].flags != dn[0].flags || gu[0].splits != dn[0].splits) return TG_ERR_ARG;
   w->gu_off = 0;
   w->dn_off = round_up(w->gu.total, kAlign);
   w->y1 = w->dn_off + round_up(w->dn.total, kAlign);
@@ -480,7 +507,7 @@ int32_t moe_geometry(const tg_layer* gu, int32_t n_gu, const tg_layer* dn, int32
 }
 
 GroupedArgs grouped_args(const tg_layer* d_layers, int32_t n_layers, const int32_t* d_sel, int32_t n_sel,
-                         const GroupedWs& g, char* ws, float* y, int64_t y_stride, bool round) {
+                         const GroupedWs& g, char* ws, float* y, int64_t y_stride, bool round, uint32_t* status) {
   GroupedArgs a;
   a.layers = reinterpret_cast<const LayerDev*>(d_layers);
   a.sel = d_sel;
@@ -492,6 +519,7 @@ GroupedArgs grouped_args(const tg_layer* d_layers, int32_t n_layers, const int32
   a.y_stride = y_stride;
   a.counters = reinterpret_cast<uint32_t*>(ws + g.counters);
   a.slots = reinterpret_cast<uint64_t*>(ws + g.slots);
+  a.status = status;
   a.max_m = g.max_m;
   a.splits = g.splits;
   a.round_weights = round ? 1 : 0;
@@ -528,11 +556,13 @@ TG_API int32_t trellis_moe_block(const tg_layer* gate_up, const tg_layer* d_gate
   float* Y1 = reinterpret_cast<float*>(base + w.y1);   // [2 top_k][inter]: gate, up rows per selection
   float* Y2 = reinterpret_cast<float*>(base + w.y2);   // [top_k][hidden]
   const bool round = (gate_up[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0;
-  GroupedArgs g1 = grouped_args(d_gate_up, n_gate_up, d_sel, 2 * top_k, w.gu, base + w.gu_off, Y1, w.inter, round);
+  uint32_t* status = reinterpret_cast<uint32_t*>(base);   // the first region's header
+  GroupedArgs g1 = grouped_args(d_gate_up, n_gate_up, d_sel, 2 * top_k, w.gu, base + w.gu_off, Y1, w.inter, round,
+                                status);
   g1.x = x;
   g1.sel_pairs = 1;
   if (launch_grouped(g1, w.gu.max_m / kBlock, w.gu.max_n, s) != hipSuccess) return TG_ERR_LAUNCH;
-  GroupedArgs g2 = grouped_args(d_down, n_down, d_sel, top_k, w.dn, base + w.dn_off, Y2, w.hidden, round);
+  GroupedArgs g2 = grouped_args(d_down, n_down, d_sel, top_k, w.dn, base + w.dn_off, Y2, w.hidden, round, status);
   g2.hin = Y1;
   g2.hin_stride = w.inter;
   if (launch_grouped(g2, w.dn.max_m / kBlock, w.dn.max_n, s) != hipSuccess) return TG_ERR_LAUNCH;

@@ -356,8 +356,9 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
         s1[j] = peek_slot(slots + (size_t)t * kBlock + lane + 64);
       }
     }
+    bool empty = true;
     for (uint32_t it = 0; it < kSlotPolls; ++it) {
-      bool empty = false;
+      empty = false;
 #pragma unroll
       for (int j = 0; j < J; ++j) empty |= !slot_ready(s0[j], tag) || !slot_ready(s1[j], tag);
       if (!empty) break;
@@ -369,6 +370,9 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
         if (!slot_ready(s1[j], tag)) s1[j] = peek_slot(slots + (size_t)t * kBlock + lane + 64);
       }
     }
+    // A wait that ran out: its outputs become NaN (slot_value) and the
+    // workspace's status word records it for the host.
+    if (empty) report_status(a.status, kStatusSplitkTimeout);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int t = t0 + wave + j * WAVES;
@@ -440,6 +444,10 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
   const int li = g.sel_pairs ? 2 * sv + (e & 1) : sv;
   const LayerDev L = g.layers[li];
   if (ob >= (L.m >> 7)) return;
+  // The launch's split count comes from the table's widest layer; a layer with
+  // fewer 128-blocks runs one chunk per block, so no chunk is ever empty.
+  const int splits = g.splits < (L.n >> 7) ? g.splits : (L.n >> 7);
+  if (split >= splits) return;
   GemvArgs a;
   a.codes = L.codes;
   a.scales = L.scales;
@@ -449,9 +457,10 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
   a.y = g.y + (size_t)e * g.y_stride;
   a.slots = g.slots + (size_t)e * g.splits * g.max_m;
   a.counters = g.counters + (size_t)e * (g.max_m >> 7);
+  a.status = g.status;
   a.m = L.m;
   a.n = L.n;
-  a.splits = g.splits;
+  a.splits = splits;
   a.hg = GATED ? g.hin + (size_t)(2 * e) * g.hin_stride : nullptr;
   a.hu = GATED ? g.hin + (size_t)(2 * e + 1) * g.hin_stride : nullptr;
   if (L.code_id == 0) grouped_dispatch<0, ROUND, GATED>(a, L.k_bits, ob, split, lds);
@@ -541,6 +550,58 @@ hipError_t launch_moe_combine(const float* Y2, int64_t y2_stride, const int32_t*
                               int n_experts, int hidden, float* y, hipStream_t s) {
   hipLaunchKernelGGL(moe_combine_kernel, dim3((hidden + 255) / 256), dim3(256), 0, s, Y2, y2_stride, sel, w, top_k,
                      n_experts, hidden, y);
+  return hipGetLastError();
+}
+
+// Decode-only rate of the batch-1 loop (the VALU ceiling of the path): each
+// wave runs the same per-step work as gemv_workgroup -- the x~ words of its
+// tile column from LDS, the quad rotate for the overlap bits, the window
+// extraction, code and dot product of its 64 weights per lane -- but reads
+// its code words from LDS instead of HBM (on odd steps those of the lane 64
+// threads on, so nothing can be hoisted out of the loop). The per-lane sums
+// are written out so that no work is dead.
+template <int K, int CODE>
+__global__ __launch_bounds__(512) void decode_ceiling_kernel(float* __restrict__ out, int steps, uint32_t seed) {
+  constexpr int NW = 2 * K;
+  constexpr int NX = CODE == 0 ? 16 : 8;
+  __shared__ uint32_t xx_lds[16 * NX];
+  __shared__ uint32_t words[512 * NW];
+  const int tid = threadIdx.x, lane = tid & 63, jslot = lane >> 2;
+  for (int i = tid; i < 16 * NX; i += 512) xx_lds[i] = 0x3C003C00u ^ ((uint32_t)i * 0x00010001u);
+  for (int i = tid; i < 512 * NW; i += 512) {
+    uint32_t h = (uint32_t)i * 0x9E3779B1u + seed + blockIdx.x * 0x85EBCA6Bu;
+    h ^= h >> 15;
+    words[i] = h * 0x2C1B3C6Du;
+  }
+  __syncthreads();
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const CodeRegs cr;
+  for (int st = 0; st < steps; ++st) {
+    uint32_t w[NW], xv[NX];
+    const uint32_t* src = &words[((tid + (st & 1) * 64) & 511) * NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = src[i];
+    read_xx(xx_lds, jslot, xv);
+    const uint32_t nbw = quad_rotate_next(w[0]);
+    if constexpr (CODE == 0) decode_dot_64<K, false>(w, nbw, xv, acc, cr);
+    else decode_dot_pair_64<K, false>(w, nbw, xv, acc, cr);
+  }
+  out[(size_t)blockIdx.x * 512 + tid] = acc[0] + acc[1] + acc[2] + acc[3];
+}
+
+hipError_t launch_decode_ceiling(int k_bits, int code_id, int workgroups, int steps, float* out, hipStream_t s) {
+#define TG_CASE(K)                                                                                          \
+  case K:                                                                                                 \
+    if (code_id == 0)                                                                                     \
+      hipLaunchKernelGGL((decode_ceiling_kernel<K, 0>), dim3(workgroups), dim3(512), 0, s, out, steps, 1u); \
+    else                                                                                                  \
+      hipLaunchKernelGGL((decode_ceiling_kernel<K, 1>), dim3(workgroups), dim3(512), 0, s, out, steps, 1u); \
+    break;
+  switch (k_bits) {
+    TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef TG_CASE
   return hipGetLastError();
 }
 

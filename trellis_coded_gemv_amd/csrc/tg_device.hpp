@@ -381,6 +381,11 @@ __device__ __forceinline__ uint64_t peek_slot(const uint64_t* p) {
 
 __device__ __forceinline__ bool slot_ready(uint64_t s, uint32_t tag) { return (uint32_t)(s >> 32) == tag; }
 
+// Set sticky error bits in a workspace's status word (device scope, any lane may call).
+__device__ __forceinline__ void report_status(uint32_t* status, uint32_t bits) {
+  __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Value of a slot read; NaN if it does not hold this call's partial (a wait that ran out).
 __device__ __forceinline__ float slot_value(uint64_t s, uint32_t tag) {
   return slot_ready(s, tag) ? __builtin_bit_cast(float, (uint32_t)s) : __builtin_nanf("");

@@ -16,6 +16,8 @@ constexpr int kGemvThreads = 64 * kGemvWaves;
 #endif
 constexpr int kGemvP = TG_GEMV_P;        // batch-1 path: waves per tile row (interleaved steps)
 constexpr int kMaxChunkBlocks = 64;      // 128-blocks of x~ held in LDS by one GEMV workgroup
+constexpr size_t kWsHeader = 256;        // every workspace starts with this header; word 0 = status
+constexpr uint32_t kStatusSplitkTimeout = 1u;   // a split-K wait ran out (its outputs were written as NaN)
 
 // One batch-1 GEMV as a workgroup sees it.
 struct GemvArgs {
@@ -27,6 +29,7 @@ struct GemvArgs {
   float* y;
   uint64_t* slots;      // [m/128][splits][128] call-tagged split-K slots (unused when splits == 1)
   uint32_t* counters;   // [m/128] ticket counters, on a call boundary (multiple of 2^16) between calls
+  uint32_t* status;     // the workspace's status word (sticky error bits)
   int32_t m, n, splits;
   const float* hg;      // gated-MLP input mode: x = fp16(silu(hg) * hu), fp32 rows of n values
   const float* hu;
@@ -34,7 +37,7 @@ struct GemvArgs {
 
 // Grouped batch-1 GEMVs: the layer table lives in device memory.
 struct LayerDev {          // mirrors tg_layer
-  int32_t m, n, k_bits, code_id, flags, reserved;
+  int32_t m, n, k_bits, code_id, flags, splits;
   const uint32_t* codes;
   const uint16_t* scales;
   const uint32_t* sign_in;
@@ -51,6 +54,7 @@ struct GroupedArgs {
   int64_t y_stride;
   uint64_t* slots;      // per selection [max_m/128][splits][128] call-tagged split-K slots
   uint32_t* counters;   // [n_sel][max_m/128] ticket counters
+  uint32_t* status;     // the workspace's status word
   int32_t max_m, splits, round_weights;
   int32_t sel_pairs;    // 1: selection e uses layer 2*sel[e/2] + e%2 (gate and up of the selected experts)
   const float* hin;     // non-null: selection e's input is fp16(silu(hin row 2e) * hin row 2e+1)
@@ -72,6 +76,7 @@ struct GemmArgs {
 
 hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_weights, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, int max_ob, int max_n, hipStream_t s);
+hipError_t launch_decode_ceiling(int k_bits, int code_id, int workgroups, int steps, float* out, hipStream_t s);
 hipError_t launch_moe_combine(const float* Y2, int64_t y2_stride, const int32_t* sel, const float* w, int top_k,
                               int n_experts, int hidden, float* y, hipStream_t s);
 hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in,
