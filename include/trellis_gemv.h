@@ -179,6 +179,32 @@ int32_t trellis_gemv(const tg_layer *layer, const uint16_t *x, float *y,
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * trellis_gemv for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation
+ * and kernels, with the split-K state (ticket counters and slots) in a
+ * file-scope device array of the library instead of a caller workspace. No
+ * memory is allocated or freed by this call.
+ *   x, y  : as for trellis_gemv.
+ * Limits: the array holds tg_noalloc_scratch_bytes() bytes (about 1.1 MiB): at
+ * most 16384 output blocks (m <= 2^21) and at most 1024 (output block, input
+ * chunk) pairs (m/128 times the layer's split count); a layer beyond either
+ * returns TG_ERR_WORKSPACE with nothing enqueued.
+ * Each GPU holds its own copy of the array until the process ends; every call
+ * on that GPU shares it, and it keeps the last call's state (which, as in a
+ * shared caller workspace, needs no clearing between calls). Calls that overlap
+ * on one GPU (concurrent streams or threads) race on it and must not happen.
+ * The first call on a device looks the array up and zero-fills it, waiting
+ * for the device; it must not be made while a stream is being captured
+ * (TG_ERR_ARG then). Later calls enqueue one kernel launch and may be captured.
+ * The status word (TG_STATUS_*) is the array's first word; it is not readable
+ * through tg_workspace_status.
+ */
+int32_t trellis_gemv_noalloc(const tg_layer *layer, const uint16_t *x, float *y, void *stream);
+
+/* Size in bytes of trellis_gemv_noalloc's per-device array. */
+size_t tg_noalloc_scratch_bytes(void);
+
+/*
  * Small-batch trellis-coded GEMM on the matrix cores: Y[r] = W X[r] for
  * r < M, 1 <= M <= 64. Each decoded 16x16 tile feeds an fp32-accumulating
  * MFMA (lecture, Part eight: the 16x16 tile matches the matrix-multiply tile;

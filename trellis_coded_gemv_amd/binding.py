@@ -25,7 +25,8 @@ STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS",
 
 # every symbol the header declares
 EXPORTS = ("tg_abi_version", "tg_build_id", "tg_workspace_status", "tg_status_str", "tg_workspace_size",
-           "trellis_gemv", "trellis_gemm_small", "tg_decode_ceiling",
+           "trellis_gemv", "trellis_gemv_noalloc", "tg_noalloc_scratch_bytes", "trellis_gemm_small",
+           "tg_decode_ceiling",
            "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table",
            "trellis_encode", "tg_encode_workspace_size", "trellis_gemm_prefill", "tg_prefill_workspace_size",
            "trellis_moe_block", "tg_moe_workspace_size")
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         "tg_status_str": (ctypes.c_char_p, [I32]),
         "tg_workspace_size": (SZ, [LP, I32]),
         "trellis_gemv": (I32, [LP, P, P, P, SZ, P]),
+        "trellis_gemv_noalloc": (I32, [LP, P, P, P]),
+        "tg_noalloc_scratch_bytes": (SZ, []),
         "trellis_gemm_small": (I32, [LP, I32, P, I64, P, I64, P, SZ, P]),
         "rht_apply": (I32, [I32, I32, P, P, P, I32, P]),
         "trellis_gemv_grouped": (I32, [LP, P, I32, P, I32, P, I64, P, I64, P, SZ, P]),

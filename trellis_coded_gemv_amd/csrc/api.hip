@@ -266,6 +266,87 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
       launch_gemv(a, L->k_bits, L->code_id, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------------------
+// Batch-1 GEMV without a caller workspace (for callers that cannot allocate).
+// Its split-K state lives in `scratch`, one file-scope device array per GPU:
+// [header 256 B][ticket counters kNoAllocCounterBytes][slots kNoAllocSlotBytes].
+// The kernels are the batch-1 ones; they get the array's device address, taken
+// once per device with hipGetSymbolAddress (host code never uses the symbol
+// itself). The array keeps its contents between calls; like a shared caller
+// workspace, the tickets and call-tagged slots need no clearing between calls,
+// only a zero start, which the set-up provides.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocCounterBytes = 64 * 1024;                 // 16384 output blocks: m <= 2^21
+constexpr int kNoAllocSlotPairs = 1024;                            // (output block, split) pairs
+constexpr size_t kNoAllocSlotBytes = (size_t)kNoAllocSlotPairs * kBlock * 8;   // 1 MiB
+constexpr size_t kNoAllocScratchBytes = kWsHeader + kNoAllocCounterBytes + kNoAllocSlotBytes;
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;   // device -> device address of that device's `scratch`
+
+// Device address of the current device's array; on the first call on a device
+// (not allowed during stream capture) it is looked up and zero-filled.
+int32_t scratch_address(hipStream_t s, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    *out = it->second;
+    return TG_OK;
+  }
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return TG_ERR_LAUNCH;
+  if (cap != hipStreamCaptureStatusNone) return TG_ERR_ARG;   // set-up must run outside capture
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TG_ERR_LAUNCH;
+  if (hipMemset(p, 0, kNoAllocScratchBytes) != hipSuccess) return TG_ERR_LAUNCH;
+  if (hipDeviceSynchronize() != hipSuccess) return TG_ERR_LAUNCH;
+  g_scratch[dev] = p;
+  *out = p;
+  return TG_OK;
+}
+
+}  // namespace
+
+TG_API size_t tg_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+TG_API int32_t trellis_gemv_noalloc(const tg_layer* L, const uint16_t* x, float* y, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != TG_OK) return st;
+  if (!x || !y) return TG_ERR_NULL;
+  if (misaligned(x, 2) || misaligned(y, 4)) return TG_ERR_ALIGN;
+  const int splits = gemv_splits(L->m, L->n, L->splits);
+  if (gemv_slots_overflow(L->m, splits)) return TG_ERR_SHAPE;
+  if ((size_t)(L->m / kBlock) * 4 > kNoAllocCounterBytes) return TG_ERR_WORKSPACE;
+  if (splits > 1 && (int64_t)splits * (L->m / kBlock) > kNoAllocSlotPairs) return TG_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void* p = nullptr;
+  st = scratch_address(s, &p);
+  if (st != TG_OK) return st;
+  char* base = (char*)p;
+  GemvArgs a;
+  a.codes = L->codes;
+  a.scales = L->scales;
+  a.sign_in = L->sign_in;
+  a.sign_out = L->sign_out;
+  a.x = x;
+  a.y = y;
+  a.status = reinterpret_cast<uint32_t*>(base);
+  a.counters = reinterpret_cast<uint32_t*>(base + kWsHeader);
+  a.slots = reinterpret_cast<uint64_t*>(base + kWsHeader + kNoAllocCounterBytes);
+  a.m = L->m;
+  a.n = L->n;
+  a.splits = splits;
+  a.hg = nullptr;
+  a.hu = nullptr;
+  return launch_status(launch_gemv(a, L->k_bits, L->code_id, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, s));
+}
+
 TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* X, int64_t ldx, float* Y,
                                   int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_layer(L);
