@@ -160,34 +160,80 @@ def _copies(total_bytes):
     return max(1, min(MAX_COPIES, math.ceil(CACHE_DEFEAT_BYTES / total_bytes)))
 
 
-def setup_linears(torch, tg, inputs, wl, dev, code_id):
-    """Workloads 1-3: batch-1 GEMVs over the workload's tensors, one call each per step."""
+# The decoder layer's launch groups when layers that read one input vector are fused:
+# q/k/v read the attention input, gate/up the MLP input (each group one launch).
+FUSED_GROUPS = {3: [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",))]}
+FUSED = {"on": True}
+
+
+def launch_groups(workload, names):
+    """[(launch name, tensor names)]: one launch per tensor, or the fused groups."""
+    if FUSED["on"] and workload in FUSED_GROUPS:
+        return FUSED_GROUPS[workload]
+    return [(n, (n,)) for n in names]
+
+
+def group_inputs(inputs, wl, members, code_id, copy=0):
+    """{tensor: (layer arrays, x bits)} of one launch group's tensors in one copy: every layer of a
+    fused group reads the input vector of the group's first tensor."""
     names = list(wl.tensors)
+    x = inputs.make_x(wl.tensors[members[0]][1], wl.seed, tensor=names.index(members[0]), copy=copy)
+    out = {}
+    for name in members:
+        m, n, k = wl.tensors[name]
+        out[name] = (inputs.make_layer(m, n, k, wl.seed, tensor=names.index(name), copy=copy, code_id=code_id), x)
+    return out
+
+
+def linear_inputs(inputs, wl, workload, code_id, copy=0):
+    """{tensor: (layer arrays, x bits)} of one copy of the whole workload, as the bench's launches read them."""
+    out = {}
+    for _, members in launch_groups(workload, list(wl.tensors)):
+        out.update(group_inputs(inputs, wl, members, code_id, copy))
+    return out
+
+
+def setup_linears(torch, tg, inputs, wl, dev, code_id, workload=3):
+    """Workloads 1-3: batch-1 GEMVs over the workload's tensors, each launch group once per step.
+    Every launch group has its own number of seeded copies (>= 1 GiB of codes each, at most 64), so
+    a launch never reads a copy it read less than 1 GiB of its own launches ago."""
+    names = list(wl.tensors)
+    groups = launch_groups(workload, names)
     code_bytes = sum(m * n * k // 8 for (m, n, k) in wl.tensors.values())
-    copies = _copies(code_bytes)
-    log(f"{wl.name}: {len(names)} tensor(s), {code_bytes} code bytes per step, {copies} copies")
-    per = []
-    for c in range(copies):
-        layers = {}
-        for ti, name in enumerate(names):
-            m, n, k = wl.tensors[name]
-            L = tg.DeviceLayer(inputs.make_layer(m, n, k, wl.seed, tensor=ti, copy=c, code_id=code_id), dev)
-            x = tg.fp16_tensor(inputs.make_x(n, wl.seed, tensor=ti, copy=c), dev)
-            y = torch.empty(m, dtype=torch.float32, device=dev)
-            layers[name] = (L, x, y)
-        per.append(layers)
-    ws = {name: tg.workspace(per[0][name][0], 1, dev) for name in names}
+    gbytes = {g: sum(wl.tensors[t][0] * wl.tensors[t][1] * wl.tensors[t][2] // 8 for t in members)
+              for g, members in groups}
+    copies = {g: _copies(b) for g, b in gbytes.items()}
+    log(f"{wl.name}: {len(names)} tensor(s) in {len(groups)} launch(es), {code_bytes} code bytes per step, "
+        f"copies per launch {copies}")
+    per = {g: [] for g, _ in groups}
+    for g, members in groups:
+        for c in range(copies[g]):
+            arrays = group_inputs(inputs, wl, members, code_id, copy=c)
+            Ls = [tg.DeviceLayer(arrays[t][0], dev) for t in members]
+            x = tg.fp16_tensor(arrays[members[0]][1], dev)
+            ys = [torch.empty(L.m, dtype=torch.float32, device=dev) for L in Ls]
+            per[g].append((Ls, x, ys))
+    ws = {g: (tg.fused_workspace(per[g][0][0], dev) if len(members) > 1 else tg.workspace(per[g][0][0][0], 1, dev))
+          for g, members in groups}
 
     def step(i, launch):
-        layers = per[i % copies]
-        for name in names:
-            L, x, y = layers[name]
-            launch(name, lambda L=L, x=x, y=y, w=ws[name]: tg.trellis_gemv(L, x, y, w, torch.cuda.current_stream()))
+        s = torch.cuda.current_stream()
+        for g, members in groups:
+            Ls, x, ys = per[g][i % copies[g]]
+            if len(members) > 1:
+                launch(g, lambda Ls=Ls, x=x, ys=ys, w=ws[g]: tg.trellis_gemv_fused(Ls, x, ys, w, s))
+            else:
+                launch(g, lambda L=Ls[0], x=x, y=ys[0], w=ws[g]: tg.trellis_gemv(L, x, y, w, s))
 
-    alg = {name: gemv_bytes(*wl.tensors[name]) for name in names}
-    return step, dict(code_bytes=code_bytes, copies=copies, alg_bytes=alg, names=names,
-                      weights={name: wl.tensors[name][0] * wl.tensors[name][1] for name in names}, mfma=False,
-                      units="layer" if len(names) == 1 else "decoder layer (7 GEMVs)")
+    alg = {g: sum(gemv_bytes(*wl.tensors[t]) - (2 * wl.tensors[t][1] if j else 0) for j, t in enumerate(members))
+           for g, members in groups}
+    fused = any(len(m) > 1 for _, m in groups)
+    units = "layer" if len(names) == 1 else \
+        f"decoder layer (7 GEMVs in {len(groups)} launches{', q/k/v and gate/up fused' if fused else ''})"
+    return step, dict(code_bytes=code_bytes, copies=max(copies.values()), copies_per_launch=copies, alg_bytes=alg,
+                      names=[g for g, _ in groups], mfma=False, units=units, k_bits={g: wl.tensors[m[0]][2]
+                                                                                     for g, m in groups},
+                      weights={g: sum(wl.tensors[t][0] * wl.tensors[t][1] for t in members) for g, members in groups})
 
 
 def setup_gemm(torch, tg, inputs, wl, dev, code_id):
@@ -330,9 +376,11 @@ def run_gpu(workload, steps, warmup, use_graph, code_id=0, hot=True):
 
     dev = "cuda"
     wl = workload_of(inputs, workload)
-    setup = {1: setup_linears, 2: setup_linears, 3: setup_linears, 4: setup_gemm, 5: setup_moe,
-             6: setup_prefill, 7: setup_moe_block}[workload]
-    step, info = setup(torch, tg, inputs, wl, dev, code_id)
+    if workload in (1, 2, 3):
+        step, info = setup_linears(torch, tg, inputs, wl, dev, code_id, workload)
+    else:
+        setup = {4: setup_gemm, 5: setup_moe, 6: setup_prefill, 7: setup_moe_block}[workload]
+        step, info = setup(torch, tg, inputs, wl, dev, code_id)
     dom = max(info["names"], key=lambda k: info["alg_bytes"][k])     # kernel moving the most bytes
     copies = info["copies"]
     for i in range(warmup):
@@ -476,9 +524,13 @@ def cpu_baseline(workload, code_id=0, blocks_per_tensor=32, tokens=16, max_worke
         _CPU_JOB["layers"] = {}
         items = []
         Mo = min(wl.batch, 16)               # oracle rows per block; the rate is scaled to the step's rows
+        arrays = linear_inputs(inputs, wl, workload, code_id) if wl.batch == 1 else None
         for ti, (name, (m, n, k)) in enumerate(wl.tensors.items()):
-            arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
-            X = inputs.make_x(n, wl.seed, tensor=ti, rows=Mo)
+            if arrays is not None:           # the batch-1 step's own inputs (shared within a fused group)
+                arr, X = arrays[name]
+            else:
+                arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
+                X = inputs.make_x(n, wl.seed, tensor=ti, rows=Mo)
             _CPU_JOB["layers"][name] = (arr, X)
             nb = m // 128
             blocks = np.unique(np.linspace(0, nb - 1, min(blocks_per_tensor, nb)).astype(int))
@@ -529,14 +581,24 @@ def parity_spot_check(workload, code_id, refs):
     by_tensor = {}
     for item, y in refs.items():
         by_tensor.setdefault(item[1], []).append((item[2], y))
+    if wl.batch == 1:                        # the step's own launches on copy 0
+        arrays = linear_inputs(inputs, wl, workload, code_id)
+        for _, members in launch_groups(workload, list(wl.tensors)):
+            Ls = [tg.DeviceLayer(arrays[t][0], "cuda") for t in members]
+            x = tg.fp16_tensor(arrays[members[0]][1], "cuda")
+            ys = tg.trellis_gemv_fused(Ls, x) if len(members) > 1 else [tg.trellis_gemv(Ls[0], x)]
+            torch.cuda.synchronize()
+            for name, y in zip(members, ys):
+                y = y.cpu().numpy()
+                for b, ref in by_tensor.get(name, []):
+                    errs.append(float(np.abs(y[128 * b:128 * b + 128] - ref).max() / np.abs(ref).max()))
+        return max(errs) if errs else None
     for ti, (name, (m, n, k)) in enumerate(wl.tensors.items()):
         arr = inputs.make_layer(m, n, k, wl.seed, tensor=ti, code_id=code_id)
         Mo = min(wl.batch, 16)
         X = inputs.make_x(n, wl.seed, tensor=ti, rows=Mo)
         L = tg.DeviceLayer(arr, "cuda")
-        if wl.batch == 1:
-            Y = tg.trellis_gemv(L, tg.fp16_tensor(X, "cuda"))[None, :]
-        elif workload == 6:
+        if workload == 6:
             Y = tg.trellis_gemm_prefill(L, tg.fp16_tensor(X, "cuda"))
         else:
             Y = tg.trellis_gemm_small(L, tg.fp16_tensor(X, "cuda"))
@@ -578,6 +640,8 @@ def main(argv=None):
     ap.add_argument("--code", type=int, default=0, choices=[0, 1],
                     help="code_id of every layer: 0 the three-instruction code, 1 the pair code")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="workload 3: one launch per tensor (default: q/k/v and gate/up in one launch each)")
     ap.add_argument("--cpu-blocks", type=int, default=32,
                     help="oracle sample: 128-output blocks per tensor (tokens for workloads 5/7); 0 skips it")
     ap.add_argument("--context", default="2,4,5",
@@ -585,6 +649,7 @@ def main(argv=None):
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="after timing, write (fill) and read (sum) this many MiB (counter calibration)")
     args = ap.parse_args(argv)
+    FUSED["on"] = not args.unfused
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU path.",
               file=sys.stderr)
@@ -608,7 +673,7 @@ def main(argv=None):
     dom = t["dom"]
     achieved = info["alg_bytes"][dom] / (dom_launch_ms * 1e-3) / 1e9
     config = {"workload": rec["workload"], "units": info["units"], "code_bytes_per_step": int(info["code_bytes"]),
-              "copies": info["copies"], "us_per_step": rec["us_per_step"],
+              "copies": info.get("copies_per_launch", info["copies"]), "us_per_step": rec["us_per_step"],
               "pct_of_hbm_peak": rec["pct_of_hbm_peak"], "timing": t["timing"],
               "eager_us_per_step": round(t["eager_ms"] / steps * 1e3, 3),
               "code_id": args.code, "build_id": tg.build_id()}
@@ -618,7 +683,7 @@ def main(argv=None):
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload, dom, args.code),
             "algorithmic_bytes": int(info["alg_bytes"][dom]), "launch_us": round(dom_launch_ms * 1e3, 3)}
     if not info["mfma"]:
-        k_dom = wl.tensors[dom][2] if args.workload not in (5, 7) else 2
+        k_dom = info["k_bits"][dom] if "k_bits" in info else 2
         ceil = decode_ceiling(k_dom, args.code)
         wps = info["weights"][dom] / (dom_launch_ms * 1e-3)
         roof["alu"] = {"achieved": round(wps / 1e9, 2), "ceiling": round(ceil / 1e9, 2), "unit": "G weights/s",

@@ -60,8 +60,8 @@
  *   - Results are bitwise deterministic for identical inputs and launch
  *     configuration.
  *   - Calls that share a workspace must not run concurrently.
- *   - The workspaces of trellis_gemv, trellis_gemm_small, trellis_gemv_grouped
- *     and trellis_moe_block start with a 256-byte header whose first 32-bit
+ *   - The workspaces of trellis_gemv, trellis_gemv_fused, trellis_gemm_small,
+ *     trellis_gemv_grouped and trellis_moe_block start with a 256-byte header whose first 32-bit
  *     word is the status word: sticky TG_STATUS_* bits the kernels set and
  *     tg_workspace_status() reads (zero-filling a workspace clears it).
  *   - The library reads no environment variables; the only tuning input is a
@@ -129,8 +129,8 @@ const char *tg_build_id(void);
  * was last cleared): enqueues a 4-byte device-to-host copy on `stream` and waits for the
  * stream, so every call enqueued before it has finished. clear != 0 then enqueues a reset
  * of the word to zero (only when it was non-zero). Not for use inside graph capture.
- *   ws     : device workspace of trellis_gemv, trellis_gemm_small, trellis_gemv_grouped
- *            or trellis_moe_block, 256-byte aligned.
+ *   ws     : device workspace of trellis_gemv, trellis_gemv_fused, trellis_gemm_small,
+ *            trellis_gemv_grouped or trellis_moe_block, 256-byte aligned.
  *   status : host, receives the word.
  * Returns TG_OK, or TG_ERR_LAUNCH if the runtime reports an error.
  */
@@ -203,6 +203,35 @@ int32_t trellis_gemv_noalloc(const tg_layer *layer, const uint16_t *x, float *y,
 
 /* Size in bytes of trellis_gemv_noalloc's per-device array. */
 size_t tg_noalloc_scratch_bytes(void);
+
+/*
+ * Several batch-1 GEMVs that read the same input vector x -- a decoder layer's
+ * q, k and v projections, or its gate and up projections -- in one launch:
+ * y_l = W_l x for l < n_layers (the same computation as trellis_gemv, per
+ * layer; lecture, Parts eight, nine and eleven; Deep Dive, Section 2). The
+ * layers' work is cut into units of 16 tiles of one 128-output block and split
+ * evenly over the launch's workgroups (about one per compute unit), so small
+ * layers cost no launch of their own and no compute unit idles; blocks shared
+ * by several workgroups are summed in a fixed order, so results are bitwise
+ * deterministic.
+ *   layers   : host array of 1..8 layer descriptors with equal n (<= 16384),
+ *              k_bits, code_id, flags and splits (each layer keeps its own
+ *              codes, scales and sign vectors); splits > 0 forces the number
+ *              of workgroups (a tuning aid).
+ *   x        : device, n fp16 patterns, shared by all layers.
+ *   ys       : host array of n_layers device pointers; ys[l] receives m_l fp32.
+ *   ws       : device workspace, ws_bytes >= tg_fused_workspace_size(layers,
+ *              n_layers), 256-byte aligned, zero-filled before its first use;
+ *              every call leaves its ticket counters on a call boundary. Calls
+ *              that share it must be ordered (one stream), and a workspace used
+ *              before with other layer shapes or another count must be
+ *              zero-filled again.
+ */
+int32_t trellis_gemv_fused(const tg_layer *layers, int32_t n_layers, const uint16_t *x, float *const *ys,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for trellis_gemv_fused over these layers (0 if invalid). */
+size_t tg_fused_workspace_size(const tg_layer *layers, int32_t n_layers);
 
 /*
  * Small-batch trellis-coded GEMM on the matrix cores: Y[r] = W X[r] for

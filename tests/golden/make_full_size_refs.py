@@ -46,6 +46,14 @@ def _cases():
         m, n, k = inputs.CFG3.tensors[name]
         cases[f"w3_{name}_c1"] = dict(m=m, n=n, k=k, seed=inputs.CFG3.seed, tensor=ti, code_id=1,
                                       x=(inputs.CFG3.seed, ti, 1), pick=None, sample_seed=ti)
+    # the fused launches of the decoder layer: q/k/v read one shared vector, gate/up another
+    for cid, names in ((0, ("q", "k", "v", "gate", "up")), (1, ("q", "k", "v"))):
+        for name in names:
+            ti = list(inputs.CFG3.tensors).index(name)
+            m, n, k = inputs.CFG3.tensors[name]
+            shared = 100 if name in ("q", "k", "v") else 101
+            cases[f"w3f_{name}_c{cid}"] = dict(m=m, n=n, k=k, seed=inputs.CFG3.seed, tensor=ti, code_id=cid,
+                                              x=(inputs.CFG3.seed, shared, 1), pick=None, sample_seed=ti)
     m, n, k = inputs.CFG4.tensors["gate"]
     for cid in (0, 1):
         cases[f"w4_gate_c{cid}"] = dict(m=m, n=n, k=k, seed=inputs.CFG4.seed, tensor=0, code_id=cid,

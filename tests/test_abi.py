@@ -242,3 +242,25 @@ def test_decode_ceiling_validation():
     assert L.tg_decode_ceiling(2, 0, 1, 0, A16, None) == -8
     assert L.tg_decode_ceiling(2, 0, 1, 1, 0, None) == -1
     assert L.tg_decode_ceiling(2, 0, 1, 1, A16 + 2, None) == -4
+
+
+def test_fused_validation():
+    L = tg.lib()
+    arr = (tg.TgLayer * 3)(_layer(m=512, n=1024), _layer(m=128, n=1024), _layer(m=256, n=1024))
+    need = L.tg_fused_workspace_size(arr, 3)
+    assert need >= 256 and need % 256 == 0
+    assert L.tg_fused_workspace_size(arr, 0) == 0 and L.tg_fused_workspace_size(arr, 9) == 0
+    ys = (ctypes.c_void_p * 3)(A16, A16, A16)
+    assert L.trellis_gemv_fused(arr, 3, A16, ys, 0, need, None) == -5
+    assert L.trellis_gemv_fused(arr, 3, A16, ys, A16, need - 1, None) == -5
+    assert L.trellis_gemv_fused(arr, 3, 0, ys, A16, need, None) == -1
+    assert L.trellis_gemv_fused(arr, 3, A16, None, A16, need, None) == -1
+    assert L.trellis_gemv_fused(arr, 3, A16 + 1, ys, A16, need, None) == -4
+    bad_y = (ctypes.c_void_p * 3)(A16, 0, A16)
+    assert L.trellis_gemv_fused(arr, 3, A16, bad_y, A16, need, None) == -1
+    mixed_n = (tg.TgLayer * 2)(_layer(n=1024), _layer(n=2048))
+    assert L.tg_fused_workspace_size(mixed_n, 2) == 0
+    mixed_k = (tg.TgLayer * 2)(_layer(n=1024), _layer(n=1024, k_bits=3))
+    assert L.tg_fused_workspace_size(mixed_k, 2) == 0
+    too_wide = (tg.TgLayer * 1)(_layer(n=16384 + 128))
+    assert L.tg_fused_workspace_size(too_wide, 1) == 0

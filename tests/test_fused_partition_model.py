@@ -1,0 +1,63 @@
+"""A CPU model of the fused launch's partition (trellis_gemv_fused): layers' units (one 16-tile step
+of one 128-output block) in layer, block, step order; workgroup w takes [w*upw, (w+1)*upw). The
+model replays the host's choice of upw and the kernel's segment and contributor arithmetic, and
+checks that every unit is decoded exactly once, that a run crosses at most one layer boundary (the
+kernel keeps two layers' inputs in LDS), that each block's contributor indices are 0..count-1
+with count <= the workspace's max_contrib, and that exactly one contributor finishes each block."""
+import numpy as np
+
+
+def geometry(ms, n, target=256):
+    nb = n // 128
+    spr = (nb + 1) // 2
+    units = [(m // 128) * spr for m in ms]
+    unit0 = np.concatenate([[0], np.cumsum(units)[:-1]]).astype(int)
+    total = sum(units)
+    upw = max(1, min(-(-total // target), min(units)))
+    grid = -(-total // upw)
+    maxc = 1
+    for l, m in enumerate(ms):
+        for ob in range(m // 128):
+            b0 = unit0[l] + ob * spr
+            maxc = max(maxc, (b0 + spr - 1) // upw - b0 // upw + 1)
+    return spr, unit0, total, upw, grid, maxc
+
+
+def replay(ms, n, target=256):
+    spr, unit0, total, upw, grid, maxc = geometry(ms, n, target)
+    covered = np.zeros(total, int)
+    contributors = {}
+    for w in range(grid):
+        u0, u1 = w * upw, min((w + 1) * upw, total)
+        layers = {int(np.searchsorted(unit0, u, side="right") - 1) for u in range(u0, u1)}
+        assert len(layers) <= 2 and max(layers) - min(layers) <= 1, (w, layers)
+        u = u0
+        while u < u1:
+            l = int(np.searchsorted(unit0, u, side="right") - 1)
+            ob = (u - unit0[l]) // spr
+            seg_u0 = unit0[l] + ob * spr
+            seg_end = min(seg_u0 + spr, u1)
+            covered[u:seg_end] += 1
+            first, last = seg_u0 // upw, (seg_u0 + spr - 1) // upw
+            count = last - first + 1
+            assert count <= maxc
+            contributors.setdefault((l, ob), []).append((w - first, count))
+            u = seg_end
+    assert (covered == 1).all()
+    for key, lst in contributors.items():
+        counts = {c for _, c in lst}
+        assert len(counts) == 1 and sorted(i for i, _ in lst) == list(range(counts.pop())), key
+    return upw, grid, maxc
+
+
+def test_decoder_layer_groups():
+    assert replay([8192, 1024, 1024], 8192) == (10, 256, 4)      # q/k/v: 2560 units, 10 per workgroup
+    assert replay([28672, 28672], 8192) == (56, 256, 2)          # gate/up: 14336 units, 56 per workgroup
+
+
+def test_random_tables_and_forced_counts():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        n = 128 * int(rng.integers(1, 129))
+        ms = [128 * int(rng.integers(1, 65)) for _ in range(int(rng.integers(1, 9)))]
+        replay(ms, n, target=int(rng.integers(1, 700)))

@@ -25,7 +25,8 @@ STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS",
 
 # every symbol the header declares
 EXPORTS = ("tg_abi_version", "tg_build_id", "tg_workspace_status", "tg_status_str", "tg_workspace_size",
-           "trellis_gemv", "trellis_gemv_noalloc", "tg_noalloc_scratch_bytes", "trellis_gemm_small",
+           "trellis_gemv", "trellis_gemv_noalloc", "tg_noalloc_scratch_bytes", "trellis_gemv_fused",
+           "tg_fused_workspace_size", "trellis_gemm_small",
            "tg_decode_ceiling",
            "rht_apply", "trellis_gemv_grouped", "tg_grouped_workspace_size", "trellis_decode", "tg_code_table",
            "trellis_encode", "tg_encode_workspace_size", "trellis_gemm_prefill", "tg_prefill_workspace_size",
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         "tg_workspace_size": (SZ, [LP, I32]),
         "trellis_gemv": (I32, [LP, P, P, P, SZ, P]),
         "trellis_gemv_noalloc": (I32, [LP, P, P, P]),
+        "trellis_gemv_fused": (I32, [LP, I32, P, P, P, SZ, P]),
+        "tg_fused_workspace_size": (SZ, [LP, I32]),
         "tg_noalloc_scratch_bytes": (SZ, []),
         "trellis_gemm_small": (I32, [LP, I32, P, I64, P, I64, P, SZ, P]),
         "rht_apply": (I32, [I32, I32, P, P, P, I32, P]),
@@ -191,6 +194,33 @@ def trellis_gemv(layer: DeviceLayer, x, y=None, ws=None, stream=None):
     _check(lib().trellis_gemv(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
            "trellis_gemv")
     return y
+
+
+def _layer_array(layers):
+    arr = (TgLayer * len(layers))(*[L.desc() for L in layers])
+    return arr
+
+
+def fused_workspace(layers, device="cuda"):
+    """Zero-filled workspace for trellis_gemv_fused over these layers."""
+    size = int(lib().tg_fused_workspace_size(_layer_array(layers), len(layers)))
+    if size == 0:
+        raise TgError(-8, "tg_fused_workspace_size")
+    return _torch().zeros(size, dtype=_torch().uint8, device=device)
+
+
+def trellis_gemv_fused(layers, x, ys=None, ws=None, stream=None):
+    """y_l = W_l x for layers that share the fp16 input x [n]; returns the list of fp32 outputs."""
+    torch = _torch()
+    if ys is None:
+        ys = [torch.empty(L.m, dtype=torch.float32, device=x.device) for L in layers]
+    if ws is None:
+        ws = fused_workspace(layers, x.device)
+    arr = _layer_array(layers)
+    yp = (ctypes.c_void_p * len(layers))(*[y.data_ptr() for y in ys])
+    _check(lib().trellis_gemv_fused(arr, len(layers), _ptr(x), yp, _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)), "trellis_gemv_fused")
+    return ys
 
 
 def trellis_gemm_small(layer: DeviceLayer, X, Y=None, ws=None, stream=None):

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtrellis_gemv.so")
-SOURCES = ["api.hip", "gemv.hip", "gemm_small.hip", "misc.hip", "encode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "gemv.hip", "fused.hip", "gemm_small.hip", "misc.hip", "encode.hip", "prefill.hip"]
 ROCM_LIB = "/opt/rocm/lib"
 ARCH = "gfx950"
 

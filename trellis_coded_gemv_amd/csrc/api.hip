@@ -2,6 +2,7 @@
 // sizing, split selection and kernel launches. Nothing here touches the GPU
 // before every argument has been checked.
 #include <stddef.h>
+#include <stdint.h>
 #include <stdlib.h>
 
 #include <map>
@@ -345,6 +346,112 @@ TG_API int32_t trellis_gemv_noalloc(const tg_layer* L, const uint16_t* x, float*
   a.hg = nullptr;
   a.hu = nullptr;
   return launch_status(launch_gemv(a, L->k_bits, L->code_id, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, s));
+}
+
+// ---------------------------------------------------------------------------
+// Fused batch-1 GEMVs of layers that read one input vector (q/k/v, gate/up).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kFusedMaxN = 16384;   // two layers' x~ in LDS: 2 x n x 4 bytes
+
+struct FusedGeom {
+  int upw, grid, total_units, total_blocks, max_contrib;
+  int unit0[kFusedMaxLayers], block0[kFusedMaxLayers];
+  size_t counters, slots, total;
+};
+
+int32_t fused_geometry(const tg_layer* layers, int32_t n_layers, FusedGeom* g) {
+  if (!layers) return TG_ERR_NULL;
+  if (n_layers < 1 || n_layers > kFusedMaxLayers) return TG_ERR_ARG;
+  for (int i = 0; i < n_layers; ++i) {
+    const int32_t st = check_layer(&layers[i]);
+    if (st != TG_OK) return st;
+    if (layers[i].n != layers[0].n) return TG_ERR_SHAPE;
+    if (layers[i].k_bits != layers[0].k_bits || layers[i].code_id != layers[0].code_id ||
+        layers[i].flags != layers[0].flags || layers[i].splits != layers[0].splits)
+      return TG_ERR_ARG;
+  }
+  if (layers[0].n > kFusedMaxN) return TG_ERR_SHAPE;
+  const int nb = layers[0].n / kBlock, spr = (nb + 1) / 2;
+  int64_t units = 0, blocks = 0, min_units = INT64_MAX;
+  for (int i = 0; i < n_layers; ++i) {
+    g->unit0[i] = (int)units;
+    g->block0[i] = (int)blocks;
+    const int64_t u = (int64_t)(layers[i].m / kBlock) * spr;
+    units += u;
+    blocks += layers[i].m / kBlock;
+    if (u < min_units) min_units = u;
+  }
+  if (units > INT32_MAX / 2) return TG_ERR_SHAPE;
+  // One workgroup per compute unit by default (the layer's splits field forces another count);
+  // a run is never longer than the smallest layer, so it crosses at most one layer boundary.
+  const int target = layers[0].splits > 0 ? layers[0].splits : 256;
+  int upw = (int)((units + target - 1) / target);
+  if (upw > min_units) upw = (int)min_units;
+  if (upw < 1) upw = 1;
+  g->upw = upw;
+  g->total_units = (int)units;
+  g->grid = (int)((units + upw - 1) / upw);
+  if (g->grid > 65535 * 16) return TG_ERR_SHAPE;
+  g->total_blocks = (int)blocks;
+  int maxc = 1;
+  for (int i = 0; i < n_layers; ++i)
+    for (int ob = 0; ob < layers[i].m / kBlock; ++ob) {
+      const int64_t b0 = g->unit0[i] + (int64_t)ob * spr;
+      const int c = (int)((b0 + spr - 1) / upw - b0 / upw + 1);
+      if (c > maxc) maxc = c;
+    }
+  g->max_contrib = maxc;
+  g->counters = kWsHeader;
+  g->slots = kWsHeader + round_up((size_t)blocks * 4, kAlign);
+  g->total = g->slots + (maxc > 1 ? round_up((size_t)blocks * maxc * kBlock * 8, kAlign) : 0);
+  return TG_OK;
+}
+
+}  // namespace
+
+TG_API size_t tg_fused_workspace_size(const tg_layer* layers, int32_t n_layers) {
+  FusedGeom g;
+  if (fused_geometry(layers, n_layers, &g) != TG_OK) return 0;
+  return g.total;
+}
+
+TG_API int32_t trellis_gemv_fused(const tg_layer* layers, int32_t n_layers, const uint16_t* x, float* const* ys,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  FusedGeom g;
+  int32_t st = fused_geometry(layers, n_layers, &g);
+  if (st != TG_OK) return st;
+  if (!x || !ys) return TG_ERR_NULL;
+  if (misaligned(x, 2)) return TG_ERR_ALIGN;
+  for (int i = 0; i < n_layers; ++i) {
+    if (!ys[i]) return TG_ERR_NULL;
+    if (misaligned(ys[i], 4)) return TG_ERR_ALIGN;
+  }
+  if (!ws || ws_bytes < g.total) return TG_ERR_WORKSPACE;
+  if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
+  FusedArgs a;
+  for (int i = 0; i < kFusedMaxLayers; ++i) {
+    const tg_layer& L = layers[i < n_layers ? i : 0];
+    a.L[i].codes = L.codes;
+    a.L[i].scales = L.scales;
+    a.L[i].sign_in = L.sign_in;
+    a.L[i].sign_out = L.sign_out;
+    a.L[i].y = ys[i < n_layers ? i : 0];
+    a.L[i].unit0 = i < n_layers ? g.unit0[i] : INT32_MAX;
+    a.L[i].block0 = i < n_layers ? g.block0[i] : 0;
+  }
+  a.x = x;
+  a.counters = reinterpret_cast<uint32_t*>((char*)ws + g.counters);
+  a.slots = reinterpret_cast<uint64_t*>((char*)ws + g.slots);
+  a.status = reinterpret_cast<uint32_t*>(ws);
+  a.n_layers = n_layers;
+  a.n = layers[0].n;
+  a.upw = g.upw;
+  a.total_units = g.total_units;
+  a.max_contrib = g.max_contrib;
+  return launch_status(launch_fused(a, layers[0].k_bits, layers[0].code_id,
+                                    (layers[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0, g.grid, (hipStream_t)stream));
 }
 
 TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* X, int64_t ldx, float* Y,

@@ -1,0 +1,270 @@
+// Several batch-1 GEMVs that read the same input vector (a decoder layer's
+// q/k/v, or gate/up), in one launch with work split evenly over the GPU.
+//
+// Same computation per layer as gemv.hip ("ExLlamaV3 & EXL3 Deep Dive",
+// Section 2; "Trellis Quantization" lecture, Parts eight, nine and eleven).
+// The work of all layers is cut into units of one 16-tile step (two 128-blocks
+// of the input) of one 128-output block: layer-major, then output block, then
+// step. Workgroup w takes the contiguous run of units
+// [w * upw, (w + 1) * upw), so every workgroup has the same decode work
+// whatever the layers' shapes, and the launch needs no more workgroups than
+// the GPU has compute units (no partly filled last round, no idle units).
+//
+// A workgroup's run crosses output blocks (and at most one layer boundary).
+// It transforms the input vector once per layer it touches (each layer has its
+// own input signs) into LDS, then streams its run: the code prefetch ring runs
+// over the global unit index, so it flows across block boundaries without a
+// bubble. At the end of each block segment the 8 waves reduce their sums; a
+// block covered by one workgroup is finished there (scale, output transform,
+// signs); otherwise each contributor publishes its partial sums in call-tagged
+// slots and then takes a ticket of the block, and the holder of the last
+// ticket -- every other contributor has published by then -- sums the
+// partials in contributor order and finishes the block. No workgroup ever
+// waits for one that has not run yet.
+#include "tg_decode.hpp"
+#include "tg_internal.hpp"
+
+namespace tg {
+
+#ifndef TG_FUSED_PF
+#define TG_FUSED_PF 2
+#endif
+
+// Input transform of one layer's x~ into LDS: blocks [0, nbp) (the padding
+// block of an odd block count is zero), 8 lanes per block, 64 blocks per pass
+// of the workgroup's 512 threads. `raw` holds this lane's raw inputs of the
+// first pass (loaded early by the caller); later passes load their own.
+template <int CODE, bool ROUND>
+__device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
+                                                int nb, int nbp, X16 raw, uint32_t* xx) {
+  constexpr int XB = (CODE == 0 ? 16 : 8) * 8;   // input words per 128-block
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int xs = lane & 7;
+  for (int pass = 0; pass * 64 < nbp; ++pass) {
+    const int xb = pass * 64 + 8 * wave + (lane >> 3);
+    const int first = (xb < nb ? xb : nb - 1) * kBlock + 16 * xs;
+    if (pass > 0) raw = load_x16(x, sign_in, first);
+    const bool active = xb < nbp, live = xb < nb;
+    float* sc = reinterpret_cast<float*>(xx) + xb * kBlock;
+    float e[8], o[8];
+    {
+      float v[16];
+      x16_phase1(raw, first, v);
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          reinterpret_cast<float4_t*>(sc + 16 * xs)[i] = float4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 t = active ? *reinterpret_cast<const float2*>(sc + 16 * j + 2 * xs) : float2{0.f, 0.f};
+        e[j] = live ? t.x : 0.f;
+        o[j] = live ? t.y : 0.f;
+      }
+      x16_phase2(e, o);
+    }
+    __syncthreads();   // every wave has read its exchange values before the area is overwritten
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (CODE == 0) {
+          const uint32_t he = pack_half2(e[j], e[j]), ho = pack_half2(o[j], o[j]);
+          *reinterpret_cast<u32x2*>(xx + xb * XB + 16 * j + 2 * xs) = u32x2{he, ho};
+        } else if constexpr (ROUND) {
+          xx[xb * XB + 8 * j + xs] = pack_half2(e[j], o[j]);
+        } else {
+          xx[xb * XB + 8 * j + xs] = pack_half2(e[j] - o[j], e[j] + o[j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ int fused_layer_of(const FusedArgs& a, int u) {
+  int l = 0;
+  for (int i = 1; i < a.n_layers; ++i)
+    if (u >= a.L[i].unit0) l = i;
+  return l;
+}
+
+template <int K, int CODE, bool ROUND>
+__global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
+  constexpr int NW = 2 * K;
+  constexpr int NX = CODE == 0 ? 16 : 8;
+  constexpr int PF = TG_FUSED_PF;
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63, wave = wave_id();   // wave = tile row within the block
+  const int jslot = lane >> 2;
+  const int w = blockIdx.x;
+  const int u0 = w * a.upw;
+  const int u1 = u0 + a.upw < a.total_units ? u0 + a.upw : a.total_units;
+  if (u0 >= u1) return;
+  const int nb = a.n >> 7, nbp = (nb + 1) & ~1, n16 = a.n >> 4, spr = nbp >> 1;
+  const int lay0 = fused_layer_of(a, u0), lay1 = fused_layer_of(a, u1 - 1);
+  const size_t buf_words = (size_t)nbp * kBlock;                   // one layer's x~ area (fp32 exchange size)
+  uint32_t* xx0 = lds;
+  uint32_t* xx1 = lds + buf_words;
+  float* ybuf = reinterpret_cast<float*>(lds + 2 * buf_words);    // [128]
+  uint32_t* flag = lds + 2 * buf_words + kBlock;                   // [2]
+
+  // Raw inputs of the first transform pass, before the code prefetch (loads complete in order).
+  const int xfirst = ((8 * wave + (lane >> 3)) < nb ? (8 * wave + (lane >> 3)) : nb - 1) * kBlock + 16 * (lane & 7);
+  const X16 raw0 = load_x16(a.x, a.L[lay0].sign_in, xfirst);
+  const X16 raw1 = load_x16(a.x, a.L[lay1].sign_in, xfirst);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Code prefetch ring over the run's units; units past the run read a dummy line.
+  uint32_t buf[PF][NW];
+  const uint32_t* __restrict__ dummy = a.L[lay0].codes;
+  auto issue = [&](int u, uint32_t(&dst)[NW]) {
+    const uint32_t* p = dummy;
+    if (u < u1) {
+      const int l = fused_layer_of(a, u);
+      const int rel = u - a.L[l].unit0;
+      const int ob = rel / spr, st = rel - ob * spr;
+      if (st * 16 + jslot < n16)
+        p = a.L[l].codes + ((size_t)(ob * 8 + wave) * n16 + (size_t)st * 16) * (8 * K) + (size_t)lane * NW;
+    }
+    load_lane_words<K>(p, dst);
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) issue(u0 + p, buf[p]);
+
+  fused_transform<CODE, ROUND>(a.x, a.L[lay0].sign_in, nb, nbp, raw0, xx0);
+  if (lay1 != lay0) fused_transform<CODE, ROUND>(a.x, a.L[lay1].sign_in, nb, nbp, raw1, xx1);
+
+  const CodeRegs cr;
+  // The current block segment: layer l, output block ob, units [seg_u0, seg_end).
+  int l = lay0, ob = 0, seg_u0 = u0, seg_end = u0;
+  const uint32_t* xx = xx0;
+  auto start_segment = [&](int u) {
+    l = fused_layer_of(a, u);
+    ob = (u - a.L[l].unit0) / spr;
+    seg_u0 = a.L[l].unit0 + ob * spr;
+    const int e = seg_u0 + spr;
+    seg_end = e < u1 ? e : u1;
+    xx = l == lay0 ? xx0 : xx1;
+  };
+  start_segment(u0);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+
+  // Segment epilogue (uniform): reduce the waves' sums of the block, then finish the block here
+  // (one contributor) or publish this workgroup's partial sums and hand over by ticket.
+  auto finish_segment = [&]() {
+    const FusedLayer& Ld = a.L[l];
+    const float d = reduce_slots(acc, lane);
+    const int orow = wave * 16 + reduced_row(lane);
+    const int first_wg = seg_u0 / a.upw, last_wg = (seg_u0 + spr - 1) / a.upw;
+    const int count = last_wg - first_wg + 1;                          // workgroups contributing to the block
+    __syncthreads();                                                   // ybuf is free (previous segment done)
+    if (lane < 16) ybuf[orow] = d;
+    if (count == 1) {
+      __syncthreads();
+      if (wave == 0) rht_out_block(ybuf[lane], ybuf[lane + 64], Ld.scales, Ld.sign_out, Ld.y, ob * kBlock, lane);
+      return;
+    }
+    const int me = w - first_wg;
+    const int bglob = Ld.block0 + ob;
+    uint32_t* counter = a.counters + bglob;
+    uint64_t* slots = a.slots + (size_t)bglob * a.max_contrib * kBlock;
+    // The block's call number: its counter stays on this call's boundary (high bits) until the
+    // reducer moves it on, which happens only after every contributor's ticket.
+    if (threadIdx.x == 0)
+      flag[1] = (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ~(kTicketCall - 1u)) |
+                (uint32_t)count;
+    __syncthreads();
+    const uint32_t tag = flag[1];
+    if (lane < 16) put_slot(slots + (size_t)me * kBlock + orow, d, tag);
+    __syncthreads();                                                   // every wave has published
+    if (threadIdx.x == 0) flag[0] = (take_ticket(counter) & (kTicketCall - 1u)) == (uint32_t)count - 1u ? 1u : 0u;
+    __syncthreads();
+    if (flag[0] == 0u || wave != 0) return;
+    // the last contributor: every other one has published; sum in contributor order
+    float v0 = 0.f, v1 = 0.f;
+    bool late = false;
+    for (int i = 0; i < count; ++i) {
+      if (i == me) {
+        v0 += ybuf[lane];
+        v1 += ybuf[lane + 64];
+        continue;
+      }
+      uint64_t s0 = peek_slot(slots + (size_t)i * kBlock + lane);
+      uint64_t s1 = peek_slot(slots + (size_t)i * kBlock + lane + 64);
+      for (uint32_t it = 0; it < kSlotPolls && (!slot_ready(s0, tag) || !slot_ready(s1, tag)); ++it) {
+        __builtin_amdgcn_s_sleep(1);
+        if (!slot_ready(s0, tag)) s0 = peek_slot(slots + (size_t)i * kBlock + lane);
+        if (!slot_ready(s1, tag)) s1 = peek_slot(slots + (size_t)i * kBlock + lane + 64);
+      }
+      late |= !slot_ready(s0, tag) || !slot_ready(s1, tag);
+      v0 += slot_value(s0, tag);
+      v1 += slot_value(s1, tag);
+    }
+    if (late) report_status(a.status, kStatusSplitkTimeout);
+    rht_out_block(v0, v1, Ld.scales, Ld.sign_out, Ld.y, ob * kBlock, lane);
+    if (lane == 0) finish_call(counter, (uint32_t)count);
+  };
+
+  // Main loop in groups of PF units with the ring slot fixed per position, so every load is issued
+  // unconditionally in program order and the compiler's waits for the ring stay exact.
+  for (int ub = u0; ub < u1; ub += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int u = ub + p;
+      const bool live = u < u1;
+      if (live) {
+        uint32_t xv[NX];
+        read_xx(xx, (u - seg_u0) * 16 + jslot, xv);
+        const uint32_t nbw = quad_rotate_next(buf[p][0]);
+        if constexpr (CODE == 0) decode_dot_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
+        else decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
+      }
+      issue(u + PF, buf[p]);     // refill after use; past the run: the dummy line
+      if (live && u + 1 == seg_end) {
+        finish_segment();
+        if (u + 1 < u1) {
+          start_segment(u + 1);
+          acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+        }
+      }
+    }
+  }
+}
+
+size_t fused_lds_bytes(int n) {
+  const int nbp = ((n >> 7) + 1) & ~1;
+  return (size_t)2 * nbp * kBlock * 4 + kBlock * 4 + 16;
+}
+
+template <int K, int CODE, bool ROUND>
+static hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
+  const size_t lds = fused_lds_bytes(a.n);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<K, CODE, ROUND>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((fused_kernel<K, CODE, ROUND>), dim3(grid), dim3(512), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int CODE, bool ROUND>
+static hipError_t launch_fused_k(const FusedArgs& a, int k_bits, int grid, hipStream_t s) {
+  switch (k_bits) {
+    case 1: return launch_fused_t<1, CODE, ROUND>(a, grid, s);
+    case 2: return launch_fused_t<2, CODE, ROUND>(a, grid, s);
+    case 3: return launch_fused_t<3, CODE, ROUND>(a, grid, s);
+    case 4: return launch_fused_t<4, CODE, ROUND>(a, grid, s);
+    case 5: return launch_fused_t<5, CODE, ROUND>(a, grid, s);
+    case 6: return launch_fused_t<6, CODE, ROUND>(a, grid, s);
+    case 7: return launch_fused_t<7, CODE, ROUND>(a, grid, s);
+    case 8: return launch_fused_t<8, CODE, ROUND>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fused(const FusedArgs& a, int k_bits, int code_id, bool round_weights, int grid, hipStream_t s) {
+  if (code_id == 0)
+    return round_weights ? launch_fused_k<0, true>(a, k_bits, grid, s) : launch_fused_k<0, false>(a, k_bits, grid, s);
+  return round_weights ? launch_fused_k<1, true>(a, k_bits, grid, s) : launch_fused_k<1, false>(a, k_bits, grid, s);
+}
+
+}  // namespace tg

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(64 * MW) void gemm_small_kernel(GemmArgs a) {
   constexpr int PF = TG_MFMA_PF;
   using G = MfmaGeom<K, CODE>;
   constexpr int SLICE = 8 * G::SPAN * G::WPT;   // staged words per wave
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);

@@ -35,7 +35,7 @@
 // workgroup of the block is already running and finishes without waiting)
 // waits for those slots, sums them in a fixed order and applies scale, output
 // FWHT and signs. No other workgroup waits on anything.
-#include "tg_device.hpp"
+#include "tg_decode.hpp"
 #include "tg_internal.hpp"
 
 namespace tg {
@@ -51,123 +51,6 @@ namespace tg {
 template <int K>
 constexpr int gemv_pf() { return K <= 4 ? TG_GEMV_PF_SMALL_K : 2; }
 
-// Load this lane's 2K words (8K bytes) of the current step.
-template <int K>
-__device__ __forceinline__ void load_lane_words(const uint32_t* __restrict__ p, uint32_t (&w)[2 * K]) {
-  if constexpr (K % 2 == 0) {
-#pragma unroll
-    for (int i = 0; i < K / 2; ++i) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
-      w[4 * i + 0] = v[0];
-      w[4 * i + 1] = v[1];
-      w[4 * i + 2] = v[2];
-      w[4 * i + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + i);
-      w[2 * i + 0] = v[0];
-      w[2 * i + 1] = v[1];
-    }
-  }
-}
-
-// Decode the lane's 64 weights (4 rows x 16 columns of one tile) and
-// accumulate their dot products with x~ of that tile column.
-//   w   : the lane's 2K stream words (stream bits 0 .. 64K-1 of the lane, MSB first)
-//   nb  : first word of the next lane in the tile (wrapping at the tile's end)
-//   xx  : 16 pairs (x~_c, x~_c) for the tile's 16 input columns
-template <int K, bool ROUND>
-__device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xx)[16],
-                                              float (&acc)[4], const CodeRegs& cr) {
-  constexpr int NW = 2 * K;
-  auto word = [&](int j) -> uint32_t { return j < NW ? w[j] : nb; };
-#pragma unroll
-  for (int tl = 0; tl < 64; ++tl) {
-    const int p = K * tl;            // window start, bits from the lane's first stream bit
-    const int j = p >> 5, q = p & 31;
-    uint32_t s;
-    if (q <= 16) {
-      s = ubfe(word(j), 16 - q, 16);
-    } else {
-      s = ubfe(alignbit(word(j), word(j + 1), 16), 32 - q, 16);
-    }
-    const uint32_t u = code_halves(s, cr);
-    if constexpr (ROUND) {
-      const uint32_t wr = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
-      acc[tl >> 4] = dot2(wr, xx[tl & 15], acc[tl >> 4]);
-    } else {
-      acc[tl >> 4] = dot2(u, xx[tl & 15], acc[tl >> 4]);
-    }
-  }
-}
-
-// Pair code (code_id 1): the lane's 64 weights are 32 states, state s at
-// stream bit 2K*s (two weights per trellis step), weights 2s and 2s+1 of the
-// lane's run = columns 2(s%8), 2(s%8)+1 of row s/8. Per state: one window
-// extract, v_mad_u32_u24, v_and_or_b32 and one v_dot2c_f32_f16 against the
-// rotated input pair (x~0 - x~1, x~0 + x~1) -- two weights per dot.
-// ROUND: the rounded pair (RNE(a+b), RNE(b-a)) against the plain pair (x~0, x~1).
-//   xp : 8 pair words for the tile's 8 column pairs
-template <int K, bool ROUND>
-__device__ __forceinline__ void decode_dot_pair_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xp)[8],
-                                                   float (&acc)[4], const CodeRegs& cr) {
-  constexpr int NW = 2 * K;
-  auto word = [&](int j) -> uint32_t { return j < NW ? w[j] : nb; };
-#pragma unroll
-  for (int sl = 0; sl < 32; ++sl) {
-    const int p = 2 * K * sl;
-    const int j = p >> 5, q = p & 31;
-    uint32_t s;
-    if (q <= 16) {
-      s = ubfe(word(j), 16 - q, 16);
-    } else {
-      s = ubfe(alignbit(word(j), word(j + 1), 16), 32 - q, 16);
-    }
-    const uint32_t u = code_halves(s, cr);
-    if constexpr (ROUND) {
-      acc[sl >> 3] = dot2(pair_weights_rne(u), xp[sl & 7], acc[sl >> 3]);
-    } else {
-      acc[sl >> 3] = dot2(u, xp[sl & 7], acc[sl >> 3]);
-    }
-  }
-}
-
-// Sum acc[g] over the 16 tile slots of the wave (lane bits 2..5) with a
-// transposing reduction: the exchanges over bits 2 and 3 each halve the number
-// of values a lane carries, so 5 shuffles replace 16. On return lanes 0..15
-// hold the total of tile row 4*(l&3) + 2*((l>>2)&1) + ((l>>3)&1).
-__device__ __forceinline__ float reduce_slots(const float (&acc)[4], int lane) {
-  const bool b0 = (lane & 4) != 0, b1 = (lane & 8) != 0;
-  const float s0 = b0 ? acc[0] : acc[2], s1 = b0 ? acc[1] : acc[3];
-  const float c0 = (b0 ? acc[2] : acc[0]) + shfl_xor(s0, 4);
-  const float c1 = (b0 ? acc[3] : acc[1]) + shfl_xor(s1, 4);
-  float d = (b1 ? c1 : c0) + shfl_xor(b1 ? c0 : c1, 8);
-  d += shfl_xor(d, 16);
-  d += shfl_xor(d, 32);
-  return d;
-}
-
-__device__ __forceinline__ int reduced_row(int lane) {
-  return 4 * (lane & 3) + 2 * ((lane >> 2) & 1) + ((lane >> 3) & 1);
-}
-
-// The NX input words of one tile column (NX = 16 fp16 pairs (x~, x~) for
-// code 0, 8 column-pair words for code 1).
-template <int NX>
-__device__ __forceinline__ void read_xx(const uint32_t* xx_lds, int tile, uint32_t (&xv)[NX]) {
-  const u32x4* xs = reinterpret_cast<const u32x4*>(xx_lds + tile * NX);
-#pragma unroll
-  for (int v = 0; v < NX / 4; ++v) {
-    const u32x4 t = xs[v];
-    xv[4 * v + 0] = t[0];
-    xv[4 * v + 1] = t[1];
-    xv[4 * v + 2] = t[2];
-    xv[4 * v + 3] = t[3];
-  }
-}
-
 // One workgroup = 8 tile rows (a 128-output block) x one input chunk, with P
 // waves per tile row that take interleaved 16-tile steps of the chunk.
 // GATED: the input is fp16(silu(a.hg) * a.hu) (the down projection of a gated
@@ -180,7 +63,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   constexpr int NX = CODE == 0 ? 16 : 8;   // input words per tile column
   constexpr int XB = NX * 8;               // input words per 128-block
   constexpr int WAVES = 8 * P;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int rw = wave & 7, kp = wave >> 3;     // tile row within the block, step phase
   const int nb128 = a.n >> 7;
   const int blk0 = (int)((int64_t)split * nb128 / a.splits);

@@ -68,6 +68,12 @@ __device__ __forceinline__ uint32_t quad_rotate_next(uint32_t v) {
   return __builtin_amdgcn_update_dpp(0u, v, 0x39, 0xF, 0xF, false);
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value:
+// the compiler cannot tell on its own that threadIdx.x / 64 is the same for all
+// lanes, and would otherwise keep everything derived from it (step counts, row
+// pointers, loop tests) in vector registers with exec-mask branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }

@@ -61,6 +61,27 @@ struct GroupedArgs {
   int64_t hin_stride;   // floats between hin rows
 };
 
+// Fused batch-1 GEMVs of several layers that read one input vector (fused.hip).
+constexpr int kFusedMaxLayers = 8;
+struct FusedLayer {
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint32_t* sign_in;
+  const uint32_t* sign_out;
+  float* y;
+  int32_t unit0;        // first unit of this layer in the launch's unit order
+  int32_t block0;       // first output block of this layer among all layers' blocks
+};
+
+struct FusedArgs {
+  FusedLayer L[kFusedMaxLayers];
+  const uint16_t* x;
+  uint32_t* counters;   // [all layers' output blocks] ticket counters
+  uint64_t* slots;      // [all blocks][max_contrib][128] call-tagged partials
+  uint32_t* status;
+  int32_t n_layers, n, upw, total_units, max_contrib;
+};
+
 // Small-batch MFMA path.
 struct GemmArgs {
   const uint32_t* codes;
@@ -76,6 +97,8 @@ struct GemmArgs {
 
 hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_weights, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, int max_ob, int max_n, hipStream_t s);
+hipError_t launch_fused(const FusedArgs& a, int k_bits, int code_id, bool round_weights, int grid, hipStream_t s);
+size_t fused_lds_bytes(int n);
 hipError_t launch_decode_ceiling(int k_bits, int code_id, int workgroups, int steps, float* out, hipStream_t s);
 hipError_t launch_moe_combine(const float* Y2, int64_t y2_stride, const int32_t* sel, const float* w, int top_k,
                               int n_experts, int hidden, float* y, hipStream_t s);
