@@ -16,11 +16,12 @@
 // over the global unit index, so it flows across block boundaries without a
 // bubble. At the end of each block segment the 8 waves reduce their sums; a
 // block covered by one workgroup is finished there (scale, output transform,
-// signs); otherwise each contributor publishes its partial sums in call-tagged
-// slots and then takes a ticket of the block, and the holder of the last
-// ticket -- every other contributor has published by then -- sums the
-// partials in contributor order and finishes the block. No workgroup ever
-// waits for one that has not run yet.
+// signs); otherwise each contributor takes a ticket of the block when its
+// segment's decode is done and publishes its partial sums in call-tagged
+// slots, and the holder of the last ticket sums the partials in contributor
+// order and finishes the block. Every other contributor has finished its
+// decode by then and publishes without waiting, so no workgroup ever waits
+// for one that has not run yet.
 #include "tg_decode.hpp"
 #include "tg_internal.hpp"
 
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
 
   const CodeRegs cr;
   // The current block segment: layer l, output block ob, units [seg_u0, seg_end).
-  int l = lay0, ob = 0, seg_u0 = u0, seg_end = u0;
+  int l = lay0, ob = 0, seg_u0 = u0, seg_end = u0, count = 1;
   const uint32_t* xx = xx0;
   auto start_segment = [&](int u) {
     l = fused_layer_of(a, u);
@@ -146,6 +147,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
     const int e = seg_u0 + spr;
     seg_end = e < u1 ? e : u1;
     xx = l == lay0 ? xx0 : xx1;
+    count = (seg_u0 + spr - 1) / a.upw - seg_u0 / a.upw + 1;       // workgroups contributing to the block
   };
   start_segment(u0);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -156,8 +158,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
     const FusedLayer& Ld = a.L[l];
     const float d = reduce_slots(acc, lane);
     const int orow = wave * 16 + reduced_row(lane);
-    const int first_wg = seg_u0 / a.upw, last_wg = (seg_u0 + spr - 1) / a.upw;
-    const int count = last_wg - first_wg + 1;                          // workgroups contributing to the block
+    const int first_wg = seg_u0 / a.upw;
     __syncthreads();                                                   // ybuf is free (previous segment done)
     if (lane < 16) ybuf[orow] = d;
     if (count == 1) {
@@ -169,17 +170,17 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
     const int bglob = Ld.block0 + ob;
     uint32_t* counter = a.counters + bglob;
     uint64_t* slots = a.slots + (size_t)bglob * a.max_contrib * kBlock;
-    // The block's call number: its counter stays on this call's boundary (high bits) until the
-    // reducer moves it on, which happens only after every contributor's ticket.
-    if (threadIdx.x == 0)
-      flag[1] = (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ~(kTicketCall - 1u)) |
-                (uint32_t)count;
+    // The ticket is taken once this segment's decode is done (one round trip; its high bits give
+    // the call number of the slot tag), so the holder of the block's last ticket finds every
+    // other contributor done with its decode: they publish at once and never wait on it.
+    if (threadIdx.x == 0) {
+      const uint32_t ticket = take_ticket(counter);
+      flag[0] = (ticket & (kTicketCall - 1u)) == (uint32_t)count - 1u ? 1u : 0u;
+      flag[1] = slot_tag(ticket, (uint32_t)count);                     // the call number and the count
+    }
     __syncthreads();
     const uint32_t tag = flag[1];
     if (lane < 16) put_slot(slots + (size_t)me * kBlock + orow, d, tag);
-    __syncthreads();                                                   // every wave has published
-    if (threadIdx.x == 0) flag[0] = (take_ticket(counter) & (kTicketCall - 1u)) == (uint32_t)count - 1u ? 1u : 0u;
-    __syncthreads();
     if (flag[0] == 0u || wave != 0) return;
     // the last contributor: every other one has published; sum in contributor order
     float v0 = 0.f, v1 = 0.f;
