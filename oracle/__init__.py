@@ -18,9 +18,12 @@ Sources (web pages on QTIP / EXL3 trellis quantization):
   [TQ]  "Trellis Quantization: Trading Memory for Cheap Compute" (lecture) --
         Part three (mantissa-splice int->fp16 trick), Part eight (16-bit window,
         random access at bit K*t, 16x16 tiles, tail-biting circle), Part nine
-        (3INST computed code), Part eleven (EXL3: 128-blocks, K from 1 to 8).
+        (3INST computed code), Part eleven (EXL3: 128-blocks, K from 1 to 8,
+        the MCG and mul1 codes, int8 activations fused into the four-byte dot
+        product), Part twelve (the masked byte-sum integer generator).
   [FG]  "LLM Cal" EXL3 field guide -- "What QTIP contributes" (16x16 block as
-        one sequence, tail-biting), "out_scales always".
+        one sequence, tail-biting), "out_scales always", "What the EXL3
+        converter actually sets" (mul1 is the default codebook).
 
 Parity status of each function (what pins it, beyond itself) is listed in the
 module docstrings. Functions whose end-to-end values have no printed worked

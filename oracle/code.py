@@ -98,4 +98,56 @@ def pair_table() -> np.ndarray:
     return np.stack([e, o], axis=-1)
 
 
-CODE_V = {0: 1, 1: 2}     # weights per trellis step of each code_id
+# ---------------------------------------------------------------------------
+# code_id 2, "mul1": the EXL3 converter's default codebook ([FG] "What the EXL3
+# converter actually sets"; [TQ] Part eleven, Part twelve). Steps, as the pages
+# describe them: (1) multiply the state by a constant with no additive term
+# (EXL3's MCG change to the generator); (2) keep the low six bits of each of
+# the product's four bytes; (3) add the four bytes (one four-byte dot product
+# against ones on a GPU) and subtract a fixed offset, giving an integer level
+# in [-126, 126] with a bell-shaped spread; the weight is an affine function of
+# that level.
+# Readings where the pages leave it open: the multiplier is code 0's 0x9E3779
+# (the pages print no constant for mul1 either); the offset is 126, the mean
+# of four uniform six-bit bytes, so the levels are symmetric; the weight is the
+# level times 1/32, exact in binary16 (|w| <= 126/32), so no rounding is
+# involved anywhere.
+# Pins (tests/test_oracle_code.py): hand-worked values
+# (tests/golden/mul1_hand_values.txt); all 65,536 states against a separate
+# pure-Python integer byte sum; the level histogram against the exact
+# distribution of a sum of four independent uniform six-bit bytes.
+# ---------------------------------------------------------------------------
+
+BYTE_MASK = 0x3F3F3F3F    # low six bits of each byte
+MUL1_OFFSET = 126
+MUL1_STEP = 1.0 / 32.0    # weight per level
+
+
+def mcg(states) -> np.ndarray:
+    """Step (1): h = (MUL * S) mod 2^32, the multiply with the additive constant dropped."""
+    s = np.asarray(states, dtype=np.int64)
+    return (s * MUL) & _M32
+
+
+def byte_sum(h) -> np.ndarray:
+    """Step (2) and the sum of step (3): sum of the four bytes of (h AND 0x3F3F3F3F), in 0..252."""
+    m = np.asarray(h, dtype=np.int64) & BYTE_MASK
+    return (m & 0xFF) + ((m >> 8) & 0xFF) + ((m >> 16) & 0xFF) + ((m >> 24) & 0xFF)
+
+
+def mul1_level(states) -> np.ndarray:
+    """Integer level of each state: byte sum minus the offset, in -126..126."""
+    return byte_sum(mcg(states)) - MUL1_OFFSET
+
+
+def mul1_bits(states) -> np.ndarray:
+    """fp16 bits of the weight level / 32 (exact: a multiple of 2^-5 below 4 in magnitude)."""
+    return fp16.round_rne(mul1_level(states).astype(np.float64) * MUL1_STEP)
+
+
+def mul1_table() -> np.ndarray:
+    """code_id 2 for all states: fp16 bits [65536]."""
+    return mul1_bits(np.arange(1 << 16))
+
+
+CODE_V = {0: 1, 1: 2, 2: 1}     # weights per trellis step of each code_id

@@ -30,14 +30,16 @@ from . import code, fp16, hadamard, trellis
 def decode_layer(layer, tile_rows=None) -> np.ndarray:
     """fp16 bit patterns of the decoded weights, [m, n] (or only the listed tile rows).
 
-    code_id 0: one state per weight. code_id 1: one state per pair of weights
-    (t = 2*tau, 2*tau + 1 of the row-major tile order).
+    code_id 0 and 2: one state per weight. code_id 1: one state per pair of
+    weights (t = 2*tau, 2*tau + 1 of the row-major tile order).
     """
     cid = int(getattr(layer, "code_id", 0))
     v = code.CODE_V[cid]
     states = trellis.layer_states(layer.codes, layer.m, layer.n, layer.k_bits, tile_rows, v)
     if cid == 0:
         w = code.weight_bits(states)
+    elif cid == 2:
+        w = code.mul1_bits(states)
     else:
         even, odd = code.pair_weight_bits(states)
         w = np.stack([even, odd], axis=-1).reshape(*states.shape[:-1], trellis.SEQ)
@@ -102,6 +104,85 @@ def gemv_rows(layer, x_bits: np.ndarray, rows) -> np.ndarray:
         sel = rows // hadamard.BLOCK == blk
         out[..., sel] = yb[..., rows[sel] % hadamard.BLOCK]
     return out
+
+
+# ---------------------------------------------------------------------------
+# int8 activations ([TQ] Part eleven: with the mul1 code and activations held
+# as int8, decoding a weight and multiplying it fuse into one four-byte dot
+# product). The pages fix neither the quantiser nor its scale. Reading, chosen
+# so that the integer decision is exact and identical on every machine:
+#   u   = blockdiag(+-1 Hadamard) diag(s_in) x     exact in float64 (binary16 x)
+#   e_b = the smallest integer with max_{j in block b} |u_j| * 2^-e_b <= 127
+#         (e_b = 0 for an all-zero block)
+#   q_j = round-half-even(u_j * 2^-e_b)             in -127..127, exact scaling
+#   x^_j = q_j * 2^e_b / sqrt(128)                  replaces x~ in y~ = g * (W^ x~)
+# Pins (tests/test_oracle_int8.py): the quantiser against a pure-Python route
+# with exact fractions and Python's round(); lossless cases (integer u with
+# max |u| <= 127) where the int8 product equals the plain GEMV; the half-step
+# error bound; every block's largest |q| in 64..127.
+# ---------------------------------------------------------------------------
+
+INT8_MAX = 127
+
+
+def block_exponents(u: np.ndarray) -> np.ndarray:
+    """e_b per 128-block of u (last axis): smallest e with max|u_b| 2^-e <= 127."""
+    amax = np.abs(hadamard._blocks(u)).max(axis=-1)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    _, E = np.frexp(amax[nz])                 # amax = f 2^E, f in [1/2, 1): a first guess
+    ez = E.astype(np.int64) - 7
+    a = amax[nz]
+    while True:                               # raise e until the block fits ...
+        up = a * np.exp2(-ez.astype(np.float64)) > INT8_MAX
+        if not up.any():
+            break
+        ez += up
+    while True:                               # ... and lower it while it still fits
+        down = a * np.exp2(-(ez - 1).astype(np.float64)) <= INT8_MAX
+        if not down.any():
+            break
+        ez -= down
+    e[nz] = ez
+    return e
+
+
+def quantize_rotated(layer, x_bits: np.ndarray):
+    """(q int64 [..., n], e int64 [..., n/128]) of the int8 form of x~ for one layer's input signs."""
+    x = fp16.value(x_bits)
+    u = hadamard.apply_blocks_pm1(hadamard.signs(layer.sign_in, layer.n) * x)
+    e = block_exponents(u)
+    step = np.repeat(np.exp2(e.astype(np.float64)), hadamard.BLOCK, axis=-1)
+    q = np.rint(u / step).astype(np.int64)        # exact scaling by a power of two; rint: ties to even
+    return q, e
+
+
+def dequantized(q: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """x^ = q 2^e / sqrt(128), float64."""
+    step = np.repeat(np.exp2(e.astype(np.float64)), hadamard.BLOCK, axis=-1)
+    return q * step / np.sqrt(hadamard.BLOCK)
+
+
+def gemv_int8_rows(layer, x_bits: np.ndarray, rows) -> np.ndarray:
+    """int8-activation product at the listed outputs: y~ = g * (W^ x^), then the output transform."""
+    rows = np.asarray(rows)
+    xh = dequantized(*quantize_rotated(layer, x_bits))
+    g = scales(layer)
+    s_out = hadamard.signs(layer.sign_out, layer.m)
+    out = np.empty(xh.shape[:-1] + (len(rows),))
+    for blk in np.unique(rows // hadamard.BLOCK):
+        W = weight_matrix(layer, np.arange(blk * 8, blk * 8 + 8))
+        o = slice(blk * hadamard.BLOCK, (blk + 1) * hadamard.BLOCK)
+        yb = s_out[o] * hadamard.apply_blocks(g[o] * (xh @ W.T))
+        sel = rows // hadamard.BLOCK == blk
+        out[..., sel] = yb[..., rows[sel] % hadamard.BLOCK]
+    return out
+
+
+def gemv_int8(layer, x_bits: np.ndarray) -> np.ndarray:
+    """int8-activation product for one vector, all m outputs (the factored route with x^ for x~)."""
+    xh = dequantized(*quantize_rotated(layer, x_bits))
+    return hadamard.rht_inverse(scales(layer) * (weight_matrix(layer) @ xh), layer.sign_out)
 
 
 def gemm(layer, X_bits: np.ndarray, W: np.ndarray = None) -> np.ndarray:

@@ -55,6 +55,24 @@ def apply_blocks(v: np.ndarray) -> np.ndarray:
     return (b @ H.T).reshape(np.shape(v))
 
 
+def hadamard_pm1(n: int = BLOCK) -> np.ndarray:
+    """Unnormalised Sylvester-Hadamard matrix of order n: entries exactly +1 / -1 (float64)."""
+    i = np.arange(n)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def apply_blocks_pm1(v: np.ndarray) -> np.ndarray:
+    """blockdiag(sqrt(128) H) @ v along the last axis: the +-1 transform without its 1/sqrt(128).
+
+    For binary16 inputs every partial sum is a multiple of 2^-24 below 2^23 in
+    magnitude (47 significant bits), so each result is exact in float64 in any
+    summation order.
+    """
+    b = _blocks(v)
+    return (b @ hadamard_pm1(BLOCK).T).reshape(np.shape(v))
+
+
 def rht_forward(x: np.ndarray, sign_words: np.ndarray) -> np.ndarray:
     """Input side: x~ = blockdiag(H) diag(s) x (last axis)."""
     x = np.asarray(x, dtype=np.float64)

@@ -108,3 +108,45 @@ def test_pair_table_matches_numpy_and_is_balanced():
     for w in (we, wo):
         assert np.isfinite(w).all() and abs(w.mean()) < 0.02 and 1.1 < w.std() < 1.4
     assert abs(np.corrcoef(we, wo)[0, 1]) < 0.05
+
+
+# --- code_id 2, mul1 ----------------------------------------------------------------------
+
+def test_mul1_hand_values():
+    """Every intermediate of mul1 against the hand-worked fixture."""
+    for state, h, m, b0, b1, b2, b3, sig, lev, w in golden_rows("mul1_hand_values.txt"):
+        s = np.array([int(state, 16)])
+        assert int(code.mcg(s)[0]) == int(h, 16)
+        assert int(code.mcg(s)[0]) & code.BYTE_MASK == int(m, 16)
+        assert sum(int(v) for v in (b0, b1, b2, b3)) == int(sig)
+        assert int(code.byte_sum(code.mcg(s))[0]) == int(sig)
+        assert int(code.mul1_level(s)[0]) == int(lev)
+        assert int(code.mul1_bits(s)[0]) == int(w, 16)
+
+
+def test_mul1_all_states_against_python_byte_sum():
+    """All 65,536 states against a separate route: Python integers, bytes() and a per-byte mask."""
+    ref = []
+    for s in range(1 << 16):
+        h = (0x9E3779 * s) % (1 << 32)
+        ref.append(sum(b & 0x3F for b in h.to_bytes(4, "little")) - 126)
+    ref = np.array(ref)
+    assert (code.mul1_level(np.arange(1 << 16)) == ref).all()
+    exact = ref / 32.0
+    assert (code.mul1_table() == exact.astype(np.float16).view(np.uint16)).all()
+    assert (fp16.value(code.mul1_table()) == exact).all()       # no rounding anywhere
+
+
+def test_mul1_levels_follow_four_uniform_bytes():
+    """The level histogram over all states against the exact law of a sum of four independent
+    uniform six-bit bytes (the bell shape the pages describe), and its symmetry."""
+    law = np.ones(64)
+    for _ in range(3):
+        law = np.convolve(law, np.ones(64))
+    law /= law.sum()                                   # P(sigma = s), s = 0..252
+    lev = code.mul1_level(np.arange(1 << 16))
+    assert lev.min() >= -126 and lev.max() <= 126
+    hist = np.bincount(lev + 126, minlength=253) / lev.size
+    assert 0.5 * np.abs(hist - law).sum() < 0.03      # total variation distance
+    assert abs(lev.mean()) < 0.5 and abs(lev.std() - np.sqrt(4 * (64 ** 2 - 1) / 12)) < 1.0
+    assert code.mul1_level(np.array([0]))[0] == -126   # multiply-only: state 0 stays 0

@@ -91,7 +91,7 @@ def test_two_pass_tail_biting_closes_the_circle_near_the_optimum():
     assert np.mean(ratios) < 1.2, ratios
 
 
-@pytest.mark.parametrize("code_id,k", [(0, 2), (0, 3), (1, 1)])
+@pytest.mark.parametrize("code_id,k", [(0, 2), (0, 3), (1, 1), (2, 2)])
 def test_representable_sequence_is_encoded_exactly(code_id, k):
     """Targets that are the decoded weights of some stored tile are reached with zero error."""
     words = inputs.make_layer(16, 16, k, 55 + k).codes
@@ -119,3 +119,14 @@ def test_gaussian_source_two_bits_mse():
     mse = np.mean([float(ov.encode_tile(rng.standard_normal(256).astype(np.float32), 2, 0, 0.75, wvals)[1]) / 256
                    for _ in range(16)])
     assert 0.055 < mse < 0.075, mse
+
+
+def test_gaussian_source_two_bits_mse_mul1():
+    """The same measurement with the mul1 code (code_id 2) at its reconstruction scale 0.9:
+    a little above the three-instruction code, well under Lloyd-Max's 0.118 ([TQ] Part nine)."""
+    rng = np.random.default_rng(2024)
+    wvals = ov.code_values(2)
+    assert wvals.shape == (1 << 16,) and (wvals * 32 == np.rint(wvals * 32)).all()
+    mse = np.mean([float(ov.encode_tile(rng.standard_normal(256).astype(np.float32), 2, 2, 0.9, wvals)[1]) / 256
+                   for _ in range(16)])
+    assert 0.062 < mse < 0.080, mse
