@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the trellis-coded GEMV hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--code 0]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--code 0] [--int8]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 input-side randomized Hadamard transform, trellis decode of every weight,
@@ -42,6 +42,9 @@ decode-only ceiling (tg_decode_ceiling: the batch-1 loop on code words held
 in LDS), measured in the same run. `traffic` is the measured HBM bytes of one
 launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, profiles/traffic.json) while the
 kernel sources match the ones it was taken on.
+
+--code 2 --int8: the mul1 code with the int8 form of the rotated input (the
+batch-1 workloads 1-3; the context workloads then run code 2 without it).
 """
 from __future__ import annotations
 
@@ -81,6 +84,8 @@ def recorded_traffic(workload: int, kernel: str, code_id: int = 0):
     if rec.get("csrc_sha") != kernel_source_hash():
         return None
     key = str(workload) if code_id == 0 else f"{workload}/code{code_id}"
+    if LAYER_FLAGS["int8"]:
+        key += "/int8"
     ent = rec.get("workloads", {}).get(key, {}).get(kernel)
     return None if ent is None else int(ent["hbm_bytes_per_launch"])
 
@@ -164,6 +169,12 @@ def _copies(total_bytes):
 # q/k/v read the attention input, gate/up the MLP input (each group one launch).
 FUSED_GROUPS = {3: [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",))]}
 FUSED = {"on": True}
+# --int8: batch-1 layers carry TG_FLAG_INT8_ACT (mul1 with the int8 form of x~)
+LAYER_FLAGS = {"int8": False}
+
+
+def batch1_flags(tg):
+    return tg.TG_FLAG_INT8_ACT if LAYER_FLAGS["int8"] else 0
 
 
 def launch_groups(workload, names):
@@ -209,7 +220,7 @@ def setup_linears(torch, tg, inputs, wl, dev, code_id, workload=3):
     for g, members in groups:
         for c in range(copies[g]):
             arrays = group_inputs(inputs, wl, members, code_id, copy=c)
-            Ls = [tg.DeviceLayer(arrays[t][0], dev) for t in members]
+            Ls = [tg.DeviceLayer(arrays[t][0], dev, flags=batch1_flags(tg)) for t in members]
             x = tg.fp16_tensor(arrays[members[0]][1], dev)
             ys = [torch.empty(L.m, dtype=torch.float32, device=dev) for L in Ls]
             per[g].append((Ls, x, ys))
@@ -421,7 +432,7 @@ def stream_read_gbs(torch, nbytes=1 << 30, reps=5):
     return round(nbytes / (best * 1e-3) / 1e9, 1)
 
 
-def decode_ceiling(k_bits, code_id):
+def decode_ceiling(k_bits, code_id, flags=0):
     """Decoded weights per second of the decode-only probe (the batch-1 loop on LDS-resident code words):
     the best of 256, 512 and 1024 workgroups of 8 waves (2, 4 and 8 waves per SIMD)."""
     import torch
@@ -430,12 +441,12 @@ def decode_ceiling(k_bits, code_id):
     best = None
     for wgs in (256, 512, 1024):
         out = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
-        tg.decode_ceiling(k_bits, code_id, wgs, steps, out)
+        tg.decode_ceiling(k_bits, code_id, wgs, steps, out, flags=flags)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(5):
-            tg.decode_ceiling(k_bits, code_id, wgs, steps, out)
+            tg.decode_ceiling(k_bits, code_id, wgs, steps, out, flags=flags)
         b.record()
         torch.cuda.synchronize()
         rate = 5 * wgs * 512 * 64 * steps / (a.elapsed_time(b) * 1e-3)
@@ -475,7 +486,10 @@ def _cpu_item(item):
         _, name, b = item
         arr, X = _CPU_JOB["layers"][name]
         rows = np.arange(128 * b, 128 * b + 128)
-        y = ogemv.gemv_rows(arr, X, rows) if X.ndim == 1 else ogemv.gemm_rows(arr, X, rows)
+        if _CPU_JOB.get("int8"):
+            y = ogemv.gemv_int8_rows(arr, X, rows)
+        else:
+            y = ogemv.gemv_rows(arr, X, rows) if X.ndim == 1 else ogemv.gemm_rows(arr, X, rows)
         return 128 * arr.n * arr.k_bits // 8, y
     if kind == "token":                      # a whole MoE block (workload 7) or its 24 GEMVs (workload 5)
         from oracle import moe
@@ -522,6 +536,7 @@ def cpu_baseline(workload, code_id=0, blocks_per_tensor=32, tokens=16, max_worke
         scale = 1.0
     else:
         _CPU_JOB["layers"] = {}
+        _CPU_JOB["int8"] = LAYER_FLAGS["int8"] and wl.batch == 1
         items = []
         Mo = min(wl.batch, 16)               # oracle rows per block; the rate is scaled to the step's rows
         arrays = linear_inputs(inputs, wl, workload, code_id) if wl.batch == 1 else None
@@ -536,7 +551,8 @@ def cpu_baseline(workload, code_id=0, blocks_per_tensor=32, tokens=16, max_worke
             blocks = np.unique(np.linspace(0, nb - 1, min(blocks_per_tensor, nb)).astype(int))
             items += [("block", name, int(b)) for b in blocks]
         what = (f"{len(items)} 128-output blocks over the tensors {', '.join(wl.tensors)}"
-                f" (decode + fp64 GEMV{'' if Mo == 1 else f' of {Mo} rows, scaled to {wl.batch}'})")
+                f" (decode + fp64 GEMV{'' if Mo == 1 else f' of {Mo} rows, scaled to {wl.batch}'}"
+                f"{', int8 form of x~' if _CPU_JOB['int8'] else ''})")
         scale = wl.batch / Mo
     ctx = mp.get_context("fork")
     with ctx.Pool(workers) as pool:
@@ -584,7 +600,7 @@ def parity_spot_check(workload, code_id, refs):
     if wl.batch == 1:                        # the step's own launches on copy 0
         arrays = linear_inputs(inputs, wl, workload, code_id)
         for _, members in launch_groups(workload, list(wl.tensors)):
-            Ls = [tg.DeviceLayer(arrays[t][0], "cuda") for t in members]
+            Ls = [tg.DeviceLayer(arrays[t][0], "cuda", flags=batch1_flags(tg)) for t in members]
             x = tg.fp16_tensor(arrays[members[0]][1], "cuda")
             ys = tg.trellis_gemv_fused(Ls, x) if len(members) > 1 else [tg.trellis_gemv(Ls[0], x)]
             torch.cuda.synchronize()
@@ -620,7 +636,8 @@ def measure(workload, code_id, steps, warmup, use_graph, hot=True):
     value = info["code_bytes"] / (ms_per_step * 1e-3) / 1e9
     dom = t["dom"]
     dom_launch_ms = t["dom_ms"] / steps
-    rec = {"workload": wl.name + ("_block" if workload == 7 else ""), "code_id": code_id, "units": info["units"],
+    rec = {"workload": wl.name + ("_block" if workload == 7 else ""), "code_id": code_id,
+           "int8_activations": bool(LAYER_FLAGS["int8"] and workload in (1, 2, 3)), "units": info["units"],
            "us_per_step": round(ms_per_step * 1e3, 3), "gbs": round(value, 2),
            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "timing": t["timing"],
            "dominant": dom, "dominant_launch_us": round(dom_launch_ms * 1e3, 3)}
@@ -637,8 +654,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5, 6, 7])
-    ap.add_argument("--code", type=int, default=0, choices=[0, 1],
-                    help="code_id of every layer: 0 the three-instruction code, 1 the pair code")
+    ap.add_argument("--code", type=int, default=0, choices=[0, 1, 2],
+                    help="code_id of every layer: 0 the three-instruction code, 1 the pair code, 2 mul1")
+    ap.add_argument("--int8", action="store_true",
+                    help="with --code 2: the batch-1 layers multiply by the int8 form of x~ (TG_FLAG_INT8_ACT)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="workload 3: one launch per tensor (default: q/k/v and gate/up in one launch each)")
@@ -650,6 +669,10 @@ def main(argv=None):
                     help="after timing, write (fill) and read (sum) this many MiB (counter calibration)")
     args = ap.parse_args(argv)
     FUSED["on"] = not args.unfused
+    if args.int8 and args.code != 2:
+        print("--int8 needs --code 2 (the int8 form is mul1's)", file=sys.stderr)
+        return 2
+    LAYER_FLAGS["int8"] = args.int8
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU path.",
               file=sys.stderr)
@@ -676,7 +699,7 @@ def main(argv=None):
               "copies": info.get("copies_per_launch", info["copies"]), "us_per_step": rec["us_per_step"],
               "pct_of_hbm_peak": rec["pct_of_hbm_peak"], "timing": t["timing"],
               "eager_us_per_step": round(t["eager_ms"] / steps * 1e3, 3),
-              "code_id": args.code, "build_id": tg.build_id()}
+              "code_id": args.code, "int8_activations": rec["int8_activations"], "build_id": tg.build_id()}
     if args.workload not in (5, 7):
         config.update({"tensors": {k: list(v) for k, v in wl.tensors.items()}, "batch": wl.batch})
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -684,11 +707,12 @@ def main(argv=None):
             "algorithmic_bytes": int(info["alg_bytes"][dom]), "launch_us": round(dom_launch_ms * 1e3, 3)}
     if not info["mfma"]:
         k_dom = info["k_bits"][dom] if "k_bits" in info else 2
-        ceil = decode_ceiling(k_dom, args.code)
+        cflags = tg.TG_FLAG_INT8_ACT if rec["int8_activations"] else 0
+        ceil = decode_ceiling(k_dom, args.code, cflags)
         wps = info["weights"][dom] / (dom_launch_ms * 1e-3)
         roof["alu"] = {"achieved": round(wps / 1e9, 2), "ceiling": round(ceil / 1e9, 2), "unit": "G weights/s",
                        "frac": round(wps / ceil, 4), "ceiling_kernel": f"tg_decode_ceiling(k_bits={k_dom}, "
-                                                                    f"code_id={args.code})"}
+                                                                    f"code_id={args.code}, flags={cflags})"}
     if "flops" in info:
         tf = info["flops"] / (dom_launch_ms * 1e-3) / 1e12
         roof["mfma"] = {"achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -716,7 +740,8 @@ def main(argv=None):
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic", "config": config, "roofline": roof,
+        "vs_baseline": None, "dtype": "i8" if rec["int8_activations"] else "fp16", "data": "synthetic",
+        "config": config, "roofline": roof,
     }
     if args.copy_calib_mb > 0:
         # counter calibration: a pure write (fill) and a pure read (sum) of known size

@@ -38,6 +38,24 @@
  *   w_{2 tau + 1} = fp16_rne(b - a). Each weight is again a sum of two bounded
  *   halves (lecture, Part nine); the pair costs one code evaluation, so the
  *   decode work per weight is about half that of code_id 0.
+ *
+ * Storage format (code_id 2, "mul1", the EXL3 converter's default codebook;
+ *   lecture, Part eleven: the MCG generator drops the additive constant, mul1
+ *   sums the product's bytes with one four-byte dot product; Part twelve: each
+ *   byte masked to six bits, the sum offset to about -126..126; LLM Cal field
+ *   guide, "What the EXL3 converter actually sets"): stream layout as code_id 0,
+ *   one state per weight, and
+ *     h = 0x9E3779*S mod 2^32;  m = h & 0x3F3F3F3F;
+ *     level = (sum of the four bytes of m) - 126;  w = level / 32 (exact in fp16).
+ *   The pages fix none of these constants; these are this library's.
+ *   With TG_FLAG_INT8_ACT the batch-1 and fused paths multiply by an int8 form
+ *   of x~ instead (lecture, Part eleven: with int8 activations the decode and
+ *   the multiply are one four-byte dot product), defined per 128-block b as
+ *     u = blockdiag(+-1 Hadamard) diag(s_in) x  (exact: computed in float64),
+ *     e_b = the smallest integer with max_b |u| * 2^-e_b <= 127 (0 if all zero),
+ *     q = round-half-even(u * 2^-e_b),   x~ replaced by q * 2^e_b / sqrt(128).
+ *   The integer products are exact; only the per-block fp32 scaling rounds.
+ *
  *   scales  : m fp16 bit patterns (g).
  *   sign_in : ceil(n/32) uint32 words; bit i%32 of word i/32 set means s_in[i] = -1.
  *   sign_out: ceil(m/32) uint32 words, same convention.
@@ -77,7 +95,7 @@
 extern "C" {
 #endif
 
-#define TG_ABI_VERSION 2
+#define TG_ABI_VERSION 3
 
 typedef enum tg_status {
   TG_OK = 0,
@@ -86,7 +104,7 @@ typedef enum tg_status {
   TG_ERR_KBITS = -3,      /* k_bits outside 1..8                                      */
   TG_ERR_ALIGN = -4,      /* a pointer is not aligned as documented                   */
   TG_ERR_WORKSPACE = -5,  /* workspace missing or smaller than tg_workspace_size()     */
-  TG_ERR_CODE_ID = -6,    /* code_id other than 0 or 1                                */
+  TG_ERR_CODE_ID = -6,    /* code_id other than 0, 1 or 2                             */
   TG_ERR_LAUNCH = -7,     /* the HIP runtime rejected a kernel launch                 */
   TG_ERR_ARG = -8         /* any other invalid argument (stride, flags, index range)   */
 } tg_status;
@@ -98,14 +116,20 @@ typedef enum tg_status {
 /* Layer flags. */
 #define TG_FLAG_ROUND_WEIGHTS 1  /* GEMV paths round each weight to fp16 before the product
                                     (the default adds the two fp16 halves inside the fp32
-                                    product, which is exact up to fp32 rounding). */
+                                    product, which is exact up to fp32 rounding). No effect
+                                    with code_id 2, whose weights are exact. */
+#define TG_FLAG_INT8_ACT 2       /* code_id 2 only (else TG_ERR_ARG): trellis_gemv,
+                                    trellis_gemv_noalloc and trellis_gemv_fused multiply by
+                                    the int8 form of x~ defined above; the small-batch,
+                                    prefill, grouped and mixture-of-experts paths refuse it
+                                    (TG_ERR_ARG). */
 
 /* One trellis-coded linear layer: out_features m, in_features n. Read on the host. */
 typedef struct tg_layer {
   int32_t m;                 /* out_features, multiple of 128                              */
   int32_t n;                 /* in_features, multiple of 128                               */
   int32_t k_bits;            /* bits per weight K, 1..8 (lecture, Part eleven)              */
-  int32_t code_id;           /* 0 = the three-instruction code; 1 = the pair code            */
+  int32_t code_id;           /* 0 = the three-instruction code; 1 = the pair code; 2 = mul1  */
   int32_t flags;             /* TG_FLAG_*                                                  */
   int32_t splits;            /* input chunks (split-K) of the batch-1, grouped and          *
                               * small-batch paths: 0 = the library's choice; S > 0 forces  *
@@ -370,8 +394,8 @@ int32_t trellis_decode(const tg_layer *layer, uint16_t *w_out, void *stream);
  * The whole computed code as a table (test / export hook; lecture, Part nine:
  * each state's weight is a function of the 16-bit state alone, so the code has
  * exactly 2^16 entries), for every state S < 65536:
- *   code_id 0: out[S] = fp16 pattern of the weight for state S  (65536 entries);
- *   code_id 1: out[2S], out[2S+1] = the state's weight pair      (131072 entries).
+ *   code_id 0, 2: out[S] = fp16 pattern of the weight for state S  (65536 entries);
+ *   code_id 1:    out[2S], out[2S+1] = the state's weight pair      (131072 entries).
  *   out : device, 2-byte aligned.
  */
 int32_t tg_code_table(int32_t code_id, uint16_t *out, void *stream);
@@ -385,12 +409,13 @@ int32_t tg_code_table(int32_t code_id, uint16_t *out, void *stream);
  * per weight; Part eleven: the same decode is compute-bound on data-centre
  * cards). workgroups of 512 threads (8 waves) each run `steps` steps, i.e.
  * decode workgroups * 512 * 64 * steps weights.
- *   k_bits     : 1..8;  code_id : 0 or 1.
+ *   k_bits     : 1..8;  code_id : 0, 1 or 2.
+ *   flags      : 0, or TG_FLAG_INT8_ACT with code_id 2 (the int8-activation loop).
  *   workgroups : 1..65535;  steps : 1..2^20.
  *   out        : device, workgroups * 512 fp32 (one per thread, keeps the work live).
  */
-int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t workgroups, int32_t steps, float *out,
-                          void *stream);
+int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t flags, int32_t workgroups, int32_t steps,
+                          float *out, void *stream);
 
 /*
  * Tail-biting Viterbi encoder (offline conversion; lecture, Part seven: the
@@ -400,7 +425,7 @@ int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t workgroups, i
  * constrained to start and end on it). For every tile it stores the stream
  * whose decoded weights w minimise sum_t (scale * w_t - target_t)^2.
  *   n_tiles  : 1 .. 2^24 tiles.
- *   k_bits   : 1..8 for code_id 0; 1..4 for the pair code (2K bits per step).
+ *   k_bits   : 1..8 for code_id 0 and 2; 1..4 for the pair code (2K bits per step).
  *   scale    : reconstruction scale, finite and > 0.
  *   targets  : device, n_tiles * 256 fp32, each tile in sequence order
  *              t = 16r + c, 4-byte aligned.

@@ -1,6 +1,6 @@
 """Write the oracle's outputs for the full-size parity tests: tests/golden/full_size_refs.npz.
 
-    python tests/golden/make_full_size_refs.py [--jobs 8]
+    python tests/golden/make_full_size_refs.py [--jobs 8] [--reuse]
 
 Every case is a full-size layer of one of the workloads (seeded inputs from
 trellis_coded_gemv_amd/inputs.py); the stored values are the oracle's y at two
@@ -9,6 +9,9 @@ GPU kernels), for the activation rows the test checks. The values come from
 oracle/ only (oracle.gemv.gemv_rows / gemm_rows). Decoding a whole large layer in
 the oracle takes about a minute, too long inside a GPU test, hence the file.
 The GPU tests regenerate the same inputs from the same seeds and compare.
+Cases marked int8 hold the oracle's int8-activation product of the mul1 code
+(oracle.gemv.gemv_int8_rows). --reuse keeps the stored outputs of cases whose
+description is unchanged and computes only the others.
 """
 from __future__ import annotations
 
@@ -54,6 +57,16 @@ def _cases():
             shared = 100 if name in ("q", "k", "v") else 101
             cases[f"w3f_{name}_c{cid}"] = dict(m=m, n=n, k=k, seed=inputs.CFG3.seed, tensor=ti, code_id=cid,
                                               x=(inputs.CFG3.seed, shared, 1), pick=None, sample_seed=ti)
+    # mul1 (code_id 2) with int8 activations: every layer of the decoder layer, q/k/v and gate/up
+    # on their shared vectors as in the fused launches, o and down on their own
+    for ti, name in enumerate(inputs.CFG3.tensors):
+        m, n, k = inputs.CFG3.tensors[name]
+        shared = {"q": 100, "k": 100, "v": 100, "gate": 101, "up": 101}.get(name, ti)
+        cases[f"w3i8_{name}_c2"] = dict(m=m, n=n, k=k, seed=inputs.CFG3.seed, tensor=ti, code_id=2,
+                                         x=(inputs.CFG3.seed, shared, 1), pick=None, sample_seed=ti, int8=True)
+    m, n, k = inputs.CFG3.tensors["down"]
+    cases["w3_down_c2"] = dict(m=m, n=n, k=k, seed=inputs.CFG3.seed, tensor=6, code_id=2,
+                               x=(inputs.CFG3.seed, 6, 1), pick=None, sample_seed=6)
     m, n, k = inputs.CFG4.tensors["gate"]
     for cid in (0, 1):
         cases[f"w4_gate_c{cid}"] = dict(m=m, n=n, k=k, seed=inputs.CFG4.seed, tensor=0, code_id=cid,
@@ -81,6 +94,8 @@ def case_inputs(key):
 def _compute(key):
     from oracle import gemv
     arr, X, rows, pick = case_inputs(key)
+    if CASES[key].get("int8"):
+        return key, rows, gemv.gemv_int8_rows(arr, X, rows)[None, :]
     if X.ndim == 1:
         y = gemv.gemv_rows(arr, X, rows)[None, :]
     else:
@@ -91,10 +106,19 @@ def _compute(key):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=8)
+    ap.add_argument("--reuse", action="store_true")
     args = ap.parse_args(argv)
+    keep = {}
+    if args.reuse and os.path.exists(OUT):
+        z = np.load(OUT, allow_pickle=False)
+        old = json.loads(str(z["meta"]))
+        for key in CASES:
+            if old.get(key) == json.loads(json.dumps(CASES[key])):
+                keep[key] = (key, z[key + "/rows"], z[key + "/y"])
     import multiprocessing as mp
+    todo = sorted(k for k in CASES if k not in keep)
     with mp.get_context("fork").Pool(args.jobs) as pool:
-        res = pool.map(_compute, sorted(CASES), chunksize=1)
+        res = pool.map(_compute, todo, chunksize=1) + list(keep.values())
     out = {"meta": np.array(json.dumps(CASES, sort_keys=True))}
     for key, rows, y in res:
         out[key + "/rows"] = rows.astype(np.int32)

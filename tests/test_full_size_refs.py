@@ -12,7 +12,7 @@ from gpu_common import _refs_module
 from oracle import gemv
 
 
-@pytest.mark.parametrize("key", ["w3_k_c0", "w2_down_c1", "w4_gate_c1", "prefill_gate_m256_c0"])
+@pytest.mark.parametrize("key", ["w3_k_c0", "w2_down_c1", "w4_gate_c1", "prefill_gate_m256_c0", "w3i8_k_c2"])
 def test_first_block_matches_oracle(key):
     mod = _refs_module()
     z = np.load(mod.OUT, allow_pickle=False)
@@ -20,7 +20,9 @@ def test_first_block_matches_oracle(key):
     arr, X, rows, pick = mod.case_inputs(key)
     assert np.array_equal(z[key + "/rows"], rows)
     first = rows < 128
-    if X.ndim == 1:
+    if mod.CASES[key].get("int8"):
+        y = gemv.gemv_int8_rows(arr, X, rows[first])[None, :]
+    elif X.ndim == 1:
         y = gemv.gemv_rows(arr, X, rows[first])[None, :]
     else:
         y = gemv.gemm_rows(arr, X if pick is None else X[pick], rows[first])

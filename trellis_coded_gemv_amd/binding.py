@@ -17,8 +17,9 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrellis_gemv.so")
 
 TG_FLAG_ROUND_WEIGHTS = 1
+TG_FLAG_INT8_ACT = 2
 TG_STATUS_SPLITK_TIMEOUT = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS", -4: "TG_ERR_ALIGN",
           -5: "TG_ERR_WORKSPACE", -6: "TG_ERR_CODE_ID", -7: "TG_ERR_LAUNCH", -8: "TG_ERR_ARG"}
@@ -85,7 +86,7 @@ def lib() -> ctypes.CDLL:
         "tg_grouped_workspace_size": (SZ, [LP, I32, I32]),
         "trellis_decode": (I32, [LP, P, P]),
         "tg_code_table": (I32, [I32, P, P]),
-        "tg_decode_ceiling": (I32, [I32, I32, I32, I32, P, P]),
+        "tg_decode_ceiling": (I32, [I32, I32, I32, I32, I32, P, P]),
         "trellis_encode": (I32, [I32, I32, I32, ctypes.c_float, P, P, P, P, SZ, P]),
         "tg_encode_workspace_size": (SZ, [I32, I32, I32]),
         "trellis_gemm_prefill": (I32, [LP, I32, P, I64, P, I64, P, SZ, P]),
@@ -292,12 +293,12 @@ def trellis_decode(layer: DeviceLayer, out=None, stream=None):
     return out
 
 
-def decode_ceiling(k_bits: int, code_id: int, workgroups: int, steps: int, out=None, stream=None):
+def decode_ceiling(k_bits: int, code_id: int, workgroups: int, steps: int, out=None, stream=None, flags: int = 0):
     """Launch the decode-only rate probe; returns its fp32 output [workgroups * 512]."""
     torch = _torch()
     if out is None:
         out = torch.empty(workgroups * 512, dtype=torch.float32, device="cuda")
-    _check(lib().tg_decode_ceiling(k_bits, code_id, workgroups, steps, _ptr(out), _stream(stream)),
+    _check(lib().tg_decode_ceiling(k_bits, code_id, int(flags), workgroups, steps, _ptr(out), _stream(stream)),
            "tg_decode_ceiling")
     return out
 
@@ -305,7 +306,7 @@ def decode_ceiling(k_bits: int, code_id: int, workgroups: int, steps: int, out=N
 def code_table(device="cuda", code_id: int = 0, stream=None):
     """The code for all 65536 states: int16 [65536] (code 0) or [65536, 2] (pair code)."""
     torch = _torch()
-    shape = (1 << 16,) if code_id == 0 else (1 << 16, 2)
+    shape = (1 << 16, 2) if code_id == 1 else (1 << 16,)
     out = torch.empty(shape, dtype=torch.int16, device=device)
     _check(lib().tg_code_table(int(code_id), _ptr(out), _stream(stream)), "tg_code_table")
     return out

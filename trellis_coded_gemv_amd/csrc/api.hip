@@ -45,13 +45,18 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
 
+// Kernel form of a layer: its code_id, or mul1 against the int8 form of x~.
+int kernel_form(const tg_layer* L) { return (L->flags & TG_FLAG_INT8_ACT) != 0 ? kCodeMul1I8 : L->code_id; }
+
 int32_t check_layer(const tg_layer* L) {
   if (!L) return TG_ERR_NULL;
-  if (L->code_id != 0 && L->code_id != 1) return TG_ERR_CODE_ID;
+  if (L->code_id < 0 || L->code_id > 2) return TG_ERR_CODE_ID;
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || (L->m % kBlock) != 0 || (L->n % kBlock) != 0) return TG_ERR_SHAPE;
   if (L->m > (1 << 22) || L->n > (1 << 22)) return TG_ERR_SHAPE;
-  if ((L->flags & ~TG_FLAG_ROUND_WEIGHTS) != 0 || L->splits < 0 || L->splits > 65535) return TG_ERR_ARG;
+  if ((L->flags & ~(TG_FLAG_ROUND_WEIGHTS | TG_FLAG_INT8_ACT)) != 0 || L->splits < 0 || L->splits > 65535)
+    return TG_ERR_ARG;
+  if ((L->flags & TG_FLAG_INT8_ACT) != 0 && L->code_id != 2) return TG_ERR_ARG;   // the int8 form is mul1's
   if (!L->codes || !L->scales || !L->sign_in || !L->sign_out) return TG_ERR_NULL;
   if (misaligned(L->codes, 16) || misaligned(L->scales, 2) || misaligned(L->sign_in, 4) ||
       misaligned(L->sign_out, 4))
@@ -103,7 +108,7 @@ int gemv_splits(int m, int n, int forced) {
 // tiles.
 int gemm_splits(int m, int n, int M, int k_bits, int code_id, int forced) {
   const int ob = m / kBlock;
-  const int nsub = n / (code_id == 0 ? kBlock : 2 * kBlock);
+  const int nsub = n / (code_id == 1 ? 2 * kBlock : kBlock);
   int s = forced;
   if (s <= 0) {
     s = (256 + ob / 2) / ob;                                     // about 256 workgroups
@@ -170,6 +175,7 @@ int32_t grouped_geometry(const tg_layer* layers, int32_t n_layers, int32_t n_sel
     const int32_t st = check_layer(&layers[i]);
     if (st != TG_OK) return st;
     if (layers[i].flags != flags || layers[i].splits != layers[0].splits) return TG_ERR_ARG;
+    if ((layers[i].flags & TG_FLAG_INT8_ACT) != 0) return TG_ERR_ARG;   // batch-1 and fused paths only
     if (layers[i].m > max_m) max_m = layers[i].m;
     if (layers[i].n > max_n) max_n = layers[i].n;
   }
@@ -264,7 +270,7 @@ TG_API int32_t trellis_gemv(const tg_layer* L, const uint16_t* x, float* y, void
   a.hg = nullptr;
   a.hu = nullptr;
   return launch_status(
-      launch_gemv(a, L->k_bits, L->code_id, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
+      launch_gemv(a, L->k_bits, kernel_form(L), (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -345,7 +351,7 @@ TG_API int32_t trellis_gemv_noalloc(const tg_layer* L, const uint16_t* x, float*
   a.splits = splits;
   a.hg = nullptr;
   a.hu = nullptr;
-  return launch_status(launch_gemv(a, L->k_bits, L->code_id, (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, s));
+  return launch_status(launch_gemv(a, L->k_bits, kernel_form(L), (L->flags & TG_FLAG_ROUND_WEIGHTS) != 0, s));
 }
 
 // ---------------------------------------------------------------------------
@@ -450,7 +456,7 @@ TG_API int32_t trellis_gemv_fused(const tg_layer* layers, int32_t n_layers, cons
   a.upw = g.upw;
   a.total_units = g.total_units;
   a.max_contrib = g.max_contrib;
-  return launch_status(launch_fused(a, layers[0].k_bits, layers[0].code_id,
+  return launch_status(launch_fused(a, layers[0].k_bits, kernel_form(&layers[0]),
                                     (layers[0].flags & TG_FLAG_ROUND_WEIGHTS) != 0, g.grid, (hipStream_t)stream));
 }
 
@@ -458,6 +464,7 @@ TG_API int32_t trellis_gemm_small(const tg_layer* L, int32_t M, const uint16_t* 
                                   int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_layer(L);
   if (st != TG_OK) return st;
+  if ((L->flags & TG_FLAG_INT8_ACT) != 0) return TG_ERR_ARG;   // batch-1 and fused paths only
   if (M < 1 || M > 64) return TG_ERR_SHAPE;
   if (!X || !Y) return TG_ERR_NULL;
   if (ldx < L->n || ldy < L->m) return TG_ERR_ARG;
@@ -532,7 +539,7 @@ TG_API int32_t trellis_gemv_grouped(const tg_layer* layers, const tg_layer* d_la
 
 TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) {
   if (!L) return TG_ERR_NULL;
-  if (L->code_id != 0 && L->code_id != 1) return TG_ERR_CODE_ID;
+  if (L->code_id < 0 || L->code_id > 2) return TG_ERR_CODE_ID;
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || L->m % kTile != 0 || L->n % kTile != 0 || L->m > (1 << 22) || L->n > (1 << 22))
     return TG_ERR_SHAPE;
@@ -542,18 +549,20 @@ TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) 
   return launch_status(launch_decode(L->codes, w_out, L->m, L->n, L->k_bits, L->code_id, (hipStream_t)stream));
 }
 
-TG_API int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t workgroups, int32_t steps, float* out,
-                                 void* stream) {
-  if (code_id != 0 && code_id != 1) return TG_ERR_CODE_ID;
+TG_API int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t flags, int32_t workgroups, int32_t steps,
+                                 float* out, void* stream) {
+  if (code_id < 0 || code_id > 2) return TG_ERR_CODE_ID;
+  if ((flags & ~TG_FLAG_INT8_ACT) != 0 || ((flags & TG_FLAG_INT8_ACT) != 0 && code_id != 2)) return TG_ERR_ARG;
   if (k_bits < 1 || k_bits > 8) return TG_ERR_KBITS;
   if (workgroups < 1 || workgroups > 65535 || steps < 1 || steps > (1 << 20)) return TG_ERR_ARG;
   if (!out) return TG_ERR_NULL;
   if (misaligned(out, 4)) return TG_ERR_ALIGN;
-  return launch_status(launch_decode_ceiling(k_bits, code_id, workgroups, steps, out, (hipStream_t)stream));
+  const int form = (flags & TG_FLAG_INT8_ACT) != 0 ? kCodeMul1I8 : code_id;
+  return launch_status(launch_decode_ceiling(k_bits, form, workgroups, steps, out, (hipStream_t)stream));
 }
 
 TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
-  if (code_id != 0 && code_id != 1) return TG_ERR_CODE_ID;
+  if (code_id < 0 || code_id > 2) return TG_ERR_CODE_ID;
   if (!out) return TG_ERR_NULL;
   if (misaligned(out, 2)) return TG_ERR_ALIGN;
   return launch_status(launch_code_table(code_id, out, (hipStream_t)stream));
@@ -562,7 +571,7 @@ TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
 namespace {
 
 int32_t check_encode(int32_t n_tiles, int32_t k_bits, int32_t code_id, float scale) {
-  if (code_id != 0 && code_id != 1) return TG_ERR_CODE_ID;
+  if (code_id < 0 || code_id > 2) return TG_ERR_CODE_ID;
   if (k_bits < 1 || k_bits > 8 || (code_id == 1 && k_bits > 4)) return TG_ERR_KBITS;
   if (n_tiles < 1 || n_tiles > (1 << 24)) return TG_ERR_SHAPE;
   if (!(scale > 0.f) || !(scale < 3.0e38f)) return TG_ERR_ARG;
@@ -632,6 +641,7 @@ TG_API int32_t trellis_gemm_prefill(const tg_layer* L, int32_t M, const uint16_t
                                     int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_layer(L);
   if (st != TG_OK) return st;
+  if ((L->flags & TG_FLAG_INT8_ACT) != 0) return TG_ERR_ARG;   // batch-1 and fused paths only
   if (M < 1 || M > 65535 || (int64_t)L->m * L->n > kMaxDenseWeights) return TG_ERR_SHAPE;
   if (!X || !Y) return TG_ERR_NULL;
   if (ldx < L->n || ldy < L->m || ldy > 0x7fffffff) return TG_ERR_ARG;

@@ -53,7 +53,11 @@ struct EncGeom {
 template <int CODE>
 __device__ __forceinline__ float state_error(uint32_t s, float alpha, float v0, float v1, const CodeRegs& cr) {
   const uint32_t u = code_halves(s, cr);
-  if constexpr (CODE == 0) {
+  if constexpr (CODE == 2) {
+    const float w = (float)mul1_level(mul1_bytes(s)) * kMul1Step;   // exact
+    const float e = alpha * w - v0;
+    return e * e;
+  } else if constexpr (CODE == 0) {
     const float w = (float)halves_sum_rne(u);
     const float e = alpha * w - v0;
     return e * e;
@@ -79,7 +83,7 @@ template <int B, int CODE>
 __device__ int viterbi_pass(const float* tgt, float alpha, int rot, int start, float* const (&Mb)[2],
                             uint32_t* __restrict__ bp, float& end_cost, uint32_t& end_state) {
   using G = EncGeom<B>;
-  constexpr int V = CODE == 0 ? 1 : 2;
+  constexpr int V = CODE == 1 ? 2 : 1;
   constexpr int T = 256 / V;
   constexpr bool INPLACE = B == 1;
   constexpr int EPJ = G::NE / G::NJ;          // entries sharing one u >> B
@@ -176,7 +180,7 @@ template <int K, int CODE>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(const float* __restrict__ targets, float alpha,
                                                              int n_tiles, uint32_t* __restrict__ codes,
                                                              float* __restrict__ sq_err, uint32_t* __restrict__ ws) {
-  constexpr int V = CODE == 0 ? 1 : 2;
+  constexpr int V = CODE == 1 ? 2 : 1;
   constexpr int B = V * K;
   constexpr int T = 256 / V;
   constexpr int WPT = 8 * K;
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(const float* __rest
 
 template <int K, int CODE>
 size_t encode_lds_bytes() {
-  constexpr int B = (CODE == 0 ? 1 : 2) * K;
+  constexpr int B = (CODE == 1 ? 2 : 1) * K;
   return (size_t)EncGeom<B>::NU * 4 * (B == 1 ? 1 : 2) + 256 * 4 + 32 * 4 + 8 * K * 4 + 8;
 }
 
@@ -276,8 +280,8 @@ static hipError_t launch_enc(const float* targets, float alpha, int n_tiles, uin
 }
 
 size_t encode_ws_words_per_slot(int k_bits, int code_id) {
-  const int B = (code_id == 0 ? 1 : 2) * k_bits;
-  const int T = code_id == 0 ? 256 : 128;
+  const int B = (code_id == 1 ? 2 : 1) * k_bits;
+  const int T = code_id == 1 ? 128 : 256;
   const int NU = 1 << (16 - B);
   const int NE = NU >= kEncThreads ? NU / kEncThreads : 1;
   return (size_t)T * (NU / NE);
@@ -285,26 +289,25 @@ size_t encode_ws_words_per_slot(int k_bits, int code_id) {
 
 hipError_t launch_encode(const float* targets, float alpha, int n_tiles, int k_bits, int code_id, uint32_t* codes,
                          float* sq_err, uint32_t* ws, int slots, hipStream_t s) {
+#define TG_CASE(K, C) \
+  case K: return launch_enc<K, C>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
   if (code_id == 0) {
     switch (k_bits) {
-      case 1: return launch_enc<1, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-      case 2: return launch_enc<2, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-      case 3: return launch_enc<3, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-      case 4: return launch_enc<4, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-      case 5: return launch_enc<5, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-      case 6: return launch_enc<6, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-      case 7: return launch_enc<7, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-      case 8: return launch_enc<8, 0>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
+      TG_CASE(1, 0) TG_CASE(2, 0) TG_CASE(3, 0) TG_CASE(4, 0) TG_CASE(5, 0) TG_CASE(6, 0) TG_CASE(7, 0) TG_CASE(8, 0)
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (code_id == 2) {
+    switch (k_bits) {
+      TG_CASE(1, 2) TG_CASE(2, 2) TG_CASE(3, 2) TG_CASE(4, 2) TG_CASE(5, 2) TG_CASE(6, 2) TG_CASE(7, 2) TG_CASE(8, 2)
       default: return hipErrorInvalidValue;
     }
   }
   switch (k_bits) {
-    case 1: return launch_enc<1, 1>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-    case 2: return launch_enc<2, 1>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-    case 3: return launch_enc<3, 1>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
-    case 4: return launch_enc<4, 1>(targets, alpha, n_tiles, codes, sq_err, ws, slots, s);
+    TG_CASE(1, 1) TG_CASE(2, 1) TG_CASE(3, 1) TG_CASE(4, 1)
     default: return hipErrorInvalidValue;
   }
+#undef TG_CASE
 }
 
 }  // namespace tg

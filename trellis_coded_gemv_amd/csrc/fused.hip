@@ -35,10 +35,12 @@ namespace tg {
 // block of an odd block count is zero), 8 lanes per block, 64 blocks per pass
 // of the workgroup's 512 threads. `raw` holds this lane's raw inputs of the
 // first pass (loaded early by the caller); later passes load their own.
+// The int8 form (mul1 with int8 activations) also writes each tile column's
+// bias (xbias) and each block's factor (xfac).
 template <int CODE, bool ROUND>
 __device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
-                                                int nb, int nbp, X16 raw, uint32_t* xx) {
-  constexpr int XB = (CODE == 0 ? 16 : 8) * 8;   // input words per 128-block
+                                                int nb, int nbp, X16 raw, uint32_t* xx, int32_t* xbias, float* xfac) {
+  constexpr int XB = (CODE == 1 ? 8 : 16) * 8;   // input words per 128-block
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int xs = lane & 7;
   for (int pass = 0; pass * 64 < nbp; ++pass) {
@@ -46,11 +48,29 @@ __device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, 
     const int first = (xb < nb ? xb : nb - 1) * kBlock + 16 * xs;
     if (pass > 0) raw = load_x16(x, sign_in, first);
     const bool active = xb < nbp, live = xb < nb;
+    if constexpr (CODE == kCodeMul1I8) {
+      int32_t q[16];
+      int e;
+      x16_int8(raw, first, lane, q, e);
+      if (active) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) q[j] = live ? q[j] : 0;
+        uint32_t* dst = xx + xb * XB + 16 * xs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          reinterpret_cast<u32x4*>(dst)[i] =
+              u32x4{int8_word(q[4 * i]), int8_word(q[4 * i + 1]), int8_word(q[4 * i + 2]), int8_word(q[4 * i + 3])};
+        xbias[xb * 8 + xs] = int8_bias(q);
+        if (xs == 0) xfac[xb] = live ? int8_factor(e) : 0.f;
+      }
+      __syncthreads();
+      continue;
+    }
     float* sc = reinterpret_cast<float*>(xx) + xb * kBlock;
     float e[8], o[8];
     {
       float v[16];
-      x16_phase1(raw, first, v);
+      x16_phase1<CODE == kCodeMul1>(raw, first, v);
       if (active) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -72,6 +92,9 @@ __device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, 
         if constexpr (CODE == 0) {
           const uint32_t he = pack_half2(e[j], e[j]), ho = pack_half2(o[j], o[j]);
           *reinterpret_cast<u32x2*>(xx + xb * XB + 16 * j + 2 * xs) = u32x2{he, ho};
+        } else if constexpr (CODE == kCodeMul1) {
+          *reinterpret_cast<u32x2*>(xx + xb * XB + 16 * j + 2 * xs) =
+              u32x2{__builtin_bit_cast(uint32_t, e[j]), __builtin_bit_cast(uint32_t, o[j])};
         } else if constexpr (ROUND) {
           xx[xb * XB + 8 * j + xs] = pack_half2(e[j], o[j]);
         } else {
@@ -93,7 +116,7 @@ __device__ __forceinline__ int fused_layer_of(const FusedArgs& a, int u) {
 template <int K, int CODE, bool ROUND>
 __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   constexpr int NW = 2 * K;
-  constexpr int NX = CODE == 0 ? 16 : 8;
+  constexpr int NX = CODE == 1 ? 8 : 16;
   constexpr int PF = TG_FUSED_PF;
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63, wave = wave_id();   // wave = tile row within the block
@@ -109,6 +132,10 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   uint32_t* xx1 = lds + buf_words;
   float* ybuf = reinterpret_cast<float*>(lds + 2 * buf_words);    // [128]
   uint32_t* flag = lds + 2 * buf_words + kBlock;                   // [2]
+  int32_t* xbias0 = reinterpret_cast<int32_t*>(flag + 4);          // int8 form: [nbp * 8] per layer
+  int32_t* xbias1 = xbias0 + nbp * 8;
+  float* xfac0 = reinterpret_cast<float*>(xbias1 + nbp * 8);       // int8 form: [nbp] per layer
+  float* xfac1 = xfac0 + nbp;
 
   // Raw inputs of the first transform pass, before the code prefetch (loads complete in order).
   const int xfirst = ((8 * wave + (lane >> 3)) < nb ? (8 * wave + (lane >> 3)) : nb - 1) * kBlock + 16 * (lane & 7);
@@ -133,13 +160,15 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(u0 + p, buf[p]);
 
-  fused_transform<CODE, ROUND>(a.x, a.L[lay0].sign_in, nb, nbp, raw0, xx0);
-  if (lay1 != lay0) fused_transform<CODE, ROUND>(a.x, a.L[lay1].sign_in, nb, nbp, raw1, xx1);
+  fused_transform<CODE, ROUND>(a.x, a.L[lay0].sign_in, nb, nbp, raw0, xx0, xbias0, xfac0);
+  if (lay1 != lay0) fused_transform<CODE, ROUND>(a.x, a.L[lay1].sign_in, nb, nbp, raw1, xx1, xbias1, xfac1);
 
   const CodeRegs cr;
   // The current block segment: layer l, output block ob, units [seg_u0, seg_end).
   int l = lay0, ob = 0, seg_u0 = u0, seg_end = u0, count = 1;
   const uint32_t* xx = xx0;
+  const int32_t* xbias = xbias0;
+  const float* xfac = xfac0;
   auto start_segment = [&](int u) {
     l = fused_layer_of(a, u);
     ob = (u - a.L[l].unit0) / spr;
@@ -147,6 +176,8 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
     const int e = seg_u0 + spr;
     seg_end = e < u1 ? e : u1;
     xx = l == lay0 ? xx0 : xx1;
+    xbias = l == lay0 ? xbias0 : xbias1;
+    xfac = l == lay0 ? xfac0 : xfac1;
     count = (seg_u0 + spr - 1) / a.upw - seg_u0 / a.upw + 1;       // workgroups contributing to the block
   };
   start_segment(u0);
@@ -216,10 +247,13 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
       const bool live = u < u1;
       if (live) {
         uint32_t xv[NX];
-        read_xx(xx, (u - seg_u0) * 16 + jslot, xv);
+        const int tile = (u - seg_u0) * 16 + jslot;
+        read_xx(xx, tile, xv);
         const uint32_t nbw = quad_rotate_next(buf[p][0]);
         if constexpr (CODE == 0) decode_dot_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
-        else decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
+        else if constexpr (CODE == 1) decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
+        else if constexpr (CODE == kCodeMul1) decode_dot_mul1_64<K>(buf[p], nbw, xv, acc);
+        else decode_dot_mul1_i8_64<K>(buf[p], nbw, xv, xbias[tile], xfac[tile >> 3], acc);
       }
       issue(u + PF, buf[p]);     // refill after use; past the run: the dummy line
       if (live && u + 1 == seg_end) {
@@ -233,14 +267,14 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   }
 }
 
-size_t fused_lds_bytes(int n) {
+size_t fused_lds_bytes(int n, bool int8) {
   const int nbp = ((n >> 7) + 1) & ~1;
-  return (size_t)2 * nbp * kBlock * 4 + kBlock * 4 + 16;
+  return (size_t)2 * nbp * kBlock * 4 + kBlock * 4 + 16 + (int8 ? (size_t)2 * nbp * 9 * 4 : 0);
 }
 
 template <int K, int CODE, bool ROUND>
 static hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
-  const size_t lds = fused_lds_bytes(a.n);
+  const size_t lds = fused_lds_bytes(a.n, CODE == kCodeMul1I8);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_kernel<K, CODE, ROUND>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((fused_kernel<K, CODE, ROUND>), dim3(grid), dim3(512), lds, s, a);
@@ -262,10 +296,16 @@ static hipError_t launch_fused_k(const FusedArgs& a, int k_bits, int grid, hipSt
   }
 }
 
-hipError_t launch_fused(const FusedArgs& a, int k_bits, int code_id, bool round_weights, int grid, hipStream_t s) {
-  if (code_id == 0)
-    return round_weights ? launch_fused_k<0, true>(a, k_bits, grid, s) : launch_fused_k<0, false>(a, k_bits, grid, s);
-  return round_weights ? launch_fused_k<1, true>(a, k_bits, grid, s) : launch_fused_k<1, false>(a, k_bits, grid, s);
+hipError_t launch_fused(const FusedArgs& a, int k_bits, int variant, bool round_weights, int grid, hipStream_t s) {
+  switch (variant) {
+    case 0:
+      return round_weights ? launch_fused_k<0, true>(a, k_bits, grid, s) : launch_fused_k<0, false>(a, k_bits, grid, s);
+    case 1:
+      return round_weights ? launch_fused_k<1, true>(a, k_bits, grid, s) : launch_fused_k<1, false>(a, k_bits, grid, s);
+    case kCodeMul1: return launch_fused_k<kCodeMul1, false>(a, k_bits, grid, s);
+    case kCodeMul1I8: return launch_fused_k<kCodeMul1I8, false>(a, k_bits, grid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tg

@@ -38,6 +38,9 @@
 // the MFMA forms a (x~0 - x~1) + b (x~0 + x~1) = (a + b) x~0 + (b - a) x~1.
 // TG_FLAG_ROUND_WEIGHTS pairs the rounded weights (RNE(a+b), RNE(b-a)) with
 // the plain input pairs (x~0, x~1).
+//
+// mul1 (code_id 2): the geometry of code 0, with the exact fp16 weight in the
+// lo slot of each B word and 0 in the hi slot, as code 0's rounded form.
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
@@ -87,8 +90,8 @@ __global__ __launch_bounds__(64) void xt_prep_kernel(const uint16_t* __restrict_
 // Geometry of one MFMA step per code.
 template <int K, int CODE>
 struct MfmaGeom {
-  static constexpr int SPAN = CODE == 0 ? 1 : 2;          // tile columns per MFMA step
-  static constexpr int STEP = CODE == 0 ? K : 2 * K;      // stream bits between a lane's 4 windows
+  static constexpr int SPAN = CODE != 1 ? 1 : 2;          // tile columns per MFMA step
+  static constexpr int STEP = CODE != 1 ? K : 2 * K;      // stream bits between a lane's 4 windows
   static constexpr int WPT = 8 * K;                       // code words per tile
   static constexpr int LW = SPAN * K;                     // code words a lane loads per step
   static constexpr int NLW = 3 * STEP > 16 ? 3 : 2;       // staged words a lane reads per tile
@@ -133,8 +136,8 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
   const int lane = threadIdx.x & 63;
   const int jrow = lane & 15, g = lane >> 4;
   // first stream bit of the lane's four windows, and the tile of the step they lie in
-  const int b0 = CODE == 0 ? K * (16 * jrow + 4 * g) : 2 * K * (8 * jrow + 4 * (g & 1));
-  const int toff = CODE == 0 ? 0 : (g >> 1) * WPT;
+  const int b0 = CODE != 1 ? K * (16 * jrow + 4 * g) : 2 * K * (8 * jrow + 4 * (g & 1));
+  const int toff = CODE != 1 ? 0 : (g >> 1) * WPT;
   const int q0 = b0 & 31, j0 = b0 >> 5;
   int widx[NLW];
   uint32_t shift;
@@ -156,13 +159,13 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
   const uint32_t* __restrict__ cptr =
       a.codes + ((size_t)(ob * 8 + tl) * n16 + (size_t)col0 * SPAN) * WPT + (lane & 7) * LW;
   // x~ of this lane: row jrow (+16 per row block), input columns 4g..4g+3 of the step
-  const uint32_t* __restrict__ xptr = CODE == 0 ? a.xt + ((size_t)col0 * a.mpad + jrow) * 8 + 2 * g
+  const uint32_t* __restrict__ xptr = CODE != 1 ? a.xt + ((size_t)col0 * a.mpad + jrow) * 8 + 2 * g
                                                 : a.xt + (size_t)jrow * xrow + 4 * g + (size_t)col0 * 16;
-  const size_t xmb = CODE == 0 ? 128 : 16 * xrow;   // words between 16-row blocks
+  const size_t xmb = CODE != 1 ? 128 : 16 * xrow;   // words between 16-row blocks
   const uint32_t* __restrict__ cfirst = cptr;
   const uint32_t* __restrict__ xfirst = xptr;
   const size_t cadv = (size_t)cstep * SPAN * WPT;
-  const size_t xadv = CODE == 0 ? (size_t)cstep * a.mpad * 8 : (size_t)cstep * 16;
+  const size_t xadv = CODE != 1 ? (size_t)cstep * a.mpad * 8 : (size_t)cstep * 16;
 
   // Prefetch ring; out-of-range steps re-read the first step (valid addresses,
   // and every path issues the same loads so the waits stay exact).
@@ -175,7 +178,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
     const uint32_t* xq = ok ? xptr : xfirst;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      if constexpr (CODE == 0) {   // four fp16 values; paired up at use
+      if constexpr (CODE != 1) {   // four fp16 values; paired up at use
         const u32x2 v = *reinterpret_cast<const u32x2*>(xq + (size_t)mb * xmb);
         xd[mb] = u32x4{v.x, v.y, 0u, 0u};
       } else {
@@ -198,7 +201,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
         u32x4 av[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          if constexpr (CODE == 0) {
+          if constexpr (CODE != 1) {
             const uint32_t d0 = xa[p][mb].x, d1 = xa[p][mb].y;
             av[mb] = u32x4{__builtin_amdgcn_perm(d0, d0, 0x01000100u), __builtin_amdgcn_perm(d0, d0, 0x03020302u),
                            __builtin_amdgcn_perm(d1, d1, 0x01000100u), __builtin_amdgcn_perm(d1, d1, 0x03020302u)};
@@ -228,7 +231,8 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
             const int P = STEP * e;
             const uint32_t st = P <= 16 ? ubfe(r1, 16 - P, 16) : ubfe(alignbit(r1, r2, 48 - P), 0, 16);
             const uint32_t u = code_halves(st, cr);
-            if constexpr (!ROUND) bw[tt][e] = u;
+            if constexpr (CODE == 2) bw[tt][e] = (uint32_t)mul1_weight_bits(st);   // (w, 0) against (x~, x~)
+            else if constexpr (!ROUND) bw[tt][e] = u;
             else if constexpr (CODE == 0) bw[tt][e] = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
             else bw[tt][e] = pair_weights_rne(u);
           }
@@ -384,7 +388,7 @@ static void launch_mb(const GemmArgs& a, hipStream_t s) {
 template <int CODE>
 static hipError_t launch_code(const GemmArgs& a, int k_bits, bool round_weights, hipStream_t s) {
 #define TG_CASE(K) \
-  case K: round_weights ? launch_mb<K, CODE, true>(a, s) : launch_mb<K, CODE, false>(a, s); break;
+  case K: round_weights && CODE != 2 ? launch_mb<K, CODE, CODE != 2>(a, s) : launch_mb<K, CODE, false>(a, s); break;
   switch (k_bits) {
     TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
     default: return hipErrorInvalidValue;
@@ -395,11 +399,12 @@ static hipError_t launch_code(const GemmArgs& a, int k_bits, bool round_weights,
 
 hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in, int k_bits,
                              int code_id, bool round_weights, hipStream_t s) {
-  const int mode = code_id == 0 ? 0 : (round_weights ? 2 : 1);
+  const int mode = code_id == 1 ? (round_weights ? 2 : 1) : 0;
   hipLaunchKernelGGL(xt_prep_kernel, dim3(a.n / kBlock, a.mpad), dim3(64), 0, s, X, ldx, sign_in,
                      const_cast<uint32_t*>(a.xt), a.n, a.M, mode);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (code_id == 2) return launch_code<2>(a, k_bits, false, s);
   return code_id == 0 ? launch_code<0>(a, k_bits, round_weights, s) : launch_code<1>(a, k_bits, round_weights, s);
 }
 

@@ -59,8 +59,9 @@ constexpr int gemv_pf() { return K <= 4 ? TG_GEMV_PF_SMALL_K : 2; }
 // arrived, and the partials travel in call-tagged slots (tg_device.hpp).
 template <int K, int CODE, bool ROUND, int PF, int P, bool GATED = false>
 __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int split, uint32_t* lds) {
+  static_assert(!(GATED && CODE == kCodeMul1I8), "the gated input has no int8 form");
   constexpr int NW = 2 * K;
-  constexpr int NX = CODE == 0 ? 16 : 8;   // input words per tile column
+  constexpr int NX = CODE == 1 ? 8 : 16;   // input words per tile column
   constexpr int XB = NX * 8;               // input words per 128-block
   constexpr int WAVES = 8 * P;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -81,6 +82,8 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   float* ybuf = reinterpret_cast<float*>(lds + nsteps * 256);    // [128]
   float* red = ybuf + 128;                                       // [P-1][128]
   uint32_t* flag = lds + nsteps * 256 + 128 * P;
+  int32_t* xbias = reinterpret_cast<int32_t*>(flag + 4);          // int8 form: [2*nsteps*8] per tile column
+  float* xfac = reinterpret_cast<float*>(xbias + nsteps * 16);    // int8 form: [2*nsteps] per block
 
   uint64_t* slots = a.slots + (size_t)ob * a.splits * kBlock;   // split-K by ticket: [split][128]
 
@@ -123,14 +126,33 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   // word layout the decode loop reads. The fp32 exchange uses the x~ area
   // itself; the words are written only after every wave has read its part.
   uint32_t ticket = 0;
-  {
+  if constexpr (CODE == kCodeMul1I8) {
+    // int8 form: each lane ends with its own 16 elements, so no exchange.
+    const bool active = xb < nbp, live = xb < cb;
+    int32_t q[16];
+    int e = 0;
+    if (xwave) x16_int8(xraw, xfirst, lane, q, e);
+    __syncthreads();   // the same barriers as the other forms
+    if (a.splits > 1 && threadIdx.x == 0) ticket = take_ticket(&a.counters[ob]);
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) q[j] = live ? q[j] : 0;
+      uint32_t* dst = xx_lds + xb * XB + 16 * xs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        reinterpret_cast<u32x4*>(dst)[i] =
+            u32x4{int8_word(q[4 * i]), int8_word(q[4 * i + 1]), int8_word(q[4 * i + 2]), int8_word(q[4 * i + 3])};
+      xbias[xb * 8 + xs] = int8_bias(q);
+      if (xs == 0) xfac[xb] = live ? int8_factor(e) : 0.f;
+    }
+  } else {
     const bool active = xb < nbp, live = xb < cb;
     float* sc = reinterpret_cast<float*>(xx_lds) + xb * kBlock;
     float e[8], o[8];
     if (xwave) {
       float v[16];
       if constexpr (GATED) xraw = gated_to_x16(graw);
-      x16_phase1(xraw, xfirst, v);
+      x16_phase1<CODE == kCodeMul1>(xraw, xfirst, v);
       if (active) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -156,6 +178,9 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
         if constexpr (CODE == 0) {
           const uint32_t he = pack_half2(e[j], e[j]), ho = pack_half2(o[j], o[j]);
           *reinterpret_cast<u32x2*>(xx_lds + xb * XB + 16 * j + 2 * xs) = u32x2{he, ho};
+        } else if constexpr (CODE == kCodeMul1) {
+          *reinterpret_cast<u32x2*>(xx_lds + xb * XB + 16 * j + 2 * xs) =
+              u32x2{__builtin_bit_cast(uint32_t, e[j]), __builtin_bit_cast(uint32_t, o[j])};
         } else if constexpr (ROUND) {
           xx_lds[xb * XB + 8 * j + xs] = pack_half2(e[j], o[j]);
         } else {
@@ -183,8 +208,16 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
           read_xx(xx_lds, (kp + ls * P) * 16 + jslot, xv[0]);
         }
         const uint32_t nbw = quad_rotate_next(buf[p][0]);
-        if constexpr (CODE == 0) decode_dot_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
-        else decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
+        if constexpr (CODE == 0) {
+          decode_dot_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
+        } else if constexpr (CODE == 1) {
+          decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
+        } else if constexpr (CODE == kCodeMul1) {
+          decode_dot_mul1_64<K>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc);
+        } else {
+          const int tile = (kp + ls * P) * 16 + jslot;
+          decode_dot_mul1_i8_64<K>(buf[p], nbw, xv[p & TG_GEMV_XDB], xbias[tile], xfac[tile >> 3], acc);
+        }
       }
       issue(ls + PF, buf[p]);   // refill after use: the ring needs no register copies
     }
@@ -347,7 +380,8 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
   a.hg = GATED ? g.hin + (size_t)(2 * e) * g.hin_stride : nullptr;
   a.hu = GATED ? g.hin + (size_t)(2 * e + 1) * g.hin_stride : nullptr;
   if (L.code_id == 0) grouped_dispatch<0, ROUND, GATED>(a, L.k_bits, ob, split, lds);
-  else grouped_dispatch<1, ROUND, GATED>(a, L.k_bits, ob, split, lds);
+  else if (L.code_id == 1) grouped_dispatch<1, ROUND, GATED>(a, L.k_bits, ob, split, lds);
+  else grouped_dispatch<kCodeMul1, false, GATED>(a, L.k_bits, ob, split, lds);
 }
 
 // Router-weighted sum of the selected experts' outputs, in selection order;
@@ -389,14 +423,17 @@ static hipError_t launch_k(const GemvArgs& a, hipStream_t s) {
   const int max_chunk = (nb128 + a.splits - 1) / a.splits;
   const int grid = (a.m >> 7) * a.splits;
   hipLaunchKernelGGL((gemv_kernel<K, CODE, ROUND, PF, kGemvP>), dim3(grid), dim3(64 * 8 * kGemvP),
-                     gemv_lds_bytes(max_chunk), s, a);
+                     gemv_lds_bytes(max_chunk, CODE == kCodeMul1I8), s, a);
   return hipGetLastError();
 }
 
+// Codes 2 and 3 (mul1) have exact weights: rounding them changes nothing, so
+// they are built once, without the rounded form.
 template <int CODE>
 static hipError_t launch_code(const GemvArgs& a, int k_bits, bool round_weights, hipStream_t s) {
-#define TG_CASE(K) \
-  case K: return round_weights ? launch_k<K, CODE, true>(a, s) : launch_k<K, CODE, false>(a, s);
+#define TG_CASE(K)                                                                                \
+  case K:                                                                                         \
+    return round_weights && CODE <= 1 ? launch_k<K, CODE, CODE <= 1>(a, s) : launch_k<K, CODE, false>(a, s);
   switch (k_bits) {
     TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
     default: return hipErrorInvalidValue;
@@ -404,8 +441,14 @@ static hipError_t launch_code(const GemvArgs& a, int k_bits, bool round_weights,
 #undef TG_CASE
 }
 
-hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_weights, hipStream_t s) {
-  return code_id == 0 ? launch_code<0>(a, k_bits, round_weights, s) : launch_code<1>(a, k_bits, round_weights, s);
+hipError_t launch_gemv(const GemvArgs& a, int k_bits, int variant, bool round_weights, hipStream_t s) {
+  switch (variant) {
+    case 0: return launch_code<0>(a, k_bits, round_weights, s);
+    case 1: return launch_code<1>(a, k_bits, round_weights, s);
+    case kCodeMul1: return launch_code<kCodeMul1>(a, k_bits, false, s);
+    case kCodeMul1I8: return launch_code<kCodeMul1I8>(a, k_bits, false, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <bool ROUND, bool GATED>
@@ -446,7 +489,7 @@ hipError_t launch_moe_combine(const float* Y2, int64_t y2_stride, const int32_t*
 template <int K, int CODE>
 __global__ __launch_bounds__(512) void decode_ceiling_kernel(float* __restrict__ out, int steps, uint32_t seed) {
   constexpr int NW = 2 * K;
-  constexpr int NX = CODE == 0 ? 16 : 8;
+  constexpr int NX = CODE == 1 ? 8 : 16;
   __shared__ uint32_t xx_lds[16 * NX];
   __shared__ uint32_t words[512 * NW];
   const int tid = threadIdx.x, lane = tid & 63, jslot = lane >> 2;
@@ -467,24 +510,30 @@ __global__ __launch_bounds__(512) void decode_ceiling_kernel(float* __restrict__
     read_xx(xx_lds, jslot, xv);
     const uint32_t nbw = quad_rotate_next(w[0]);
     if constexpr (CODE == 0) decode_dot_64<K, false>(w, nbw, xv, acc, cr);
-    else decode_dot_pair_64<K, false>(w, nbw, xv, acc, cr);
+    else if constexpr (CODE == 1) decode_dot_pair_64<K, false>(w, nbw, xv, acc, cr);
+    else if constexpr (CODE == kCodeMul1) decode_dot_mul1_64<K>(w, nbw, xv, acc);
+    else decode_dot_mul1_i8_64<K>(w, nbw, xv, (int32_t)xx_lds[jslot] >> 8, 1.0f, acc);
   }
   out[(size_t)blockIdx.x * 512 + tid] = acc[0] + acc[1] + acc[2] + acc[3];
 }
 
-hipError_t launch_decode_ceiling(int k_bits, int code_id, int workgroups, int steps, float* out, hipStream_t s) {
-#define TG_CASE(K)                                                                                          \
-  case K:                                                                                                 \
-    if (code_id == 0)                                                                                     \
-      hipLaunchKernelGGL((decode_ceiling_kernel<K, 0>), dim3(workgroups), dim3(512), 0, s, out, steps, 1u); \
-    else                                                                                                  \
-      hipLaunchKernelGGL((decode_ceiling_kernel<K, 1>), dim3(workgroups), dim3(512), 0, s, out, steps, 1u); \
+hipError_t launch_decode_ceiling(int k_bits, int variant, int workgroups, int steps, float* out, hipStream_t s) {
+#define TG_LAUNCH(K, C) hipLaunchKernelGGL((decode_ceiling_kernel<K, C>), dim3(workgroups), dim3(512), 0, s, out, steps, 1u)
+#define TG_CASE(K)                                       \
+  case K:                                                \
+    switch (variant) {                                   \
+      case 0: TG_LAUNCH(K, 0); break;                    \
+      case 1: TG_LAUNCH(K, 1); break;                    \
+      case kCodeMul1: TG_LAUNCH(K, kCodeMul1); break;     \
+      default: TG_LAUNCH(K, kCodeMul1I8); break;          \
+    }                                                    \
     break;
   switch (k_bits) {
     TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
     default: return hipErrorInvalidValue;
   }
 #undef TG_CASE
+#undef TG_LAUNCH
   return hipGetLastError();
 }
 

@@ -17,23 +17,26 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t* __restrict_
   const int wpt = 8 * K;
   const uint32_t* tile = codes + ((size_t)(o >> 4) * (size_t)(n >> 4) + (size_t)(i >> 4)) * (size_t)wpt;
   const int t = 16 * (o & 15) + (i & 15);
-  const int p = code_id == 0 ? K * t : 2 * K * (t >> 1);
+  const int p = code_id == 1 ? 2 * K * (t >> 1) : K * t;
   const int j = p >> 5, q = p & 31;
   const uint64_t v = ((uint64_t)tile[j] << 32) | (uint64_t)tile[(j + 1) % wpt];
   const uint32_t state = (uint32_t)(v >> (48 - q)) & 0xFFFFu;
   const CodeRegs cr;
   const uint32_t u = code_halves(state, cr);
   if (code_id == 0) out[idx] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
+  else if (code_id == 2) out[idx] = mul1_weight_bits(state);
   else out[idx] = (uint16_t)(pair_weights_rne(u) >> (16 * (t & 1)));
 }
 
-// code_id 0: out[S] = weight of state S; code_id 1: out[2S], out[2S+1] = the state's weight pair.
+// code_id 0 and 2: out[S] = weight of state S; code_id 1: out[2S], out[2S+1] = the state's weight pair.
 __global__ __launch_bounds__(256) void code_table_kernel(uint16_t* __restrict__ out, int code_id) {
   const uint32_t s = blockIdx.x * 256 + threadIdx.x;
   const CodeRegs cr;
   const uint32_t u = code_halves(s, cr);
   if (code_id == 0) {
     out[s] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
+  } else if (code_id == 2) {
+    out[s] = mul1_weight_bits(s);
   } else {
     const uint32_t w = pair_weights_rne(u);
     out[2 * s] = (uint16_t)w;

@@ -71,6 +71,13 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint32_t* __rest
       const uint16_t b = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(window(K * (tl + 1)), cr)));
       out[tl >> 4][(tl & 15) >> 1] = (uint32_t)a | ((uint32_t)b << 16);
     }
+  } else if constexpr (CODE == 2) {
+#pragma unroll
+    for (int tl = 0; tl < 64; tl += 2) {
+      const uint16_t a = mul1_weight_bits(window(K * tl));
+      const uint16_t b = mul1_weight_bits(window(K * (tl + 1)));
+      out[tl >> 4][(tl & 15) >> 1] = (uint32_t)a | ((uint32_t)b << 16);
+    }
   } else {
 #pragma unroll
     for (int sl = 0; sl < 32; ++sl) out[sl >> 3][sl & 7] = pair_weights_rne(code_halves(window(2 * K * sl), cr));
@@ -118,6 +125,7 @@ static hipError_t launch_dec(const uint32_t* codes, uint16_t* W, int m, int n, i
 
 hipError_t launch_prefill_decode(const uint32_t* codes, uint16_t* W, int m, int n, int k_bits, int code_id,
                                  hipStream_t s) {
+  if (code_id == 2) return launch_dec<2>(codes, W, m, n, k_bits, s);
   return code_id == 0 ? launch_dec<0>(codes, W, m, n, k_bits, s) : launch_dec<1>(codes, W, m, n, k_bits, s);
 }
 

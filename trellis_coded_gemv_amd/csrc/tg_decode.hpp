@@ -137,6 +137,45 @@ __device__ __forceinline__ void decode_dot_pair_64(const uint32_t (&w)[2 * K], u
   for (int r = 0; r < 4; ++r) acc[r] = CW == 2 ? a2[r][0] + a2[r][1] : a2[r][0];
 }
 
+// mul1 (code_id 2) against x~ / 32 in fp32 (xf: 16 fp32 bit patterns, one
+// per tile column). Per weight: one window extract, v_mul_u32_u24, v_and_b32,
+// v_dot4_u32_u8 (the level as an exact integer), v_cvt_f32_i32 and one
+// v_fmac_f32. The weights are exact, so there is no rounded form.
+template <int K>
+__device__ __forceinline__ void decode_dot_mul1_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xf)[16],
+                                                   float (&acc)[4]) {
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    uint32_t b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = mul1_bytes(lane_window<K, K>(w, nb, 16 * r + c));
+    const float xc = __builtin_bit_cast(float, xf[c]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf((float)mul1_level(b[r]), xc, acc[r]);
+  }
+}
+
+// mul1 with int8 activations: decode and multiply are one v_dot4_i32_i8 of the
+// four masked code bytes against the activation's int8 in all four bytes
+// (xq), which adds level_byte_sum * q; the integer accumulators start from the
+// bias -126 sum(q) of the 16 columns, so they end at sum(level * q) exactly.
+// One fp32 multiply-add per row then applies the block factor.
+template <int K>
+__device__ __forceinline__ void decode_dot_mul1_i8_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xq)[16],
+                                                      int32_t bias, float factor, float (&acc)[4]) {
+  int32_t ai[4] = {bias, bias, bias, bias};
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    uint32_t b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = mul1_bytes(lane_window<K, K>(w, nb, 16 * r + c));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ai[r] = __builtin_amdgcn_sdot4((int32_t)b[r], (int32_t)xq[c], ai[r], false);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(factor, (float)ai[r], acc[r]);
+}
+
 // Sum acc[g] over the 16 tile slots of the wave (lane bits 2..5) with a
 // transposing reduction: the exchanges over bits 2 and 3 each halve the number
 // of values a lane carries, so 5 shuffles replace 16. On return lanes 0..15

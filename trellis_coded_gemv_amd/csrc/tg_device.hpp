@@ -174,6 +174,29 @@ __device__ __forceinline__ uint32_t pair_weights_rne(uint32_t u) {
 }
 
 // ---------------------------------------------------------------------------
+// mul1 (code_id 2; "Trellis Quantization" lecture, Parts eleven and twelve):
+// the state times the multiplier with no additive term, each product byte
+// masked to six bits, the four bytes summed and 126 subtracted; the weight is
+// that level / 32, exact in binary16.
+constexpr uint32_t kByteMask = 0x3F3F3F3Fu;
+constexpr uint32_t kByteOnes = 0x01010101u;
+constexpr int kMul1Offset = 126;
+constexpr float kMul1Step = 0.03125f;   // 1/32
+
+// Masked product bytes of a 16-bit state: v_mul_u32_u24 and v_and_b32.
+__device__ __forceinline__ uint32_t mul1_bytes(uint32_t state) { return (state * kMul) & kByteMask; }
+
+// Level = byte sum - 126 as an int32: one v_dot4_u32_u8 whose accumulator is
+// -126 (the unsigned sum wraps modulo 2^32 to the signed level).
+__device__ __forceinline__ int32_t mul1_level(uint32_t bytes) {
+  return (int32_t)__builtin_amdgcn_udot4(bytes, kByteOnes, (uint32_t)-kMul1Offset, false);
+}
+
+__device__ __forceinline__ uint16_t mul1_weight_bits(uint32_t state) {
+  return __builtin_bit_cast(uint16_t, (_Float16)((float)mul1_level(mul1_bytes(state)) * kMul1Step));
+}
+
+// ---------------------------------------------------------------------------
 // Input-side transform of many 128-blocks at once, 8 lanes per block.
 //
 // Lane s (= lane % 8 of its block) first holds elements 16s..16s+15 (one
@@ -249,11 +272,14 @@ __device__ __forceinline__ X16 gated_to_x16(const XGated16& r) {
   return x;
 }
 
-// v[j] = s[first+j] * x[first+j] / sqrt(128), then the 16-point transform over j.
+// v[j] = s[first+j] * x[first+j] * c, then the 16-point transform over j.
+// c = 1/sqrt(128), or (mul1) 1/(32 sqrt(128)), which carries the weight step:
+// a power-of-two multiple of the same constant, so the sums scale exactly.
+template <bool MUL1 = false>
 __device__ __forceinline__ void x16_phase1(const X16& r, int first, float (&v)[16]) {
   const uint32_t sb = r.sw >> (first & 16);   // bit j: sign of element first + j
   const uint32_t w[8] = {r.lo[0], r.lo[1], r.lo[2], r.lo[3], r.hi[0], r.hi[1], r.hi[2], r.hi[3]};
-  const uint32_t cbits = __builtin_bit_cast(uint32_t, kRsqrt128);
+  const uint32_t cbits = __builtin_bit_cast(uint32_t, MUL1 ? kRsqrt128 * kMul1Step : kRsqrt128);
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const uint16_t h = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
@@ -286,6 +312,76 @@ __device__ __forceinline__ void x16_phase2(float (&e)[8], float (&o)[8]) {
         o[j + h] = c - d;
       }
 }
+
+// int8 form of x~ for mul1 with int8 activations ("Trellis Quantization"
+// lecture, Part eleven). Lane s of a block's 8 consecutive lanes holds
+// elements 16s..16s+15 of the block (X16 at `first`). In float64:
+//   u = (+-1 Hadamard) diag(s_in) x -- every partial sum of binary16 values is
+//       a multiple of 2^-24 below 2^23, so each butterfly is exact and u does
+//       not depend on their order;
+//   e = the smallest integer with max|u| 2^-e <= 127 over the block (0 if the
+//       block is zero);
+//   q = round-half-even(u 2^-e), an exact power-of-two scaling.
+// Ends with q of the lane's own 16 elements and the block's e, identical in
+// every lane of the block.
+__device__ __forceinline__ void x16_int8(const X16& r, int first, int lane, int32_t (&q)[16], int& e) {
+  const uint32_t sb = r.sw >> (first & 16);
+  const uint32_t w[8] = {r.lo[0], r.lo[1], r.lo[2], r.lo[3], r.hi[0], r.hi[1], r.hi[2], r.hi[3]};
+  double v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint16_t h = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
+    const double x = (double)half_bits_to_float(h);
+    v[j] = ((sb >> j) & 1u) ? -x : x;
+  }
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & h) == 0) {
+        const double a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+  // Index bits 4..6 are lane bits 0..2 of the block's lane group.
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+    const bool upper = (lane & h) != 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const double p = __shfl_xor(v[j], h, 64);
+      v[j] = upper ? p - v[j] : v[j] + p;
+    }
+  }
+  double amax = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amax = __builtin_fmax(amax, __builtin_fabs(v[j]));
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, h, 64));
+  e = 0;
+  if (amax > 0.0) {
+    int E;
+    const double f = __builtin_frexp(amax, &E);   // amax = f 2^E, f in [1/2, 1)
+    e = f * 128.0 <= 127.0 ? E - 7 : E - 6;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) q[j] = (int32_t)__builtin_rint(__builtin_ldexp(v[j], -e));
+}
+
+// The int8 words of x16_int8's result: q repeated in all four bytes of each
+// word (for v_dot4_i32_i8 against the four masked code bytes of one weight),
+// the bias -126 sum(q) of the lane's 16 elements, and the block's fp32 factor
+// 2^e / (32 sqrt(128)) that turns the integer dot product into y~.
+__device__ __forceinline__ uint32_t int8_word(int32_t q) { return ((uint32_t)q & 0xFFu) * kByteOnes; }
+
+__device__ __forceinline__ int32_t int8_bias(const int32_t (&q)[16]) {
+  int32_t t = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t += q[j];
+  return -kMul1Offset * t;
+}
+
+__device__ __forceinline__ float int8_factor(int e) { return __builtin_ldexpf(kRsqrt128 * kMul1Step, e); }
 
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |

@@ -15,6 +15,10 @@ constexpr int kGemvThreads = 64 * kGemvWaves;
 #define TG_GEMV_P 1
 #endif
 constexpr int kGemvP = TG_GEMV_P;        // batch-1 path: waves per tile row (interleaved steps)
+// Kernel forms of the codes: code_id 0 and 1 as they are; code_id 2 (mul1)
+// against fp32 x~, and against the int8 form of x~ (TG_FLAG_INT8_ACT).
+constexpr int kCodeMul1 = 2;
+constexpr int kCodeMul1I8 = 3;
 constexpr int kMaxChunkBlocks = 64;      // 128-blocks of x~ held in LDS by one GEMV workgroup
 constexpr size_t kWsHeader = 256;        // every workspace starts with this header; word 0 = status
 constexpr uint32_t kStatusSplitkTimeout = 1u;   // a split-K wait ran out (its outputs were written as NaN)
@@ -98,7 +102,7 @@ struct GemmArgs {
 hipError_t launch_gemv(const GemvArgs& a, int k_bits, int code_id, bool round_weights, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, int max_ob, int max_n, hipStream_t s);
 hipError_t launch_fused(const FusedArgs& a, int k_bits, int code_id, bool round_weights, int grid, hipStream_t s);
-size_t fused_lds_bytes(int n);
+size_t fused_lds_bytes(int n, bool int8);
 hipError_t launch_decode_ceiling(int k_bits, int code_id, int workgroups, int steps, float* out, hipStream_t s);
 hipError_t launch_moe_combine(const float* Y2, int64_t y2_stride, const int32_t* sel, const float* w, int top_k,
                               int n_experts, int hidden, float* y, hipStream_t s);
@@ -121,10 +125,12 @@ constexpr int kEncMaxSlots = 256;        // encoder workgroups in flight (one ti
 
 // LDS bytes a GEMV workgroup needs for a chunk of `chunk_blocks` 128-blocks.
 // The x~ region doubles as [8P][128] fp32 per-wave sums in the final reduction.
-inline size_t gemv_lds_bytes(int chunk_blocks) {
+// int8: the int8 form's bias (8 words) and factor (1 word) per block follow.
+inline size_t gemv_lds_bytes(int chunk_blocks, bool int8 = false) {
   int padded_blocks = (chunk_blocks + 1) & ~1;   // steps cover 2 blocks
   if (padded_blocks < 8 * kGemvP) padded_blocks = 8 * kGemvP;
-  return (size_t)padded_blocks * kBlock * 4 + (size_t)kBlock * 4 * kGemvP + 16;
+  return (size_t)padded_blocks * kBlock * 4 + (size_t)kBlock * 4 * kGemvP + 16 +
+         (int8 ? (size_t)padded_blocks * 9 * 4 : 0);
 }
 
 }  // namespace tg
