@@ -49,18 +49,22 @@ __device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, 
     if (pass > 0) raw = load_x16(x, sign_in, first);
     const bool active = xb < nbp, live = xb < nb;
     if constexpr (CODE == kCodeMul1I8) {
-      int32_t q[16];
+      int32_t qe[8], qo[8];
       int e;
-      x16_int8(raw, first, lane, q, e);
+      {
+        double v[16], de[8], dof[8];
+        x16_int8_phase1(raw, first, v);
+        int8_exchange(xx + xb * kBlock, xs, active, live, v, de, dof);
+        x16_int8_phase2(de, dof);
+        int8_quantize(de, dof, qe, qo, e);
+      }
+      const int32_t bias = int8_group_bias(qe, qo, lane);
+      __syncthreads();   // every wave has read its exchange values before the area is overwritten
       if (active) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) q[j] = live ? q[j] : 0;
-        uint32_t* dst = xx + xb * XB + 16 * xs;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          reinterpret_cast<u32x4*>(dst)[i] =
-              u32x4{int8_word(q[4 * i]), int8_word(q[4 * i + 1]), int8_word(q[4 * i + 2]), int8_word(q[4 * i + 3])};
-        xbias[xb * 8 + xs] = int8_bias(q);
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<u32x2*>(xx + xb * XB + 16 * j + 2 * xs) = u32x2{int8_word(qe[j]), int8_word(qo[j])};
+        xbias[xb * 8 + xs] = bias;
         if (xs == 0) xfac[xb] = live ? int8_factor(e) : 0.f;
       }
       __syncthreads();

@@ -127,22 +127,25 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   // itself; the words are written only after every wave has read its part.
   uint32_t ticket = 0;
   if constexpr (CODE == kCodeMul1I8) {
-    // int8 form: each lane ends with its own 16 elements, so no exchange.
+    // int8 form: exact float64 transform, exchanged through the block's x~ area in two halves.
     const bool active = xb < nbp, live = xb < cb;
-    int32_t q[16];
+    int32_t qe[8], qo[8], bias = 0;
     int e = 0;
-    if (xwave) x16_int8(xraw, xfirst, lane, q, e);
-    __syncthreads();   // the same barriers as the other forms
+    if (xwave) {
+      double v[16], de[8], dof[8];
+      x16_int8_phase1(xraw, xfirst, v);
+      int8_exchange(xx_lds + xb * kBlock, xs, active, live, v, de, dof);
+      x16_int8_phase2(de, dof);
+      int8_quantize(de, dof, qe, qo, e);
+      bias = int8_group_bias(qe, qo, lane);
+    }
+    __syncthreads();   // every wave has read its exchange values
     if (a.splits > 1 && threadIdx.x == 0) ticket = take_ticket(&a.counters[ob]);
     if (active) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) q[j] = live ? q[j] : 0;
-      uint32_t* dst = xx_lds + xb * XB + 16 * xs;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        reinterpret_cast<u32x4*>(dst)[i] =
-            u32x4{int8_word(q[4 * i]), int8_word(q[4 * i + 1]), int8_word(q[4 * i + 2]), int8_word(q[4 * i + 3])};
-      xbias[xb * 8 + xs] = int8_bias(q);
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<u32x2*>(xx_lds + xb * XB + 16 * j + 2 * xs) = u32x2{int8_word(qe[j]), int8_word(qo[j])};
+      xbias[xb * 8 + xs] = bias;
       if (xs == 0) xfac[xb] = live ? int8_factor(e) : 0.f;
     }
   } else {

@@ -314,20 +314,20 @@ __device__ __forceinline__ void x16_phase2(float (&e)[8], float (&o)[8]) {
 }
 
 // int8 form of x~ for mul1 with int8 activations ("Trellis Quantization"
-// lecture, Part eleven). Lane s of a block's 8 consecutive lanes holds
-// elements 16s..16s+15 of the block (X16 at `first`). In float64:
+// lecture, Part eleven), in float64:
 //   u = (+-1 Hadamard) diag(s_in) x -- every partial sum of binary16 values is
 //       a multiple of 2^-24 below 2^23, so each butterfly is exact and u does
 //       not depend on their order;
 //   e = the smallest integer with max|u| 2^-e <= 127 over the block (0 if the
 //       block is zero);
 //   q = round-half-even(u 2^-e), an exact power-of-two scaling.
-// Ends with q of the lane's own 16 elements and the block's e, identical in
-// every lane of the block.
-__device__ __forceinline__ void x16_int8(const X16& r, int first, int lane, int32_t (&q)[16], int& e) {
+// The layout follows the fp32 transform: x16_int8_phase1 takes the lane's 16
+// elements 16s..16s+15 through the butterflies over index bits 0..3; one
+// exchange through LDS (two rounds of 32-bit halves) gives the lane elements
+// 16j + 2s and 16j + 2s + 1 (e[j], o[j]); x16_int8_phase2 runs the bits 4..6.
+__device__ __forceinline__ void x16_int8_phase1(const X16& r, int first, double (&v)[16]) {
   const uint32_t sb = r.sw >> (first & 16);
   const uint32_t w[8] = {r.lo[0], r.lo[1], r.lo[2], r.lo[3], r.hi[0], r.hi[1], r.hi[2], r.hi[3]};
-  double v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const uint16_t h = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
@@ -343,43 +343,108 @@ __device__ __forceinline__ void x16_int8(const X16& r, int first, int lane, int3
         v[j] = a + b;
         v[j + h] = a - b;
       }
-  // Index bits 4..6 are lane bits 0..2 of the block's lane group.
+}
+
+__device__ __forceinline__ void x16_int8_phase2(double (&e)[8], double (&o)[8]) {
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-    const bool upper = (lane & h) != 0;
+  for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const double p = __shfl_xor(v[j], h, 64);
-      v[j] = upper ? p - v[j] : v[j] + p;
+    for (int j = 0; j < 8; ++j)
+      if ((j & h) == 0) {
+        const double a = e[j], b = e[j + h];
+        e[j] = a + b;
+        e[j + h] = a - b;
+        const double c = o[j], d = o[j + h];
+        o[j] = c + d;
+        o[j + h] = c - d;
+      }
+}
+
+// Exchange of the 16 float64 values of each lane of a block's 8 lanes through
+// the block's 128-word LDS area `sc` (write: the lane's 16 values; read: the
+// values of elements 16j + 2s, 16j + 2s + 1), one 32-bit half at a time. Only
+// lanes of one wave share a block's area, so wave barriers order it; the area
+// is free again once the caller's next workgroup barrier has passed.
+__device__ __forceinline__ void int8_exchange(uint32_t* sc, int xs, bool active, bool live, const double (&v)[16],
+                                              double (&e)[8], double (&o)[8]) {
+  uint32_t el[8], ol[8];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 t;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint64_t b = __builtin_bit_cast(uint64_t, v[4 * i + c]);
+          t[c] = (uint32_t)(half ? (b >> 32) : b);
+        }
+        reinterpret_cast<u32x4*>(sc + 16 * xs)[i] = t;
+      }
     }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x2 t = active ? *reinterpret_cast<const u32x2*>(sc + 16 * j + 2 * xs) : u32x2{0u, 0u};
+      if (half == 0) {
+        el[j] = t[0];
+        ol[j] = t[1];
+      } else {
+        e[j] = live ? __builtin_bit_cast(double, ((uint64_t)t[0] << 32) | el[j]) : 0.0;
+        o[j] = live ? __builtin_bit_cast(double, ((uint64_t)t[1] << 32) | ol[j]) : 0.0;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();   // every lane has read this half before the next one is written
   }
+}
+
+// Block exponent and int8 values of the lane's 16 transformed elements (the
+// maximum is taken over the block's 8 lanes).
+__device__ __forceinline__ void int8_quantize(const double (&e)[8], const double (&o)[8], int32_t (&qe)[8],
+                                              int32_t (&qo)[8], int& ex) {
   double amax = 0.0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) amax = __builtin_fmax(amax, __builtin_fabs(v[j]));
+  for (int j = 0; j < 8; ++j) amax = __builtin_fmax(amax, __builtin_fmax(__builtin_fabs(e[j]), __builtin_fabs(o[j])));
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, h, 64));
-  e = 0;
+  ex = 0;
   if (amax > 0.0) {
     int E;
     const double f = __builtin_frexp(amax, &E);   // amax = f 2^E, f in [1/2, 1)
-    e = f * 128.0 <= 127.0 ? E - 7 : E - 6;
+    ex = f * 128.0 <= 127.0 ? E - 7 : E - 6;
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) q[j] = (int32_t)__builtin_rint(__builtin_ldexp(v[j], -e));
+  for (int j = 0; j < 8; ++j) {
+    qe[j] = (int32_t)__builtin_rint(__builtin_ldexp(e[j], -ex));
+    qo[j] = (int32_t)__builtin_rint(__builtin_ldexp(o[j], -ex));
+  }
 }
 
-// The int8 words of x16_int8's result: q repeated in all four bytes of each
-// word (for v_dot4_i32_i8 against the four masked code bytes of one weight),
-// the bias -126 sum(q) of the lane's 16 elements, and the block's fp32 factor
-// 2^e / (32 sqrt(128)) that turns the integer dot product into y~.
-__device__ __forceinline__ uint32_t int8_word(int32_t q) { return ((uint32_t)q & 0xFFu) * kByteOnes; }
-
-__device__ __forceinline__ int32_t int8_bias(const int32_t (&q)[16]) {
-  int32_t t = 0;
+// -126 times the sum of q over tile column group s (elements 16s..16s+15) of
+// the block, for lane s of the block's 8 lanes: each lane holds two elements
+// of every group; a transposing reduction over the lane bits 2, 1, 0 leaves
+// lane s with group s (7 shuffles).
+__device__ __forceinline__ int32_t int8_group_bias(const int32_t (&qe)[8], const int32_t (&qo)[8], int lane) {
+  int32_t a[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) t += q[j];
-  return -kMul1Offset * t;
+  for (int j = 0; j < 8; ++j) a[j] = qe[j] + qo[j];
+#pragma unroll
+  for (int h = 4, n = 4; h >= 1; h >>= 1, n >>= 1) {
+    const bool upper = (lane & h) != 0;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const int32_t send = upper ? a[i] : a[i + n];
+      const int32_t keep = upper ? a[i + n] : a[i];
+      a[i] = keep + __shfl_xor(send, h, 64);
+    }
+  }
+  return -kMul1Offset * a[0];
 }
+
+// An int8 value repeated in all four bytes of a word (for v_dot4_i32_i8
+// against the four masked code bytes of one weight), and the block's fp32
+// factor 2^e / (32 sqrt(128)) that turns the integer dot product into y~.
+__device__ __forceinline__ uint32_t int8_word(int32_t q) { return ((uint32_t)q & 0xFFu) * kByteOnes; }
 
 __device__ __forceinline__ float int8_factor(int e) { return __builtin_ldexpf(kRsqrt128 * kMul1Step, e); }
 
