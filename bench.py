@@ -15,8 +15,8 @@ through the C ABI. Workloads (seeded, synthetic; no trained weights):
   4  gate projection 8192 -> 28672, K=4, 16 activation rows (MFMA path)
   5  MoE: 128 experts (gate/up 2048->768, down 768->2048, K in {1,2,3}), top-8 per
      token, a step = one token = 2 grouped launches
-  6  prefill: gate projection 8192 -> 28672, K=4, 512 activation rows (decode once
-     to fp16 + dense GEMM; its roofline is the matrix cores')
+  6  prefill: gate projection 8192 -> 28672, K=4, 512 activation rows (each weight
+     decoded once into the MFMA operands; its roofline is the matrix cores')
   7  the workload-5 experts as a whole MoE block per token: gate/up -> silu * mul ->
      down -> router-weighted combine (3 launches)
 
@@ -718,7 +718,7 @@ def main(argv=None):
         roof["mfma"] = {"achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 5)}
     if info.get("prefill"):
-        # decode once + dense GEMM: the contraction is the roofline here
+        # the contraction on the matrix cores is the roofline here
         mf = roof.pop("mfma")
         hbm = {k: roof.pop(k) for k in ("achieved", "peak", "unit", "frac", "algorithmic_bytes")}
         roof.update({"bound": "mfma", "achieved": mf["achieved"], "peak": mf["peak"], "unit": "TFLOP/s",

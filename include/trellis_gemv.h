@@ -64,10 +64,7 @@
  *   - Pointers named d_* or documented "device" are device pointers (hipMalloc
  *     or any allocator of device memory); the tg_layer struct itself is read on
  *     the host. The caller owns every buffer; the library never allocates,
- *     frees, or keeps a pointer after the call returns. One exception: the
- *     prefill path creates one rocBLAS handle per device on its first call
- *     there (kept until the process ends; rocBLAS manages that handle's own
- *     device memory).
+ *     frees, or keeps a pointer after the call returns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously; the library never synchronises (except
  *     tg_workspace_status, which has to wait for the word it reads).
@@ -271,21 +268,19 @@ int32_t trellis_gemm_small(const tg_layer *layer, int32_t M,
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Prefill / large batch: Y[r] = W X[r] for r < M, 1 <= M <= 65535. Every weight
- * is decoded exactly once per call, as fp16 rows into the workspace, so the
- * decode is amortised over all M rows (lecture, Part eleven: the prefill side
- * of the bill); then one dense GEMM on the matrix cores (rocBLAS, fp16 inputs,
- * fp32 accumulation and output) and the output transform in place on Y. This
- * path always multiplies the fp16-rounded weights (TG_FLAG_ROUND_WEIGHTS has no
- * further effect here).
- *   X, ldx, Y, ldy : as for trellis_gemm_small (ldy < 2^31); m*n <= 2^38.
+ * Prefill / large batch: Y[r] = W X[r] for r < M, 1 <= M <= 65535, on the
+ * matrix cores. Every weight is decoded once per 512 rows (lecture, Part
+ * eleven: the prefill side of the bill, decoding amortised over the batch;
+ * Part fourteen), straight into the MFMA operands in registers and LDS -- the
+ * decoded weights never reach memory -- and multiplied with fp16 x~ rows, fp32
+ * accumulation; the output transform runs in the same kernel. This path always
+ * multiplies the fp16-rounded weights (TG_FLAG_ROUND_WEIGHTS has no further
+ * effect here); TG_FLAG_INT8_ACT is refused (TG_ERR_ARG).
+ *   X, ldx, Y, ldy : as for trellis_gemm_small.
  *   ws : device workspace of ws_bytes >= tg_prefill_workspace_size(layer, M):
- *        m*n*2 bytes of decoded weights plus M*n*2 bytes of transformed inputs
- *        (no zero-fill needed).
- * The GEMM uses one rocBLAS handle per device, created on the first call on
- * that device (rocBLAS allocates its own memory then) with atomics disabled,
- * so results stay bitwise deterministic; enqueueing is serialised across host
- * threads.
+ *        M*n*2 bytes of transformed inputs (no zero-fill needed).
+ * Each output is summed by one wave in a fixed order: results are bitwise
+ * deterministic.
  */
 int32_t trellis_gemm_prefill(const tg_layer *layer, int32_t M,
                              const uint16_t *X, int64_t ldx, float *Y, int64_t ldy,

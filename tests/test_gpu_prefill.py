@@ -1,4 +1,5 @@
-"""GPU parity for the prefill path (decode once to fp16, dense GEMM) against the oracle."""
+"""GPU parity for the prefill path (each weight decoded once per 512 rows straight into the matrix-core
+operands, rounded to fp16) against the oracle."""
 import numpy as np
 import pytest
 
@@ -19,7 +20,7 @@ def _prefill(arr, X_bits, dev):
 
 
 @pytest.mark.parametrize("k", range(1, 9))
-@pytest.mark.parametrize("code_id", [0, 1])
+@pytest.mark.parametrize("code_id", [0, 1, 2])
 def test_prefill_every_k(k, code_id):
     dev = device()
     arr = inputs.make_layer(256, 384, k, 5000 + k, code_id=code_id)
@@ -31,8 +32,9 @@ def test_prefill_every_k(k, code_id):
         assert rel_err(Y[r], ref[r]) <= REL_TOL, r
 
 
-@pytest.mark.parametrize("M", [1, 2, 17, 64, 129])
+@pytest.mark.parametrize("M", [1, 2, 17, 64, 129, 512, 513, 1100])
 def test_prefill_batch_sizes(M):
+    """Up to and past one workgroup's 512 rows (a second and third row chunk, the last one partial)."""
     dev = device()
     arr = inputs.make_layer(384, 1152, 3, 5100 + M)
     X = inputs.make_x(1152, 5100 + M, rows=M) if M > 1 else inputs.make_x(1152, 5100 + M)[None, :]
@@ -44,8 +46,8 @@ def test_prefill_batch_sizes(M):
 
 
 def test_prefill_decoded_weights_match_the_decode_hook():
-    """The prefill's decode kernel and trellis_decode agree bit for bit: a unit input row picks out
-    one column of W_eff, checked against the oracle's effective matrix on a small layer."""
+    """A unit input row picks out one column of W_eff: the prefill's in-register decode checked
+    column by column against the oracle's effective matrix on a small layer."""
     dev = device()
     arr = inputs.make_layer(128, 256, 2, 5200)
     X = np.zeros((3, 256), np.float16)
@@ -85,8 +87,8 @@ def test_prefill_matches_mfma_path_with_rounded_weights():
 
 @pytest.mark.parametrize("m,n,M", [(384, 1152, 129), (28672, 8192, 512)])
 def test_prefill_deterministic_and_strided(m, n, M):
-    """Two calls give bit-identical outputs (the library GEMM runs with atomics off), and an output
-    row stride wider than m leaves the gap columns untouched."""
+    """Two calls give bit-identical outputs (no atomics: each output is summed by one wave in a
+    fixed order), and an output row stride wider than m leaves the gap columns untouched."""
     import torch
     dev = device()
     arr = inputs.make_layer(m, n, 2, 5300 + M)

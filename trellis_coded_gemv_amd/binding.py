@@ -349,7 +349,7 @@ def prefill_workspace(layer: DeviceLayer, M: int, device="cuda"):
 
 
 def trellis_gemm_prefill(layer: DeviceLayer, X, Y=None, ws=None, stream=None):
-    """Y [M, m] fp32 = W X[r] for every row of fp16 X [M, n] (row stride X.stride(0)); decode once + dense GEMM."""
+    """Y [M, m] fp32 = W X[r] for every row of fp16 X [M, n] (row stride X.stride(0)); each weight decoded once per 512 rows into MFMA operands."""
     torch = _torch()
     M = int(X.shape[0])
     if Y is None:
@@ -397,7 +397,7 @@ class TrellisLinear:
       R == 1                 -> trellis_gemv
       R <= 64                -> trellis_gemm_small
       R <  prefill_min_rows  -> trellis_gemm_small on row chunks of 64
-      otherwise              -> trellis_gemm_prefill (decode once, dense GEMM)
+      otherwise              -> trellis_gemm_prefill (decode once per 512 rows into MFMA operands)
     The default threshold (192 rows) sits past the measured crossover of the last two on
     the 8192 -> 28672 gate shape. Workspaces are allocated on first use of each path and kept
     (the prefill one grows with the largest row count seen); calls are ordered on one stream.

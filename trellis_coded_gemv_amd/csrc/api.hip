@@ -8,8 +8,6 @@
 #include <map>
 #include <mutex>
 
-#include <rocblas/rocblas.h>
-
 #include "trellis_gemv.h"
 #include "tg_internal.hpp"
 
@@ -602,39 +600,14 @@ TG_API int32_t trellis_encode(int32_t n_tiles, int32_t k_bits, int32_t code_id, 
 
 namespace {
 
-// One rocBLAS handle per device, created on first use; atomics off so the GEMM
-// is bitwise deterministic. Setting the stream and enqueueing run under a lock.
-std::mutex g_blas_mu;
-std::map<int, rocblas_handle> g_blas;
-
-rocblas_handle blas_handle_locked(int dev) {
-  auto it = g_blas.find(dev);
-  if (it != g_blas.end()) return it->second;
-  rocblas_handle h = nullptr;
-  if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
-  rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed);
-  g_blas[dev] = h;
-  return h;
-}
-
-struct PrefillWs {
-  size_t w, xt, total;
-};
-
-PrefillWs prefill_ws(int m, int n, int M) {
-  PrefillWs p;
-  p.w = 0;
-  p.xt = round_up((size_t)m * n * 2, kAlign);
-  p.total = p.xt + round_up((size_t)M * n * 2, kAlign);
-  return p;
-}
+// The prefill workspace holds the transformed input rows in 32-column slabs.
+size_t prefill_ws_bytes(int n, int M) { return round_up((size_t)M * n * 2, kAlign); }
 
 }  // namespace
 
 TG_API size_t tg_prefill_workspace_size(const tg_layer* L, int32_t M) {
-  if (check_layer(L) != TG_OK || M < 1 || M > 65535) return 0;
-  if ((int64_t)L->m * L->n > kMaxDenseWeights) return 0;
-  return prefill_ws(L->m, L->n, M).total;
+  if (check_layer(L) != TG_OK || (L->flags & TG_FLAG_INT8_ACT) != 0 || M < 1 || M > 65535) return 0;
+  return prefill_ws_bytes(L->n, M);
 }
 
 TG_API int32_t trellis_gemm_prefill(const tg_layer* L, int32_t M, const uint16_t* X, int64_t ldx, float* Y,
@@ -642,34 +615,17 @@ TG_API int32_t trellis_gemm_prefill(const tg_layer* L, int32_t M, const uint16_t
   int32_t st = check_layer(L);
   if (st != TG_OK) return st;
   if ((L->flags & TG_FLAG_INT8_ACT) != 0) return TG_ERR_ARG;   // batch-1 and fused paths only
-  if (M < 1 || M > 65535 || (int64_t)L->m * L->n > kMaxDenseWeights) return TG_ERR_SHAPE;
+  if (M < 1 || M > 65535) return TG_ERR_SHAPE;
   if (!X || !Y) return TG_ERR_NULL;
-  if (ldx < L->n || ldy < L->m || ldy > 0x7fffffff) return TG_ERR_ARG;
+  if (ldx < L->n || ldy < L->m) return TG_ERR_ARG;
   if (misaligned(X, 2) || misaligned(Y, 4)) return TG_ERR_ALIGN;
-  const PrefillWs w = prefill_ws(L->m, L->n, M);
-  if (!ws || ws_bytes < w.total) return TG_ERR_WORKSPACE;
+  if (!ws || ws_bytes < prefill_ws_bytes(L->n, M)) return TG_ERR_WORKSPACE;
   if (misaligned(ws, kAlign)) return TG_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  uint16_t* Wd = reinterpret_cast<uint16_t*>((char*)ws + w.w);
-  uint16_t* Xt = reinterpret_cast<uint16_t*>((char*)ws + w.xt);
+  uint16_t* Xt = reinterpret_cast<uint16_t*>(ws);
   if (launch_prefill_rht(X, ldx, L->sign_in, Xt, L->n, M, s) != hipSuccess) return TG_ERR_LAUNCH;
-  if (launch_prefill_decode(L->codes, Wd, L->m, L->n, L->k_bits, L->code_id, s) != hipSuccess) return TG_ERR_LAUNCH;
-  {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_LAUNCH;
-    std::lock_guard<std::mutex> lock(g_blas_mu);
-    rocblas_handle h = blas_handle_locked(dev);
-    if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return TG_ERR_LAUNCH;
-    const float one = 1.f, zero = 0.f;
-    // column-major view: Y~^T [m x M] = W^ [m x n] * X~^T [n x M]; W^ rows are columns of length n
-    const rocblas_status bs = rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, L->m, M, L->n,
-                                              &one, Wd, rocblas_datatype_f16_r, L->n, Xt, rocblas_datatype_f16_r,
-                                              L->n, &zero, Y, rocblas_datatype_f32_r, (rocblas_int)ldy, Y,
-                                              rocblas_datatype_f32_r, (rocblas_int)ldy, rocblas_datatype_f32_r,
-                                              rocblas_gemm_algo_standard, 0, 0);
-    if (bs != rocblas_status_success) return TG_ERR_LAUNCH;
-  }
-  return launch_status(launch_prefill_out(Y, ldy, L->scales, L->sign_out, L->m, M, s));
+  return launch_status(launch_prefill_mfma(L->codes, L->scales, L->sign_out, Xt, Y, ldy, L->m, L->n, M, L->k_bits,
+                                           L->code_id, s));
 }
 
 namespace {

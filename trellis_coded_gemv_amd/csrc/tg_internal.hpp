@@ -117,10 +117,9 @@ hipError_t launch_encode(const float* targets, float alpha, int n_tiles, int k_b
 size_t encode_ws_words_per_slot(int k_bits, int code_id);
 hipError_t launch_prefill_rht(const uint16_t* X, int64_t ldx, const uint32_t* sign_in, uint16_t* Xt, int n, int M,
                               hipStream_t s);
-hipError_t launch_prefill_decode(const uint32_t* codes, uint16_t* W, int m, int n, int k_bits, int code_id,
-                                 hipStream_t s);
-hipError_t launch_prefill_out(float* Y, int64_t ldy, const uint16_t* scales, const uint32_t* sign_out, int m, int M,
-                              hipStream_t s);
+hipError_t launch_prefill_mfma(const uint32_t* codes, const uint16_t* scales, const uint32_t* sign_out,
+                               const uint16_t* Xt, float* Y, int64_t ldy, int m, int n, int M, int k_bits, int code_id,
+                               hipStream_t s);
 constexpr int kEncMaxSlots = 256;        // encoder workgroups in flight (one tile each at a time)
 
 // LDS bytes a GEMV workgroup needs for a chunk of `chunk_blocks` 128-blocks.

@@ -118,7 +118,7 @@ CFG3 = Workload("decoder70b_layer_k2", 303, {
 CFG4 = Workload("gate_8192x28672_k4_m16", 404, {"gate": (28672, 8192, 4)}, 16,
                 "gate projection 8192->28672, K=4, 16 activation rows (MFMA path)")
 PREFILL = Workload("prefill_gate_8192x28672_k4_m512", 606, {"gate": (28672, 8192, 4)}, 512,
-                   "gate projection 8192->28672, K=4, 512 activation rows (decode once + dense GEMM)")
+                   "gate projection 8192->28672, K=4, 512 activation rows (decode into the matrix-core operands)")
 
 
 @dataclass
