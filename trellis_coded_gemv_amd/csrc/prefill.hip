@@ -90,15 +90,13 @@ __device__ __forceinline__ u32x4 pf_decode(const uint32_t (&w)[PfGeom<K, CODE>::
   } else {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      uint16_t lo, hi;
       if constexpr (CODE == 2) {
-        lo = mul1_weight_bits(st[2 * d]);
-        hi = mul1_weight_bits(st[2 * d + 1]);
+        out[d] = mul1_weight_pair(st[2 * d], st[2 * d + 1]);
       } else {
-        lo = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(st[2 * d], cr)));
-        hi = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(st[2 * d + 1], cr)));
+        const uint16_t lo = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(st[2 * d], cr)));
+        const uint16_t hi = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(st[2 * d + 1], cr)));
+        out[d] = (uint32_t)lo | ((uint32_t)hi << 16);
       }
-      out[d] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
   }
   return out;

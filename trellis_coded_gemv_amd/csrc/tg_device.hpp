@@ -192,8 +192,26 @@ __device__ __forceinline__ int32_t mul1_level(uint32_t bytes) {
   return (int32_t)__builtin_amdgcn_udot4(bytes, kByteOnes, (uint32_t)-kMul1Offset, false);
 }
 
+// The weight as binary16 without a conversion: fp16 48.0 is 0x5200, and the
+// binade [32, 64) steps by exactly 1/32, so 0x5200 + level (|level| <= 126 keeps
+// the exponent) is the pattern of 48 + level/32. One v_dot4_u32_u8 with
+// accumulator 0x5200 - 126 forms it; subtracting 48 in binary16 is exact.
+constexpr uint32_t kMul1Magic = 0x5200u;   // binary16 48.0
+
+__device__ __forceinline__ uint32_t mul1_biased_half(uint32_t state) {
+  return __builtin_amdgcn_udot4(mul1_bytes(state), kByteOnes, kMul1Magic - (uint32_t)kMul1Offset, false);
+}
+
 __device__ __forceinline__ uint16_t mul1_weight_bits(uint32_t state) {
-  return __builtin_bit_cast(uint16_t, (_Float16)((float)mul1_level(mul1_bytes(state)) * kMul1Step));
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)mul1_biased_half(state));
+  return __builtin_bit_cast(uint16_t, (_Float16)(h - (_Float16)48.0f));
+}
+
+// Two weights as one packed word (a in the low half): one packed binary16 subtract.
+__device__ __forceinline__ uint32_t mul1_weight_pair(uint32_t sa, uint32_t sb) {
+  const uint32_t biased = mul1_biased_half(sa) | (mul1_biased_half(sb) << 16);
+  const half2_t w = __builtin_bit_cast(half2_t, biased) - half2_t{(_Float16)48.0f, (_Float16)48.0f};
+  return __builtin_bit_cast(uint32_t, w);
 }
 
 // ---------------------------------------------------------------------------
