@@ -70,3 +70,62 @@ def test_graph_gemm_small_and_moe_block():
     g = _capture(torch, lambda s: tg.trellis_moe_block(gu, dn, sel, w, x, y, mws, s))
     _replays(torch, g, y, ref, lambda: tg.trellis_moe_block(gu, dn, sel, w, x, ws=mws))
     assert np.isfinite(y.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("code_id,flags", [(0, 0), (2, tg.TG_FLAG_INT8_ACT)])
+def test_graph_fused_launch(code_id, flags):
+    """The fused launch of layers that share an input: its ticket counters and call-tagged slots live
+    in the workspace across replays; the int8 form's quantiser runs inside the launch too."""
+    dev = device()
+    import torch
+    n = 2048
+    Ls = [tg.DeviceLayer(inputs.make_layer(m, n, 2, 5200 + m, code_id=code_id), dev, flags=flags)
+          for m in (1024, 256, 256)]
+    x = tg.fp16_tensor(inputs.make_x(n, 5200), dev)
+    ws = tg.fused_workspace(Ls, dev)
+    say("graph fused", code_id, flags)
+    ref = torch.cat([y.clone() for y in tg.trellis_gemv_fused(Ls, x, ws=ws)])
+    ys = [torch.empty(L.m, dtype=torch.float32, device=dev) for L in Ls]
+    g = _capture(torch, lambda s: tg.trellis_gemv_fused(Ls, x, ys, ws, s))
+    for r in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(ys), ref), r
+        tg.trellis_gemv_fused(Ls, x, ws=ws)     # eager work between replays, on the same workspace
+        torch.cuda.synchronize()
+
+
+def test_graph_noalloc_after_setup():
+    """trellis_gemv_noalloc under capture once its device array is set up (the first call)."""
+    dev = device()
+    import ctypes
+    import torch
+    L = tg.DeviceLayer(inputs.make_layer(512, 4096, 2, 5300), dev)
+    x = tg.fp16_tensor(inputs.make_x(4096, 5300), dev)
+    d = L.desc()
+
+    def call(y, s):
+        assert tg.lib().trellis_gemv_noalloc(ctypes.byref(d), x.data_ptr(), y.data_ptr(), s.cuda_stream) == 0
+
+    say("graph noalloc")
+    ref = torch.empty(512, dtype=torch.float32, device=dev)
+    call(ref, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    y = torch.empty_like(ref)
+    g = _capture(torch, lambda s: call(y, s))
+    _replays(torch, g, y, ref, lambda: call(torch.empty_like(ref), torch.cuda.current_stream()))
+
+
+def test_graph_prefill():
+    dev = device()
+    import torch
+    L = tg.DeviceLayer(inputs.make_layer(512, 2048, 3, 5400), dev)
+    X = tg.fp16_tensor(inputs.make_x(2048, 5400, rows=600), dev)
+    ws = tg.prefill_workspace(L, 600, dev)
+    say("graph prefill")
+    ref = tg.trellis_gemm_prefill(L, X, ws=ws).clone()
+    Y = torch.empty_like(ref)
+    g = _capture(torch, lambda s: tg.trellis_gemm_prefill(L, X, Y, ws, s))
+    _replays(torch, g, Y, ref, lambda: tg.trellis_gemm_prefill(L, X, ws=ws))
