@@ -7,12 +7,26 @@ with count <= the workspace's max_contrib, and that exactly one contributor fini
 import numpy as np
 
 
-def geometry(ms, n, target=256):
+def lds_bytes(n, int8=False):
+    """The fused kernel's dynamic LDS: two layers' x~ areas, the output buffer, flags (+ int8 side arrays)."""
+    nbp = ((n // 128) + 1) & ~1
+    return 2 * nbp * 128 * 4 + 128 * 4 + 16 + (2 * nbp * 9 * 4 if int8 else 0)
+
+
+def default_target(total, n, int8=False):
+    """The host's default workgroup count: two per compute unit where each still gets at least 16
+    units and two workgroups fit 160 KB of LDS, else one."""
+    return 512 if total >= 512 * 16 and 2 * lds_bytes(n, int8) <= 160 * 1024 else 256
+
+
+def geometry(ms, n, target=None):
     nb = n // 128
     spr = (nb + 1) // 2
     units = [(m // 128) * spr for m in ms]
     unit0 = np.concatenate([[0], np.cumsum(units)[:-1]]).astype(int)
     total = sum(units)
+    if target is None:
+        target = default_target(total, n)
     upw = max(1, min(-(-total // target), min(units)))
     grid = -(-total // upw)
     maxc = 1
@@ -23,7 +37,7 @@ def geometry(ms, n, target=256):
     return spr, unit0, total, upw, grid, maxc
 
 
-def replay(ms, n, target=256):
+def replay(ms, n, target=None):
     spr, unit0, total, upw, grid, maxc = geometry(ms, n, target)
     covered = np.zeros(total, int)
     contributors = {}
@@ -52,7 +66,9 @@ def replay(ms, n, target=256):
 
 def test_decoder_layer_groups():
     assert replay([8192, 1024, 1024], 8192) == (10, 256, 4)      # q/k/v: 2560 units, 10 per workgroup
-    assert replay([28672, 28672], 8192) == (56, 256, 2)          # gate/up: 14336 units, 56 per workgroup
+    assert replay([28672, 28672], 8192) == (28, 512, 2)          # gate/up: 14336 units, 28 per workgroup
+    assert default_target(14336, 16384) == 256                   # 16384 inputs: one workgroup's x~ fills the LDS
+    assert default_target(14336, 8192, int8=True) == 512
 
 
 def test_random_tables_and_forced_counts():

@@ -388,9 +388,15 @@ int32_t fused_geometry(const tg_layer* layers, int32_t n_layers, FusedGeom* g) {
     if (u < min_units) min_units = u;
   }
   if (units > INT32_MAX / 2) return TG_ERR_SHAPE;
-  // One workgroup per compute unit by default (the layer's splits field forces another count);
-  // a run is never longer than the smallest layer, so it crosses at most one layer boundary.
-  const int target = layers[0].splits > 0 ? layers[0].splits : 256;
+  // One workgroup per compute unit by default, two where each still gets at least 16 units
+  // and two fit a compute unit's 160 KB of LDS: more waves per SIMD hide more of the decode's
+  // dependent latency (2 x 28672 x 8192 gate/up: 70.8 against 75.0 us; the 10-unit runs of a
+  // decoder layer's q/k/v lose instead: 22.9 against 21.9). The layer's splits field forces
+  // another count. A run is never longer than the smallest layer, so it crosses at most one
+  // layer boundary.
+  const bool int8 = (layers[0].flags & TG_FLAG_INT8_ACT) != 0;
+  int target = units >= (int64_t)512 * 16 && 2 * fused_lds_bytes(layers[0].n, int8) <= (size_t)160 * 1024 ? 512 : 256;
+  if (layers[0].splits > 0) target = layers[0].splits;
   int upw = (int)((units + target - 1) / target);
   if (upw > min_units) upw = (int)min_units;
   if (upw < 1) upw = 1;
