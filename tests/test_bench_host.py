@@ -52,3 +52,25 @@ def test_recorded_traffic_only_for_the_sources_it_was_taken_on(monkeypatch):
     assert bench.recorded_traffic(2, "no such launch") is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.recorded_traffic(int(key.split("/")[0]), kern) is None
+
+
+def test_int8_mode_needs_mul1_and_keys_its_traffic(monkeypatch):
+    """--int8 is the mul1 code's int8-activation form: refused with another code; its traffic record
+    and its CPU baseline are the int8 form's own."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--int8", "--code", "0"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "--code 2" in r.stderr
+    import json
+    import numpy as np
+    from oracle import gemv as ogemv
+    from trellis_coded_gemv_amd import inputs
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["csrc_sha"])
+    monkeypatch.setitem(bench.LAYER_FLAGS, "int8", True)
+    if "3/code2/int8" in rec["workloads"]:
+        assert bench.recorded_traffic(3, "gate_up", 2) == rec["workloads"]["3/code2/int8"]["gate_up"]["hbm_bytes_per_launch"]
+    cpu, refs = bench.cpu_baseline(1, code_id=2, blocks_per_tensor=2, max_workers=2)
+    assert "int8" in cpu["sample"]
+    arr, x = bench.linear_inputs(inputs, inputs.WORKLOADS[1], 1, 2)["linear"]
+    for (kind, name, b), y in refs.items():
+        assert np.array_equal(y, ogemv.gemv_int8_rows(arr, x, np.arange(128 * b, 128 * b + 128)))

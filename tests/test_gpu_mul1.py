@@ -261,3 +261,20 @@ def test_mul1_decode_ceiling_runs(flags):
     out = tg.decode_ceiling(2, MUL1, 8, 16, flags=flags)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("k", [4, 6, 8])
+def test_mul1_encode_high_rates_consistent(k):
+    """Wider steps (the oracle's search is too slow here): each stored stream decodes, through the
+    oracle's walk and code, to the error the encoder reports, and the error falls with the rate."""
+    dev = device()
+    import torch
+    tgt = np.random.default_rng(8150 + k).standard_normal((3, 256)).astype(np.float32)
+    say("mul1 encode", k)
+    codes, err = tg.trellis_encode(torch.from_numpy(tgt).to(dev), k, MUL1, 0.9)
+    torch.cuda.synchronize()
+    codes, err = codes.cpu().numpy().view(np.uint32), err.cpu().numpy()
+    for i in range(3):
+        recomputed = ov.tile_errors(codes[i], tgt[i], k, MUL1, 0.9)
+        assert abs(recomputed - float(err[i])) <= 1e-4 * max(recomputed, 1e-3), i
+    assert float(err.mean()) / 256 < {4: 0.012, 6: 0.004, 8: 0.003}[k]
