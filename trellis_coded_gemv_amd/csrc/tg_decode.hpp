@@ -49,6 +49,41 @@ __device__ __forceinline__ uint32_t lane_window(const uint32_t (&w)[2 * K], uint
   return ubfe(alignbit(wj, wj1, 16), 32 - q, 16);
 }
 
+// Multiply-only codes (mul1): with K dividing 16, the window 16 stream bits
+// after window tl is window tl + 16/K, so one 32-bit span holds two windows
+// (tl in its high half, tl + 16/K in its low half) and one v_alignbit serves
+// both. The multiplier sits in an SGPR, so each half feeds v_mul_u32_u24 through
+// an SDWA word select and needs no extract of its own.
+struct MulReg {
+  uint32_t m;
+  __device__ __forceinline__ MulReg() : m(kMul) {
+    asm volatile("" : "+s"(m));
+    m &= 0xFFFFFFu;   // known 24-bit: v_mul_u32_u24
+  }
+};
+
+// The 32 stream bits starting at window tl's first bit.
+template <int K>
+__device__ __forceinline__ uint32_t lane_span(const uint32_t (&w)[2 * K], uint32_t nb, int tl) {
+  constexpr int NW = 2 * K;
+  const int p = K * tl;
+  const int j = p >> 5, q = p & 31;
+  const uint32_t wj = j < NW ? w[j] : nb;
+  if (q == 0) return wj;
+  const uint32_t wj1 = j + 1 < NW ? w[j + 1] : nb;
+  return alignbit(wj, wj1, 32 - q);
+}
+
+// The lane's 32 leading windows, in an order that gives consecutive leads
+// different rows: lead n (0..31) -> window index. Its partner is lead + 16/K.
+template <int K>
+__device__ __forceinline__ constexpr int span_lead(int n) {
+  constexpr int D = 16 / K;
+  const int g = n >> 2, i = n & 3;
+  if constexpr (K == 1) return 16 * (2 * (i & 1)) + 2 * g + (i >> 1);   // rows 0, 2 lead rows 1, 3
+  else return 16 * i + (g / D) * 2 * D + g % D;                        // row i, columns paired D apart
+}
+
 // Decode the lane's 64 weights (4 rows x 16 columns of one tile) and
 // accumulate their dot products with x~ of that tile column.
 //   w   : the lane's 2K stream words (stream bits 0 .. 64K-1 of the lane, MSB first)
@@ -140,10 +175,34 @@ __device__ __forceinline__ void decode_dot_pair_64(const uint32_t (&w)[2 * K], u
 // mul1 (code_id 2) against x~ / 32 in fp32 (xf: 16 fp32 bit patterns, one
 // per tile column). Per weight: one window extract, v_mul_u32_u24, v_and_b32,
 // v_dot4_u32_u8 (the level as an exact integer), v_cvt_f32_i32 and one
-// v_fmac_f32. The weights are exact, so there is no rounded form.
+// v_fmac_f32; with K dividing 16 two windows share one v_alignbit and need no
+// extract (SDWA word selects). The weights are exact, so there is no rounded
+// form.
 template <int K>
 __device__ __forceinline__ void decode_dot_mul1_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xf)[16],
                                                    float (&acc)[4]) {
+  if constexpr (16 % K == 0) {
+    constexpr int D = 16 / K;
+    const MulReg mr;
+#pragma unroll
+    for (int n0 = 0; n0 < 32; n0 += 4) {
+      uint32_t b[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t t = lane_span<K>(w, nb, span_lead<K>(n0 + i));
+        b[i][0] = ((t >> 16) * mr.m) & kByteMask;
+        b[i][1] = ((t & 0xFFFFu) * mr.m) & kByteMask;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tl = span_lead<K>(n0 + i) + h * D;
+          acc[tl >> 4] = __builtin_fmaf((float)mul1_level(b[i][h]), __builtin_bit_cast(float, xf[tl & 15]), acc[tl >> 4]);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
     uint32_t b[4];
@@ -159,11 +218,36 @@ __device__ __forceinline__ void decode_dot_mul1_64(const uint32_t (&w)[2 * K], u
 // four masked code bytes against the activation's int8 in all four bytes
 // (xq), which adds level_byte_sum * q; the integer accumulators start from the
 // bias -126 sum(q) of the 16 columns, so they end at sum(level * q) exactly.
-// One fp32 multiply-add per row then applies the block factor.
+// One fp32 multiply-add per row then applies the block factor. With K dividing
+// 16 the windows go by pairs as in decode_dot_mul1_64.
 template <int K>
 __device__ __forceinline__ void decode_dot_mul1_i8_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xq)[16],
                                                       int32_t bias, float factor, float (&acc)[4]) {
   int32_t ai[4] = {bias, bias, bias, bias};
+  if constexpr (16 % K == 0) {
+    constexpr int D = 16 / K;
+    const MulReg mr;
+#pragma unroll
+    for (int n0 = 0; n0 < 32; n0 += 4) {
+      uint32_t b[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t t = lane_span<K>(w, nb, span_lead<K>(n0 + i));
+        b[i][0] = ((t >> 16) * mr.m) & kByteMask;
+        b[i][1] = ((t & 0xFFFFu) * mr.m) & kByteMask;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tl = span_lead<K>(n0 + i) + h * D;
+          ai[tl >> 4] = __builtin_amdgcn_sdot4((int32_t)b[i][h], (int32_t)xq[tl & 15], ai[tl >> 4], false);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(factor, (float)ai[r], acc[r]);
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
     uint32_t b[4];
