@@ -150,4 +150,31 @@ def mul1_table() -> np.ndarray:
     return mul1_bits(np.arange(1 << 16))
 
 
-CODE_V = {0: 1, 1: 2, 2: 1}     # weights per trellis step of each code_id
+# ---------------------------------------------------------------------------
+# code_id 3, "MCG": EXL3's variant of the three-instruction code ([TQ] Part
+# eleven: the generator keeps only the multiply, the additive constant is
+# dropped; [FG] "What the EXL3 converter actually sets": one of the converter's
+# three codebook names). Steps: (1) h = multiplier * S mod 2^32; (2) and (3) as
+# for code 0: mask/XOR each half into a bounded binary16 value and add the two
+# halves with one binary16 add.
+# Reading where the pages leave it open: the multiplier is code 0's 0x9E3779
+# (the pages mention a 32-bit constant without printing it; 24 bits keep the
+# multiply one full-rate instruction, as for code 0 and mul1).
+# Pins (tests/test_oracle_code.py): hand-worked values
+# (tests/golden/mcg_hand_values.txt); NumPy's float16 cast on all states; the
+# generator's linearity (no additive constant: h(a + b) = h(a) + h(b) mod 2^32);
+# the same bounds and balance as code 0.
+# ---------------------------------------------------------------------------
+
+def mcg_weight_bits(states) -> np.ndarray:
+    """fp16 bits of RNE(value(lo) + value(hi)) with the halves of (mcg(S) AND MASK) XOR XOR."""
+    lo, hi = halves(mask_xor(mcg(states)))
+    return fp16.round_rne(fp16.value(lo) + fp16.value(hi))
+
+
+def mcg_table() -> np.ndarray:
+    """code_id 3 for all states: fp16 bits [65536]."""
+    return mcg_weight_bits(np.arange(1 << 16))
+
+
+CODE_V = {0: 1, 1: 2, 2: 1, 3: 1}     # weights per trellis step of each code_id

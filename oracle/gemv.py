@@ -30,7 +30,7 @@ from . import code, fp16, hadamard, trellis
 def decode_layer(layer, tile_rows=None) -> np.ndarray:
     """fp16 bit patterns of the decoded weights, [m, n] (or only the listed tile rows).
 
-    code_id 0 and 2: one state per weight. code_id 1: one state per pair of
+    code_id 0, 2 and 3: one state per weight. code_id 1: one state per pair of
     weights (t = 2*tau, 2*tau + 1 of the row-major tile order).
     """
     cid = int(getattr(layer, "code_id", 0))
@@ -40,6 +40,8 @@ def decode_layer(layer, tile_rows=None) -> np.ndarray:
         w = code.weight_bits(states)
     elif cid == 2:
         w = code.mul1_bits(states)
+    elif cid == 3:
+        w = code.mcg_weight_bits(states)
     else:
         even, odd = code.pair_weight_bits(states)
         w = np.stack([even, odd], axis=-1).reshape(*states.shape[:-1], trellis.SEQ)

@@ -116,9 +116,12 @@ def encode_tail_biting(wvals: np.ndarray, alpha, targets: np.ndarray, L: int, b:
 
 
 def code_values(code_id: int) -> np.ndarray:
-    """float32 weights of every 16-bit state: [65536] (codes 0 and 2) or [65536, 2] (pair code)."""
+    """float32 weights of every 16-bit state: [65536] (codes 0, 2 and 3) or [65536, 2] (pair code)."""
     if code_id == 0:
         return code.weight_values(np.arange(1 << 16)).astype(F32)
+    if code_id == 3:
+        from . import fp16
+        return fp16.value(code.mcg_table()).astype(F32)
     if code_id == 2:
         return (code.mul1_level(np.arange(1 << 16)) * code.MUL1_STEP).astype(F32)
     e, o = code.pair_weight_bits(np.arange(1 << 16))

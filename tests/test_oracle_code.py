@@ -150,3 +150,61 @@ def test_mul1_levels_follow_four_uniform_bytes():
     assert 0.5 * np.abs(hist - law).sum() < 0.03      # total variation distance
     assert abs(lev.mean()) < 0.5 and abs(lev.std() - np.sqrt(4 * (64 ** 2 - 1) / 12)) < 1.0
     assert code.mul1_level(np.array([0]))[0] == -126   # multiply-only: state 0 stays 0
+
+
+# --- code_id 3, MCG ------------------------------------------------------------------------
+
+def test_mcg_hand_values():
+    """Every intermediate of MCG against the hand-worked fixture (a tie, the fixed point, a zero sum)."""
+    for state, h, u, lo, hi, num, den, w in golden_rows("mcg_hand_values.txt"):
+        s = np.array([int(state, 16)])
+        assert int(code.mcg(s)[0]) == int(h, 16)
+        assert int(code.mask_xor(code.mcg(s))[0]) == int(u, 16)
+        l, hh = code.halves(code.mask_xor(code.mcg(s)))
+        assert int(l[0]) == int(lo, 16) and int(hh[0]) == int(hi, 16)
+        total = fp16.value(l) + fp16.value(hh)
+        assert Fraction(float(total[0])) == Fraction(int(num), int(den))
+        assert int(code.mcg_weight_bits(s)[0]) == int(w, 16)
+
+
+def test_mcg_all_states_against_python_integers_and_numpy_cast():
+    """All 65,536 states by a separate route: Python integers for the hash and the bit logic,
+    NumPy's float16 view and cast for the halves and the rounding."""
+    lo = np.empty(1 << 16, np.uint16)
+    hi = np.empty(1 << 16, np.uint16)
+    for s in range(1 << 16):
+        u = (((0x9E3779 * s) % (1 << 32)) & 0x8FFF8FFF) | 0x30003000   # disjoint mask/XOR: OR
+        lo[s], hi[s] = u & 0xFFFF, u >> 16
+    exact = lo.view(np.float16).astype(np.float64) + hi.view(np.float16).astype(np.float64)
+    assert (code.mcg_table() == exact.astype(np.float16).view(np.uint16)).all()
+
+
+def test_mcg_generator_is_linear():
+    """No additive constant: h(a + b) = h(a) + h(b) and h(2a) = 2 h(a) mod 2^32, h(0) = 0
+    (each fails for the three-instruction code's multiply-add)."""
+    rng = np.random.default_rng(5)
+    a = rng.integers(0, 1 << 15, 4096)
+    b = rng.integers(0, 1 << 15, 4096)
+    m32 = (1 << 32) - 1
+    assert ((code.mcg(a) + code.mcg(b)) & m32 == code.mcg(a + b)).all()
+    assert ((2 * code.mcg(a)) & m32 == code.mcg(2 * a)).all()
+    assert code.mcg(np.array([0]))[0] == 0
+    assert not ((code.lcg(a) + code.lcg(b)) & m32 == code.lcg(a + b)).any()
+
+
+def test_mcg_halves_bounded_balanced_and_sum_near_gaussian():
+    """Same structure as code 0: halves in +-[1/8, 2), the low half's sign exactly balanced
+    (odd multiplier: S -> h mod 2^16 is a bijection), a finite near-Gaussian sum."""
+    u = code.mask_xor(code.mcg(np.arange(1 << 16)))
+    lo, hi = code.halves(u)
+    for half in (lo, hi):
+        v = np.abs(fp16.value(half))
+        assert v.min() >= 0.125 and v.max() < 2.0
+    assert ((lo >> 15) == 1).sum() == 1 << 15
+    assert abs(((hi >> 15) == 1).mean() - 0.5) < 0.01
+    w = fp16.value(code.mcg_table())
+    assert np.isfinite(w).all() and abs(w.mean()) < 0.01 and 1.1 < w.std() < 1.4
+    kurt = ((w - w.mean()) ** 4).mean() / w.var() ** 2
+    assert 2.5 < kurt < 3.5
+    # it is a different code from code 0 on almost every state
+    assert (code.mcg_table() != code.table()).mean() > 0.99

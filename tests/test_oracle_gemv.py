@@ -221,3 +221,20 @@ def test_naive_triple_loop_small_layer():
                                  for j in range(128))
     ref = gemv.gemv(L, x)
     assert np.allclose(ref, y, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_mcg_decode_uses_the_multiply_only_code():
+    """code_id 3 (MCG): an all-zero stream decodes to the fixed point's weight 1/4 everywhere;
+    one all-ones tile holds the weight of state 0xFFFF -- both from the hand-worked fixture."""
+    m, n, k = 128, 256, 2
+    codes = np.zeros(inputs.words_per_layer(m, n, k), np.uint32)
+    R, C = 5, 11
+    T = R * (n // 16) + C
+    codes[T * 8 * k:(T + 1) * 8 * k] = 0xFFFFFFFF
+    L = _layer(m, n, k, codes=codes)
+    L.code_id = 3
+    hand = {int(r[0], 16): int(r[7], 16) for r in golden_rows("mcg_hand_values.txt")}
+    expect = np.full((m, n), hand[0], np.uint16)
+    expect[16 * R:16 * R + 16, 16 * C:16 * C + 16] = hand[0xFFFF]
+    assert np.array_equal(gemv.decode_layer(L), expect)
+    assert float(np.array([hand[0]], np.uint16).view(np.float16)[0]) == 0.25
