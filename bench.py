@@ -654,8 +654,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5, 6, 7])
-    ap.add_argument("--code", type=int, default=0, choices=[0, 1, 2],
-                    help="code_id of every layer: 0 the three-instruction code, 1 the pair code, 2 mul1")
+    ap.add_argument("--code", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="code_id of every layer: 0 the three-instruction code, 1 the pair code, 2 mul1, 3 MCG")
     ap.add_argument("--int8", action="store_true",
                     help="with --code 2: the batch-1 layers multiply by the int8 form of x~ (TG_FLAG_INT8_ACT)")
     ap.add_argument("--no-graph", action="store_true")

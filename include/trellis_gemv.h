@@ -56,6 +56,14 @@
  *     q = round-half-even(u * 2^-e_b),   x~ replaced by q * 2^e_b / sqrt(128).
  *   The integer products are exact; only the per-block fp32 scaling rounds.
  *
+ * Storage format (code_id 3, "MCG", one of the EXL3 converter's codebooks;
+ *   lecture, Part eleven: the three-instruction code's generator with the
+ *   additive constant dropped; LLM Cal field guide, "What the EXL3 converter
+ *   actually sets"): as code_id 0 with
+ *     h = 0x9E3779*S mod 2^32;  u = (h & 0x8FFF8FFF) ^ 0x30003000;
+ *     w = fp16_rne(half(u[15:0]) + half(u[31:16])).
+ *   The pages print no multiplier for it; this is code_id 0's.
+ *
  *   scales  : m fp16 bit patterns (g).
  *   sign_in : ceil(n/32) uint32 words; bit i%32 of word i/32 set means s_in[i] = -1.
  *   sign_out: ceil(m/32) uint32 words, same convention.
@@ -92,7 +100,7 @@
 extern "C" {
 #endif
 
-#define TG_ABI_VERSION 3
+#define TG_ABI_VERSION 4
 
 typedef enum tg_status {
   TG_OK = 0,
@@ -101,7 +109,7 @@ typedef enum tg_status {
   TG_ERR_KBITS = -3,      /* k_bits outside 1..8                                      */
   TG_ERR_ALIGN = -4,      /* a pointer is not aligned as documented                   */
   TG_ERR_WORKSPACE = -5,  /* workspace missing or smaller than tg_workspace_size()     */
-  TG_ERR_CODE_ID = -6,    /* code_id other than 0, 1 or 2                             */
+  TG_ERR_CODE_ID = -6,    /* code_id other than 0, 1, 2 or 3                          */
   TG_ERR_LAUNCH = -7,     /* the HIP runtime rejected a kernel launch                 */
   TG_ERR_ARG = -8         /* any other invalid argument (stride, flags, index range)   */
 } tg_status;
@@ -126,7 +134,7 @@ typedef struct tg_layer {
   int32_t m;                 /* out_features, multiple of 128                              */
   int32_t n;                 /* in_features, multiple of 128                               */
   int32_t k_bits;            /* bits per weight K, 1..8 (lecture, Part eleven)              */
-  int32_t code_id;           /* 0 = the three-instruction code; 1 = the pair code; 2 = mul1  */
+  int32_t code_id;           /* 0 = three-instruction code; 1 = pair code; 2 = mul1; 3 = MCG */
   int32_t flags;             /* TG_FLAG_*                                                  */
   int32_t splits;            /* input chunks (split-K) of the batch-1, grouped and          *
                               * small-batch paths: 0 = the library's choice; S > 0 forces  *
@@ -389,7 +397,7 @@ int32_t trellis_decode(const tg_layer *layer, uint16_t *w_out, void *stream);
  * The whole computed code as a table (test / export hook; lecture, Part nine:
  * each state's weight is a function of the 16-bit state alone, so the code has
  * exactly 2^16 entries), for every state S < 65536:
- *   code_id 0, 2: out[S] = fp16 pattern of the weight for state S  (65536 entries);
+ *   code_id 0, 2, 3: out[S] = fp16 pattern of the weight for state S  (65536 entries);
  *   code_id 1:    out[2S], out[2S+1] = the state's weight pair      (131072 entries).
  *   out : device, 2-byte aligned.
  */
@@ -404,7 +412,7 @@ int32_t tg_code_table(int32_t code_id, uint16_t *out, void *stream);
  * per weight; Part eleven: the same decode is compute-bound on data-centre
  * cards). workgroups of 512 threads (8 waves) each run `steps` steps, i.e.
  * decode workgroups * 512 * 64 * steps weights.
- *   k_bits     : 1..8;  code_id : 0, 1 or 2.
+ *   k_bits     : 1..8;  code_id : 0, 1, 2 or 3.
  *   flags      : 0, or TG_FLAG_INT8_ACT with code_id 2 (the int8-activation loop).
  *   workgroups : 1..65535;  steps : 1..2^20.
  *   out        : device, workgroups * 512 fp32 (one per thread, keeps the work live).
@@ -420,7 +428,7 @@ int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t flags, int32_
  * constrained to start and end on it). For every tile it stores the stream
  * whose decoded weights w minimise sum_t (scale * w_t - target_t)^2.
  *   n_tiles  : 1 .. 2^24 tiles.
- *   k_bits   : 1..8 for code_id 0 and 2; 1..4 for the pair code (2K bits per step).
+ *   k_bits   : 1..8 for code_id 0, 2 and 3; 1..4 for the pair code (2K bits per step).
  *   scale    : reconstruction scale, finite and > 0.
  *   targets  : device, n_tiles * 256 fp32, each tile in sequence order
  *              t = 16r + c, 4-byte aligned.

@@ -39,7 +39,7 @@ def _cases():
     sys.path.insert(0, ROOT)
     from trellis_coded_gemv_amd import inputs
     cases = {}
-    for cfg, code_ids in ((2, (0, 1)), (3, (0,))):
+    for cfg, code_ids in ((2, (0, 1)), (3, (0, 3))):
         wl = inputs.WORKLOADS[cfg]
         for ti, (name, (m, n, k)) in enumerate(wl.tensors.items()):
             for cid in code_ids:
@@ -50,7 +50,7 @@ def _cases():
         cases[f"w3_{name}_c1"] = dict(m=m, n=n, k=k, seed=inputs.CFG3.seed, tensor=ti, code_id=1,
                                       x=(inputs.CFG3.seed, ti, 1), pick=None, sample_seed=ti)
     # the fused launches of the decoder layer: q/k/v read one shared vector, gate/up another
-    for cid, names in ((0, ("q", "k", "v", "gate", "up")), (1, ("q", "k", "v"))):
+    for cid, names in ((0, ("q", "k", "v", "gate", "up")), (1, ("q", "k", "v")), (3, ("q", "k", "v", "gate", "up"))):
         for name in names:
             ti = list(inputs.CFG3.tensors).index(name)
             m, n, k = inputs.CFG3.tensors[name]

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(tg.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.tg_abi_version() == 3
+    assert L.tg_abi_version() == 4
     from trellis_coded_gemv_amd.build import source_hash
     assert L.tg_build_id().decode() == source_hash()
 
@@ -54,7 +54,7 @@ def test_status_strings():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(k_bits=0), -3), (dict(k_bits=9), -3), (dict(m=100), -2), (dict(n=0), -2), (dict(m=-128), -2),
-    (dict(code_id=3), -6), (dict(code_id=-1), -6), (dict(flags=4), -8), (dict(flags=2), -8), (dict(splits=-1), -8), (dict(splits=65536), -8), (dict(codes=0), -1),
+    (dict(code_id=4), -6), (dict(code_id=-1), -6), (dict(flags=4), -8), (dict(flags=2), -8), (dict(splits=-1), -8), (dict(splits=65536), -8), (dict(codes=0), -1),
     (dict(sign_out=0), -1), (dict(codes=A16 + 8), -4), (dict(scales=A16 + 1), -4), (dict(sign_in=A4 + 2), -4)])
 def test_gemv_layer_validation(kw, status):
     d = _layer(**kw)
@@ -112,7 +112,7 @@ def test_decode_and_table_validation():
     assert L.trellis_decode(ctypes.byref(_layer(m=24)), A16, None) == -2
     assert L.trellis_decode(ctypes.byref(_layer(k_bits=0)), A16, None) == -3
     assert L.trellis_decode(ctypes.byref(_layer()), 0, None) == -1
-    assert L.tg_code_table(3, A16, None) == -6
+    assert L.tg_code_table(4, A16, None) == -6
     assert L.tg_code_table(0, 0, None) == -1
 
 
@@ -149,7 +149,7 @@ def test_encode_argument_validation():
     assert L.tg_encode_workspace_size(0, 2, 0) == 0
     assert L.tg_encode_workspace_size(4, 9, 0) == 0
     assert L.tg_encode_workspace_size(4, 5, 1) == 0           # pair code: at most 4 bits (8 per step)
-    assert L.tg_encode_workspace_size(4, 2, 3) == 0
+    assert L.tg_encode_workspace_size(4, 2, 4) == 0
     assert L.tg_encode_workspace_size(4, 8, 2) > 0            # mul1: one state per weight, like code 0
     need = L.tg_encode_workspace_size(4, 2, 0)
     assert L.trellis_encode(4, 2, 0, 0.75, A16, A16, A16, 0, need, None) == -5
@@ -157,7 +157,7 @@ def test_encode_argument_validation():
     assert L.trellis_encode(4, 2, 0, -1.0, A16, A16, A16, A16, need, None) == -8
     assert L.trellis_encode(4, 2, 0, float("nan"), A16, A16, A16, A16, need, None) == -8
     assert L.trellis_encode(4, 0, 0, 0.75, A16, A16, A16, A16, need, None) == -3
-    assert L.trellis_encode(4, 2, 3, 0.75, A16, A16, A16, A16, need, None) == -6
+    assert L.trellis_encode(4, 2, 4, 0.75, A16, A16, A16, A16, need, None) == -6
     assert L.trellis_encode(0, 2, 0, 0.75, A16, A16, A16, A16, need, None) == -2
     assert L.trellis_encode(4, 2, 0, 0.75, A16 + 2, A16, A16, A16, need, None) == -4
     assert L.trellis_encode(4, 2, 0, 0.75, A16, A16, A16, A16 + 16, need, None) == -4
@@ -238,7 +238,7 @@ def test_status_query_and_splits_validation():
 def test_decode_ceiling_validation():
     L = tg.lib()
     assert L.tg_decode_ceiling(0, 0, 0, 1, 1, A16, None) == -3
-    assert L.tg_decode_ceiling(2, 3, 0, 1, 1, A16, None) == -6
+    assert L.tg_decode_ceiling(2, 4, 0, 1, 1, A16, None) == -6
     assert L.tg_decode_ceiling(2, 0, 2, 1, 1, A16, None) == -8     # the int8 loop is mul1's
     assert L.tg_decode_ceiling(2, 2, 4, 1, 1, A16, None) == -8
     assert L.tg_decode_ceiling(2, 0, 0, 0, 1, A16, None) == -8
@@ -297,3 +297,24 @@ def test_mul1_and_int8_flag_validation():
     assert L.tg_fused_workspace_size(mixed, 2) == 0
     assert L.tg_code_table(2, 0, None) == -1
     assert L.trellis_decode(ctypes.byref(d), 0, None) == -1
+
+
+def test_mcg_validation():
+    """code_id 3 (MCG) passes the layer checks on every path, with or without the rounded form;
+    the int8-activation flag stays mul1's."""
+    L = tg.lib()
+    d = _layer(code_id=3)
+    r = _layer(code_id=3, flags=1)
+    assert L.tg_workspace_size(ctypes.byref(d), 1) > 0
+    assert L.trellis_gemv(ctypes.byref(d), A16, A16, 0, 1 << 30, None) == -5      # past the layer checks
+    assert L.trellis_gemv(ctypes.byref(r), A16, A16, 0, 1 << 30, None) == -5
+    assert L.trellis_gemv(ctypes.byref(_layer(code_id=3, flags=2)), A16, A16, 0, 1 << 30, None) == -8
+    assert L.trellis_gemm_small(ctypes.byref(d), 16, A16, 512, A16, 256, 0, 1 << 30, None) == -5
+    assert L.tg_encode_workspace_size(4, 8, 3) == L.tg_encode_workspace_size(4, 8, 0) > 0
+    assert L.tg_code_table(3, 0, None) == -1
+    assert L.trellis_decode(ctypes.byref(d), 0, None) == -1
+    fz = (tg.TgLayer * 2)(_layer(code_id=3, n=1024), _layer(code_id=3, m=128, n=1024))
+    assert L.tg_fused_workspace_size(fz, 2) > 0
+    mixed = (tg.TgLayer * 2)(_layer(code_id=3, n=1024), _layer(code_id=0, n=1024))
+    assert L.tg_fused_workspace_size(mixed, 2) == 0
+    assert L.tg_grouped_workspace_size((tg.TgLayer * 2)(d, _layer(code_id=0)), 2, 4) > 0

@@ -12,7 +12,7 @@ from gpu_common import _refs_module
 from oracle import gemv
 
 
-@pytest.mark.parametrize("key", ["w3_k_c0", "w2_down_c1", "w4_gate_c1", "prefill_gate_m256_c0", "w3i8_k_c2"])
+@pytest.mark.parametrize("key", ["w3_k_c0", "w2_down_c1", "w4_gate_c1", "prefill_gate_m256_c0", "w3i8_k_c2", "w3f_v_c3"])
 def test_first_block_matches_oracle(key):
     mod = _refs_module()
     z = np.load(mod.OUT, allow_pickle=False)

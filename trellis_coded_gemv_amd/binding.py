@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrellis_
 TG_FLAG_ROUND_WEIGHTS = 1
 TG_FLAG_INT8_ACT = 2
 TG_STATUS_SPLITK_TIMEOUT = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS = {0: "TG_OK", -1: "TG_ERR_NULL", -2: "TG_ERR_SHAPE", -3: "TG_ERR_KBITS", -4: "TG_ERR_ALIGN",
           -5: "TG_ERR_WORKSPACE", -6: "TG_ERR_CODE_ID", -7: "TG_ERR_LAUNCH", -8: "TG_ERR_ARG"}

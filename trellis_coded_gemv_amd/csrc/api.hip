@@ -48,7 +48,7 @@ int kernel_form(const tg_layer* L) { return (L->flags & TG_FLAG_INT8_ACT) != 0 ?
 
 int32_t check_layer(const tg_layer* L) {
   if (!L) return TG_ERR_NULL;
-  if (L->code_id < 0 || L->code_id > 2) return TG_ERR_CODE_ID;
+  if (L->code_id < 0 || L->code_id > 3) return TG_ERR_CODE_ID;
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || (L->m % kBlock) != 0 || (L->n % kBlock) != 0) return TG_ERR_SHAPE;
   if (L->m > (1 << 22) || L->n > (1 << 22)) return TG_ERR_SHAPE;
@@ -543,7 +543,7 @@ TG_API int32_t trellis_gemv_grouped(const tg_layer* layers, const tg_layer* d_la
 
 TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) {
   if (!L) return TG_ERR_NULL;
-  if (L->code_id < 0 || L->code_id > 2) return TG_ERR_CODE_ID;
+  if (L->code_id < 0 || L->code_id > 3) return TG_ERR_CODE_ID;
   if (L->k_bits < 1 || L->k_bits > 8) return TG_ERR_KBITS;
   if (L->m <= 0 || L->n <= 0 || L->m % kTile != 0 || L->n % kTile != 0 || L->m > (1 << 22) || L->n > (1 << 22))
     return TG_ERR_SHAPE;
@@ -555,7 +555,7 @@ TG_API int32_t trellis_decode(const tg_layer* L, uint16_t* w_out, void* stream) 
 
 TG_API int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t flags, int32_t workgroups, int32_t steps,
                                  float* out, void* stream) {
-  if (code_id < 0 || code_id > 2) return TG_ERR_CODE_ID;
+  if (code_id < 0 || code_id > 3) return TG_ERR_CODE_ID;
   if ((flags & ~TG_FLAG_INT8_ACT) != 0 || ((flags & TG_FLAG_INT8_ACT) != 0 && code_id != 2)) return TG_ERR_ARG;
   if (k_bits < 1 || k_bits > 8) return TG_ERR_KBITS;
   if (workgroups < 1 || workgroups > 65535 || steps < 1 || steps > (1 << 20)) return TG_ERR_ARG;
@@ -566,7 +566,7 @@ TG_API int32_t tg_decode_ceiling(int32_t k_bits, int32_t code_id, int32_t flags,
 }
 
 TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
-  if (code_id < 0 || code_id > 2) return TG_ERR_CODE_ID;
+  if (code_id < 0 || code_id > 3) return TG_ERR_CODE_ID;
   if (!out) return TG_ERR_NULL;
   if (misaligned(out, 2)) return TG_ERR_ALIGN;
   return launch_status(launch_code_table(code_id, out, (hipStream_t)stream));
@@ -575,7 +575,7 @@ TG_API int32_t tg_code_table(int32_t code_id, uint16_t* out, void* stream) {
 namespace {
 
 int32_t check_encode(int32_t n_tiles, int32_t k_bits, int32_t code_id, float scale) {
-  if (code_id < 0 || code_id > 2) return TG_ERR_CODE_ID;
+  if (code_id < 0 || code_id > 3) return TG_ERR_CODE_ID;
   if (k_bits < 1 || k_bits > 8 || (code_id == 1 && k_bits > 4)) return TG_ERR_KBITS;
   if (n_tiles < 1 || n_tiles > (1 << 24)) return TG_ERR_SHAPE;
   if (!(scale > 0.f) || !(scale < 3.0e38f)) return TG_ERR_ARG;

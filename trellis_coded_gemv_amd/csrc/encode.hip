@@ -52,12 +52,12 @@ struct EncGeom {
 // Squared error of state s against the step's target(s).
 template <int CODE>
 __device__ __forceinline__ float state_error(uint32_t s, float alpha, float v0, float v1, const CodeRegs& cr) {
-  const uint32_t u = code_halves(s, cr);
+  const uint32_t u = CODE == kCodeMcg ? mcg_halves(s, cr) : code_halves(s, cr);
   if constexpr (CODE == 2) {
     const float w = (float)mul1_level(mul1_bytes(s)) * kMul1Step;   // exact
     const float e = alpha * w - v0;
     return e * e;
-  } else if constexpr (CODE == 0) {
+  } else if constexpr (CODE == 0 || CODE == kCodeMcg) {
     const float w = (float)halves_sum_rne(u);
     const float e = alpha * w - v0;
     return e * e;
@@ -300,6 +300,12 @@ hipError_t launch_encode(const float* targets, float alpha, int n_tiles, int k_b
   if (code_id == 2) {
     switch (k_bits) {
       TG_CASE(1, 2) TG_CASE(2, 2) TG_CASE(3, 2) TG_CASE(4, 2) TG_CASE(5, 2) TG_CASE(6, 2) TG_CASE(7, 2) TG_CASE(8, 2)
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (code_id == kCodeMcg) {
+    switch (k_bits) {
+      TG_CASE(1, 3) TG_CASE(2, 3) TG_CASE(3, 3) TG_CASE(4, 3) TG_CASE(5, 3) TG_CASE(6, 3) TG_CASE(7, 3) TG_CASE(8, 3)
       default: return hipErrorInvalidValue;
     }
   }

@@ -93,7 +93,7 @@ __device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, 
     if (active) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if constexpr (CODE == 0) {
+        if constexpr (halves_form(CODE)) {
           const uint32_t he = pack_half2(e[j], e[j]), ho = pack_half2(o[j], o[j]);
           *reinterpret_cast<u32x2*>(xx + xb * XB + 16 * j + 2 * xs) = u32x2{he, ho};
         } else if constexpr (CODE == kCodeMul1) {
@@ -255,6 +255,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
         read_xx(xx, tile, xv);
         const uint32_t nbw = quad_rotate_next(buf[p][0]);
         if constexpr (CODE == 0) decode_dot_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
+        else if constexpr (CODE == kCodeMcg) decode_dot_mcg_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
         else if constexpr (CODE == 1) decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv, acc, cr);
         else if constexpr (CODE == kCodeMul1) decode_dot_mul1_64<K>(buf[p], nbw, xv, acc);
         else decode_dot_mul1_i8_64<K>(buf[p], nbw, xv, xbias[tile], xfac[tile >> 3], acc);
@@ -306,6 +307,9 @@ hipError_t launch_fused(const FusedArgs& a, int k_bits, int variant, bool round_
       return round_weights ? launch_fused_k<0, true>(a, k_bits, grid, s) : launch_fused_k<0, false>(a, k_bits, grid, s);
     case 1:
       return round_weights ? launch_fused_k<1, true>(a, k_bits, grid, s) : launch_fused_k<1, false>(a, k_bits, grid, s);
+    case kCodeMcg:
+      return round_weights ? launch_fused_k<kCodeMcg, true>(a, k_bits, grid, s)
+                           : launch_fused_k<kCodeMcg, false>(a, k_bits, grid, s);
     case kCodeMul1: return launch_fused_k<kCodeMul1, false>(a, k_bits, grid, s);
     case kCodeMul1I8: return launch_fused_k<kCodeMul1I8, false>(a, k_bits, grid, s);
     default: return hipErrorInvalidValue;

@@ -41,6 +41,7 @@
 //
 // mul1 (code_id 2): the geometry of code 0, with the exact fp16 weight in the
 // lo slot of each B word and 0 in the hi slot, as code 0's rounded form.
+// MCG (code_id 3): code 0 with v_mul_u32_u24 in place of v_mad_u32_u24.
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
@@ -230,10 +231,10 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
           for (int e = 0; e < 4; ++e) {
             const int P = STEP * e;
             const uint32_t st = P <= 16 ? ubfe(r1, 16 - P, 16) : ubfe(alignbit(r1, r2, 48 - P), 0, 16);
-            const uint32_t u = code_halves(st, cr);
+            const uint32_t u = halves_of<CODE>(st, cr);
             if constexpr (CODE == 2) bw[tt][e] = (uint32_t)mul1_weight_bits(st);   // (w, 0) against (x~, x~)
             else if constexpr (!ROUND) bw[tt][e] = u;
-            else if constexpr (CODE == 0) bw[tt][e] = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
+            else if constexpr (halves_form(CODE)) bw[tt][e] = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u));
             else bw[tt][e] = pair_weights_rne(u);
           }
         }
@@ -388,7 +389,9 @@ static void launch_mb(const GemmArgs& a, hipStream_t s) {
 template <int CODE>
 static hipError_t launch_code(const GemmArgs& a, int k_bits, bool round_weights, hipStream_t s) {
 #define TG_CASE(K) \
-  case K: round_weights && CODE != 2 ? launch_mb<K, CODE, CODE != 2>(a, s) : launch_mb<K, CODE, false>(a, s); break;
+  case K:                                                                                                  \
+    round_weights && rounded_form(CODE) ? launch_mb<K, CODE, rounded_form(CODE)>(a, s) : launch_mb<K, CODE, false>(a, s); \
+    break;
   switch (k_bits) {
     TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
     default: return hipErrorInvalidValue;
@@ -405,6 +408,7 @@ hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (code_id == 2) return launch_code<2>(a, k_bits, false, s);
+  if (code_id == kCodeMcg) return launch_code<kCodeMcg>(a, k_bits, round_weights, s);
   return code_id == 0 ? launch_code<0>(a, k_bits, round_weights, s) : launch_code<1>(a, k_bits, round_weights, s);
 }
 

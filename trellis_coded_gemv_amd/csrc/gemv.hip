@@ -178,7 +178,7 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
     if (active) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if constexpr (CODE == 0) {
+        if constexpr (halves_form(CODE)) {
           const uint32_t he = pack_half2(e[j], e[j]), ho = pack_half2(o[j], o[j]);
           *reinterpret_cast<u32x2*>(xx_lds + xb * XB + 16 * j + 2 * xs) = u32x2{he, ho};
         } else if constexpr (CODE == kCodeMul1) {
@@ -213,6 +213,8 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
         const uint32_t nbw = quad_rotate_next(buf[p][0]);
         if constexpr (CODE == 0) {
           decode_dot_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
+        } else if constexpr (CODE == kCodeMcg) {
+          decode_dot_mcg_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
         } else if constexpr (CODE == 1) {
           decode_dot_pair_64<K, ROUND>(buf[p], nbw, xv[p & TG_GEMV_XDB], acc, cr);
         } else if constexpr (CODE == kCodeMul1) {
@@ -384,6 +386,7 @@ __global__ __launch_bounds__(64 * 8 * kGemvP) void grouped_kernel(GroupedArgs g,
   a.hu = GATED ? g.hin + (size_t)(2 * e + 1) * g.hin_stride : nullptr;
   if (L.code_id == 0) grouped_dispatch<0, ROUND, GATED>(a, L.k_bits, ob, split, lds);
   else if (L.code_id == 1) grouped_dispatch<1, ROUND, GATED>(a, L.k_bits, ob, split, lds);
+  else if (L.code_id == kCodeMcg) grouped_dispatch<kCodeMcg, ROUND, GATED>(a, L.k_bits, ob, split, lds);
   else grouped_dispatch<kCodeMul1, false, GATED>(a, L.k_bits, ob, split, lds);
 }
 
@@ -430,13 +433,14 @@ static hipError_t launch_k(const GemvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Codes 2 and 3 (mul1) have exact weights: rounding them changes nothing, so
-// they are built once, without the rounded form.
+// The mul1 forms have exact weights: rounding them changes nothing, so they
+// are built once, without the rounded form.
 template <int CODE>
 static hipError_t launch_code(const GemvArgs& a, int k_bits, bool round_weights, hipStream_t s) {
 #define TG_CASE(K)                                                                                \
   case K:                                                                                         \
-    return round_weights && CODE <= 1 ? launch_k<K, CODE, CODE <= 1>(a, s) : launch_k<K, CODE, false>(a, s);
+    return round_weights && rounded_form(CODE) ? launch_k<K, CODE, rounded_form(CODE)>(a, s)      \
+                                               : launch_k<K, CODE, false>(a, s);
   switch (k_bits) {
     TG_CASE(1) TG_CASE(2) TG_CASE(3) TG_CASE(4) TG_CASE(5) TG_CASE(6) TG_CASE(7) TG_CASE(8)
     default: return hipErrorInvalidValue;
@@ -449,6 +453,7 @@ hipError_t launch_gemv(const GemvArgs& a, int k_bits, int variant, bool round_we
     case 0: return launch_code<0>(a, k_bits, round_weights, s);
     case 1: return launch_code<1>(a, k_bits, round_weights, s);
     case kCodeMul1: return launch_code<kCodeMul1>(a, k_bits, false, s);
+    case kCodeMcg: return launch_code<kCodeMcg>(a, k_bits, round_weights, s);
     case kCodeMul1I8: return launch_code<kCodeMul1I8>(a, k_bits, false, s);
     default: return hipErrorInvalidValue;
   }
@@ -513,6 +518,7 @@ __global__ __launch_bounds__(512) void decode_ceiling_kernel(float* __restrict__
     read_xx(xx_lds, jslot, xv);
     const uint32_t nbw = quad_rotate_next(w[0]);
     if constexpr (CODE == 0) decode_dot_64<K, false>(w, nbw, xv, acc, cr);
+    else if constexpr (CODE == kCodeMcg) decode_dot_mcg_64<K, false>(w, nbw, xv, acc, cr);
     else if constexpr (CODE == 1) decode_dot_pair_64<K, false>(w, nbw, xv, acc, cr);
     else if constexpr (CODE == kCodeMul1) decode_dot_mul1_64<K>(w, nbw, xv, acc);
     else decode_dot_mul1_i8_64<K>(w, nbw, xv, (int32_t)xx_lds[jslot] >> 8, 1.0f, acc);
@@ -528,6 +534,7 @@ hipError_t launch_decode_ceiling(int k_bits, int variant, int workgroups, int st
       case 0: TG_LAUNCH(K, 0); break;                    \
       case 1: TG_LAUNCH(K, 1); break;                    \
       case kCodeMul1: TG_LAUNCH(K, kCodeMul1); break;     \
+      case kCodeMcg: TG_LAUNCH(K, kCodeMcg); break;       \
       default: TG_LAUNCH(K, kCodeMul1I8); break;          \
     }                                                    \
     break;

@@ -24,17 +24,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t* __restrict_
   const CodeRegs cr;
   const uint32_t u = code_halves(state, cr);
   if (code_id == 0) out[idx] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
+  else if (code_id == kCodeMcg) out[idx] = __builtin_bit_cast(uint16_t, halves_sum_rne(mcg_halves(state, cr)));
   else if (code_id == 2) out[idx] = mul1_weight_bits(state);
   else out[idx] = (uint16_t)(pair_weights_rne(u) >> (16 * (t & 1)));
 }
 
-// code_id 0 and 2: out[S] = weight of state S; code_id 1: out[2S], out[2S+1] = the state's weight pair.
+// code_id 0, 2 and 3: out[S] = weight of state S; code_id 1: out[2S], out[2S+1] = the state's weight pair.
 __global__ __launch_bounds__(256) void code_table_kernel(uint16_t* __restrict__ out, int code_id) {
   const uint32_t s = blockIdx.x * 256 + threadIdx.x;
   const CodeRegs cr;
   const uint32_t u = code_halves(s, cr);
   if (code_id == 0) {
     out[s] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
+  } else if (code_id == kCodeMcg) {
+    out[s] = __builtin_bit_cast(uint16_t, halves_sum_rne(mcg_halves(s, cr)));
   } else if (code_id == 2) {
     out[s] = mul1_weight_bits(s);
   } else {

@@ -93,8 +93,8 @@ __device__ __forceinline__ u32x4 pf_decode(const uint32_t (&w)[PfGeom<K, CODE>::
       if constexpr (CODE == 2) {
         out[d] = mul1_weight_pair(st[2 * d], st[2 * d + 1]);
       } else {
-        const uint16_t lo = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(st[2 * d], cr)));
-        const uint16_t hi = __builtin_bit_cast(uint16_t, halves_sum_rne(code_halves(st[2 * d + 1], cr)));
+        const uint16_t lo = __builtin_bit_cast(uint16_t, halves_sum_rne(halves_of<CODE>(st[2 * d], cr)));
+        const uint16_t hi = __builtin_bit_cast(uint16_t, halves_sum_rne(halves_of<CODE>(st[2 * d + 1], cr)));
         out[d] = (uint32_t)lo | ((uint32_t)hi << 16);
       }
     }
@@ -272,6 +272,7 @@ hipError_t launch_prefill_mfma(const uint32_t* codes, const uint16_t* scales, co
                                hipStream_t s) {
   if (code_id == 1) return launch_pf_mfma<1>(codes, scales, sign_out, Xt, Y, ldy, m, n, M, k_bits, s);
   if (code_id == 2) return launch_pf_mfma<2>(codes, scales, sign_out, Xt, Y, ldy, m, n, M, k_bits, s);
+  if (code_id == kCodeMcg) return launch_pf_mfma<kCodeMcg>(codes, scales, sign_out, Xt, Y, ldy, m, n, M, k_bits, s);
   return launch_pf_mfma<0>(codes, scales, sign_out, Xt, Y, ldy, m, n, M, k_bits, s);
 }
 

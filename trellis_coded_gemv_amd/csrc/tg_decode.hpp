@@ -94,7 +94,8 @@ __device__ __forceinline__ constexpr int span_lead(int n) {
 // the next, into one accumulator per row and column parity: independent chains
 // that a wave can issue back to back, instead of one chain through a register
 // whose every instruction waits for the previous one.
-template <int K, bool ROUND>
+// CODE: 0 or kCodeMcg (the two codes in halves_form).
+template <int K, bool ROUND, int CODE = 0>
 __device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xx)[16],
                                               float (&acc)[4], const CodeRegs& cr) {
   constexpr int CW = TG_DECODE_ILP >= 8 ? 2 : 1;    // columns per group
@@ -114,7 +115,7 @@ __device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32
 #pragma unroll
     for (int cc = 0; cc < CW; ++cc)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u[r][cc] = code_halves(st[r][cc], cr);
+      for (int r = 0; r < 4; ++r) u[r][cc] = halves_of<CODE>(st[r][cc], cr);
 #pragma unroll
     for (int cc = 0; cc < CW; ++cc)
 #pragma unroll
@@ -129,6 +130,42 @@ __device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] = CW == 2 ? a2[r][0] + a2[r][1] : a2[r][0];
+}
+
+// MCG (code_id 3) with the windows paired as for mul1 when K divides 16: per
+// two weights one v_alignbit, then per weight an SDWA-selected v_mul_u32_u24,
+// v_and_or_b32 and v_dot2c_f32_f16 against (x~, x~). Other K: decode_dot_64.
+template <int K, bool ROUND>
+__device__ __forceinline__ void decode_dot_mcg_64(const uint32_t (&w)[2 * K], uint32_t nb, const uint32_t (&xx)[16],
+                                                  float (&acc)[4], const CodeRegs& cr) {
+  if constexpr (16 % K == 0) {
+    constexpr int D = 16 / K;
+    const MulReg mr;
+#pragma unroll
+    for (int n0 = 0; n0 < 32; n0 += 4) {
+      uint32_t u[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t t = lane_span<K>(w, nb, span_lead<K>(n0 + i));
+        u[i][0] = (((t >> 16) * mr.m) & cr.mask) | cr.xr;
+        u[i][1] = (((t & 0xFFFFu) * mr.m) & cr.mask) | cr.xr;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tl = span_lead<K>(n0 + i) + h * D;
+          if constexpr (ROUND) {
+            const uint32_t wr = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u[i][h]));
+            acc[tl >> 4] = dot2(wr, xx[tl & 15], acc[tl >> 4]);
+          } else {
+            acc[tl >> 4] = dot2(u[i][h], xx[tl & 15], acc[tl >> 4]);
+          }
+        }
+    }
+  } else {
+    decode_dot_64<K, ROUND, kCodeMcg>(w, nb, xx, acc, cr);
+  }
 }
 
 // Pair code (code_id 1): the lane's 64 weights are 32 states, state s at

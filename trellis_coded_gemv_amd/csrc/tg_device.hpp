@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tg_internal.hpp"
+
 namespace tg {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -17,7 +19,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Code constants (shared by code_id 0 and the pair code, code_id 1).
+// Code constants (shared by code_id 0, the pair code (code_id 1) and MCG (code_id 3);
+// mul1 uses the multiplier).
 constexpr uint32_t kMul = 0x009E3779u;   // 24-bit LCG multiplier: one full-rate v_mad_u32_u24
 constexpr uint32_t kAdd = 0x7F4A7C15u;
 constexpr uint32_t kMask = 0x8FFF8FFFu;  // sign, 2 low exponent bits, 10 fraction bits per half
@@ -41,6 +44,19 @@ struct CodeRegs {
 __device__ __forceinline__ uint32_t code_halves(uint32_t state, const CodeRegs& c) {
   const uint32_t h = state * kMul + kAdd;  // state < 2^16: v_mad_u32_u24
   return (h & c.mask) | c.xr;
+}
+
+// MCG (code_id 3; "Trellis Quantization" lecture, Part eleven): the same
+// halves from the generator with its additive constant dropped (multiply only).
+__device__ __forceinline__ uint32_t mcg_halves(uint32_t state, const CodeRegs& c) {
+  return ((state * kMul) & c.mask) | c.xr;   // v_mul_u32_u24, v_and_or_b32
+}
+
+// The halves word of a state for either code in halves_form.
+template <int CODE>
+__device__ __forceinline__ uint32_t halves_of(uint32_t state, const CodeRegs& c) {
+  if constexpr (CODE == kCodeMcg) return mcg_halves(state, c);
+  else return code_halves(state, c);
 }
 
 // fp16 weight = round-to-nearest-even(lo + hi), as a 16-bit pattern.

@@ -15,10 +15,15 @@ constexpr int kGemvThreads = 64 * kGemvWaves;
 #define TG_GEMV_P 1
 #endif
 constexpr int kGemvP = TG_GEMV_P;        // batch-1 path: waves per tile row (interleaved steps)
-// Kernel forms of the codes: code_id 0 and 1 as they are; code_id 2 (mul1)
-// against fp32 x~, and against the int8 form of x~ (TG_FLAG_INT8_ACT).
+// Kernel forms of the codes: code_id 0, 1 and 3 (MCG) as they are; code_id 2
+// (mul1) against fp32 x~, and against the int8 form of x~ (TG_FLAG_INT8_ACT).
 constexpr int kCodeMul1 = 2;
-constexpr int kCodeMul1I8 = 3;
+constexpr int kCodeMcg = 3;
+constexpr int kCodeMul1I8 = 4;
+// Codes whose weight is the sum of two binary16 halves, dotted against (x~, x~) pairs.
+constexpr bool halves_form(int code) { return code == 0 || code == kCodeMcg; }
+// Codes whose weights involve a rounding (mul1's are exact): they also have the TG_FLAG_ROUND_WEIGHTS form.
+constexpr bool rounded_form(int code) { return code == 0 || code == 1 || code == kCodeMcg; }
 constexpr int kMaxChunkBlocks = 64;      // 128-blocks of x~ held in LDS by one GEMV workgroup
 constexpr size_t kWsHeader = 256;        // every workspace starts with this header; word 0 = status
 constexpr uint32_t kStatusSplitkTimeout = 1u;   // a split-K wait ran out (its outputs were written as NaN)
