@@ -30,7 +30,8 @@ steps between two synchronisations, HIP events on the launch stream, steps
 replayed from a captured HIP graph), the roofline of the dominant kernel, the
 CPU oracle timed on a bounded sample of the same workload on every host core
 of the process's affinity mask, and short measurements of workloads 2, 4 and 5
-as context.
+and of the bench's workload with the other codes (MCG, mul1 with int8
+activations, the pair code) as context.
 
 Roofline. The dominant launch (the one moving the most bytes) is timed alone:
 the same K steps restricted to its launches, replayed from their own graph,
@@ -648,6 +649,21 @@ def measure(workload, code_id, steps, warmup, use_graph, hot=True):
     return info, t, rec, value, ms_per_step, dom_launch_ms
 
 
+def context_codes(text, code_id, int8, workload):
+    """The (code_id, int8) pairs of a --context-codes list ('3,2i8,1'), without the line's own and
+    without int8 forms the workload cannot run (mul1's int8 form, batch-1 workloads only)."""
+    out = []
+    for spec in [v.strip() for v in text.split(",") if v.strip()]:
+        i8 = spec.endswith("i8")
+        cid = int(spec[:-2] if i8 else spec)
+        if cid not in (0, 1, 2, 3):
+            raise ValueError(f"unknown code in --context-codes: {spec}")
+        if (cid, i8) == (code_id, int8) or (i8 and (cid != 2 or workload not in (1, 2, 3))):
+            continue
+        out.append((cid, i8))
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -665,6 +681,9 @@ def main(argv=None):
                     help="oracle sample: 128-output blocks per tensor (tokens for workloads 5/7); 0 skips it")
     ap.add_argument("--context", default="2,4,5",
                     help="comma-separated workloads also measured briefly as context ('' for none)")
+    ap.add_argument("--context-codes", default="3,2i8,1",
+                    help="comma-separated codes (a trailing 'i8': mul1 with int8 activations) also measured "
+                         "briefly on the bench's workload as context ('' for none)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="after timing, write (fill) and read (sum) this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -737,6 +756,17 @@ def main(argv=None):
         _, _, r, _, _, _ = measure(w, args.code, min(steps, 50), 5, not args.no_graph, hot=False)
         others.append(r)
     config["other_workloads"] = others
+    codes = []
+    for cid, i8 in context_codes(args.context_codes, args.code, args.int8, args.workload):
+        log("context code", cid, "int8" if i8 else "")
+        saved = LAYER_FLAGS["int8"]
+        LAYER_FLAGS["int8"] = i8
+        try:
+            _, _, r, _, _, _ = measure(args.workload, cid, min(steps, 50), 5, not args.no_graph, hot=False)
+        finally:
+            LAYER_FLAGS["int8"] = saved
+        codes.append(r)
+    config["other_codes"] = codes
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",

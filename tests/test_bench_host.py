@@ -3,6 +3,8 @@ import subprocess
 import sys
 import os
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -74,3 +76,15 @@ def test_int8_mode_needs_mul1_and_keys_its_traffic(monkeypatch):
     arr, x = bench.linear_inputs(inputs, inputs.WORKLOADS[1], 1, 2)["linear"]
     for (kind, name, b), y in refs.items():
         assert np.array_equal(y, ogemv.gemv_int8_rows(arr, x, np.arange(128 * b, 128 * b + 128)))
+
+
+def test_context_codes_list():
+    """The other codes measured beside the bench line: the line's own code and int8 forms that the
+    workload cannot run are left out."""
+    assert bench.context_codes("3,2i8,1", 0, False, 3) == [(3, False), (2, True), (1, False)]
+    assert bench.context_codes("3,2i8,1", 3, False, 3) == [(2, True), (1, False)]
+    assert bench.context_codes("3,2i8,1", 2, True, 3) == [(3, False), (1, False)]
+    assert bench.context_codes("3,2i8", 0, False, 4) == [(3, False)]            # no int8 on the MFMA path
+    assert bench.context_codes("", 0, False, 3) == []
+    with pytest.raises(ValueError):
+        bench.context_codes("5", 0, False, 3)
