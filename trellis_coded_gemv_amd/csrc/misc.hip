@@ -23,8 +23,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t* __restrict_
   const uint32_t state = (uint32_t)(v >> (48 - q)) & 0xFFFFu;
   const CodeRegs cr;
   const uint32_t u = code_halves(state, cr);
-  if (code_id == 0) out[idx] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
-  else if (code_id == kCodeMcg) out[idx] = __builtin_bit_cast(uint16_t, halves_sum_rne(mcg_halves(state, cr)));
+  // the rounded GEMV forms' half add (halves_sum_word), so the bit-exact table and decode checks cover it
+  if (code_id == 0) out[idx] = (uint16_t)halves_sum_word(u);
+  else if (code_id == kCodeMcg) out[idx] = (uint16_t)halves_sum_word(mcg_halves(state, cr));
   else if (code_id == 2) out[idx] = mul1_weight_bits(state);
   else out[idx] = (uint16_t)(pair_weights_rne(u) >> (16 * (t & 1)));
 }
@@ -35,9 +36,9 @@ __global__ __launch_bounds__(256) void code_table_kernel(uint16_t* __restrict__ 
   const CodeRegs cr;
   const uint32_t u = code_halves(s, cr);
   if (code_id == 0) {
-    out[s] = __builtin_bit_cast(uint16_t, halves_sum_rne(u));
+    out[s] = (uint16_t)halves_sum_word(u);
   } else if (code_id == kCodeMcg) {
-    out[s] = __builtin_bit_cast(uint16_t, halves_sum_rne(mcg_halves(s, cr)));
+    out[s] = (uint16_t)halves_sum_word(mcg_halves(s, cr));
   } else if (code_id == 2) {
     out[s] = mul1_weight_bits(s);
   } else {

@@ -121,7 +121,7 @@ __device__ __forceinline__ void decode_dot_64(const uint32_t (&w)[2 * K], uint32
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (ROUND) {
-          const uint32_t wr = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u[r][cc]));
+          const uint32_t wr = halves_sum_word(u[r][cc]);
           a2[r][cc] = dot2(wr, xx[c0 + cc], a2[r][cc]);
         } else {
           a2[r][cc] = dot2(u[r][cc], xx[c0 + cc], a2[r][cc]);
@@ -156,7 +156,7 @@ __device__ __forceinline__ void decode_dot_mcg_64(const uint32_t (&w)[2 * K], ui
         for (int i = 0; i < 4; ++i) {
           const int tl = span_lead<K>(n0 + i) + h * D;
           if constexpr (ROUND) {
-            const uint32_t wr = (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(u[i][h]));
+            const uint32_t wr = halves_sum_word(u[i][h]);
             acc[tl >> 4] = dot2(wr, xx[tl & 15], acc[tl >> 4]);
           } else {
             acc[tl >> 4] = dot2(u[i][h], xx[tl & 15], acc[tl >> 4]);

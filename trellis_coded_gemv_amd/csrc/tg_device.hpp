@@ -65,6 +65,19 @@ __device__ __forceinline__ _Float16 halves_sum_rne(uint32_t u) {
   return p[0] + p[1];
 }
 
+// The same weight as the word (w, 0): one v_add_f16 whose SDWA selects take the two halves
+// and whose unused destination bits are written as zeros (the compiler adds a v_pack for the
+// zero half otherwise). The VALU dot products of the rounded forms take it against (x~, x~).
+// Not for matrix-core operands: the compiler's wait states between a VALU write and an MFMA
+// read do not see inside inline asm, so the MFMA path keeps halves_sum_rne.
+__device__ __forceinline__ uint32_t halves_sum_word(uint32_t u) {
+  uint32_t w;
+  asm("v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1"
+      : "=v"(w)
+      : "v"(u));
+  return w;
+}
+
 __device__ __forceinline__ uint32_t ubfe(uint32_t v, uint32_t off, uint32_t width) {
   return __builtin_amdgcn_ubfe(v, off, width);
 }
