@@ -68,7 +68,7 @@ def _cases():
     cases["w3_down_c2"] = dict(m=m, n=n, k=k, seed=inputs.CFG3.seed, tensor=6, code_id=2,
                                x=(inputs.CFG3.seed, 6, 1), pick=None, sample_seed=6)
     m, n, k = inputs.CFG4.tensors["gate"]
-    for cid in (0, 1):
+    for cid in (0, 1, 2, 3):
         cases[f"w4_gate_c{cid}"] = dict(m=m, n=n, k=k, seed=inputs.CFG4.seed, tensor=0, code_id=cid,
                                         x=(inputs.CFG4.seed, 0, inputs.CFG4.batch), pick=None, sample_seed=4)
     cases["prefill_gate_m256_c0"] = dict(m=m, n=n, k=k, seed=inputs.CFG4.seed, tensor=0, code_id=0,

@@ -156,13 +156,14 @@ def test_mcg_gemv_full_size(name):
 
 
 @pytest.mark.parametrize("flags", [0, RW])
-@pytest.mark.parametrize("M", [1, 16, 33])
-def test_mcg_gemm_small(M, flags):
+@pytest.mark.parametrize("M,k", [(1, 3), (16, 3), (33, 3), (16, 2), (5, 4), (16, 4), (40, 8), (16, 1)])
+def test_mcg_gemm_small(M, k, flags):
+    """K = 2, 4, 8 run the paired windows and the paired x~ column order; K = 1, 3 the plain form."""
     dev = device()
     import torch
-    arr = _layer(256, 512, 3, 9800 + M)
+    arr = _layer(256, 512, k, 9800 + M + 10 * k)
     X = inputs.make_x(512, 9800 + M, rows=M) if M > 1 else inputs.make_x(512, 9800 + M)[None, :]
-    say("mcg gemm M", M, flags)
+    say("mcg gemm M", M, k, flags)
     Y = tg.trellis_gemm_small(tg.DeviceLayer(arr, dev, flags=flags), tg.fp16_tensor(X, dev))
     torch.cuda.synchronize()
     Y = Y.cpu().numpy()
@@ -209,3 +210,19 @@ def test_mcg_decode_ceiling_runs():
     out = tg.decode_ceiling(2, MCG, 8, 16)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("code_id", [2, 3])
+def test_multiply_only_codes_gemm_small_config4(code_id):
+    """The 28672 x 8192 gate projection at K=4 with 16 rows (paired windows and column order) for
+    mul1 and MCG: two outputs of every 128-output block of every row against stored oracle outputs."""
+    dev = device()
+    import torch
+    arr, X, rows, _, ref = full_size_case(f"w4_gate_c{code_id}")
+    say("gemm_small cfg4", code_id)
+    Y = tg.trellis_gemm_small(tg.DeviceLayer(arr, dev), tg.fp16_tensor(X, dev))
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    assert np.isfinite(Y).all()
+    for r in range(X.shape[0]):
+        assert rel_err(Y[r, rows], ref[r]) <= REL_TOL, r

@@ -207,13 +207,14 @@ def test_mul1_gemv_full_size(key, flags):
     assert err <= TIGHT
 
 
-@pytest.mark.parametrize("M", [1, 16, 33])
-def test_mul1_gemm_small(M):
+@pytest.mark.parametrize("M,k", [(1, 3), (16, 3), (33, 3), (16, 2), (7, 4), (16, 4), (48, 8)])
+def test_mul1_gemm_small(M, k):
+    """K = 2, 4, 8 run the paired windows and the paired x~ column order; K = 3 the plain form."""
     dev = device()
     import torch
-    arr = _layer(256, 512, 3, 8900 + M)
+    arr = _layer(256, 512, k, 8900 + M + 10 * k)
     X = inputs.make_x(512, 8900 + M, rows=M) if M > 1 else inputs.make_x(512, 8900 + M)[None, :]
-    say("mul1 gemm M", M)
+    say("mul1 gemm M", M, k)
     Y = tg.trellis_gemm_small(tg.DeviceLayer(arr, dev), tg.fp16_tensor(X, dev))
     torch.cuda.synchronize()
     Y = Y.cpu().numpy()

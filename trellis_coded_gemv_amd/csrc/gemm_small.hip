@@ -42,6 +42,12 @@
 // mul1 (code_id 2): the geometry of code 0, with the exact fp16 weight in the
 // lo slot of each B word and 0 in the hi slot, as code 0's rounded form.
 // MCG (code_id 3): code 0 with v_mul_u32_u24 in place of v_mad_u32_u24.
+// For both at K = 2, 4, 8 a lane's four columns are two pairs 16/K apart
+// (MfmaGeom::PAIRED): per tile and lane three v_alignbit give two 32-bit
+// spans, each holding two windows, and every window feeds its multiply through
+// an SDWA word select, with no extract (11 VALU per 4 weights against 13); the
+// x~ operand holds the same columns in the same order (xt_prep_kernel's
+// paired order), and the B and A k-orders agree, so the product is unchanged.
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
@@ -63,14 +69,31 @@
 
 namespace tg {
 
+// Paired layout: lane group g of a tile row holds input columns lead, lead + 1, lead + D,
+// lead + D + 1 with D = 16/K and lead = the (2g)-th column c of the tile with c mod 2D < D (the
+// windows 16 stream bits after those of lead and lead + 1 are those of lead + D and lead + D + 1).
+// For K = 8 that is 4g .. 4g+3, the plain order.
+__host__ __device__ constexpr int paired_lead(int K, int g) {
+  const int D = 16 / K, nl = 2 * g;
+  return (nl / D) * 2 * D + nl % D;
+}
+// Position of tile column c in the paired order (the inverse of the layout above).
+__host__ __device__ constexpr int paired_pos(int K, int c) {
+  const int D = 16 / K, r = c % (2 * D);
+  const int nl = (c / (2 * D)) * D + r % D;
+  return 4 * (nl >> 1) + (r >= D ? 2 : 0) + (nl & 1);
+}
+
 // x~ = H diag(s_in) x / sqrt(128) for every row (rows >= M are zero). Mode 0:
 // plain fp16 in tile-column order, [n/16][mpad rows][16 columns], so that the
-// 16 rows x 16 columns one MFMA step reads are 512 contiguous bytes. Modes 1
+// 16 rows x 16 columns one MFMA step reads are 512 contiguous bytes; with
+// paired_k > 0 the 16 columns of a tile column are in the paired order of that
+// K (paired_pos). Modes 1
 // and 2: fp16 pairs, the rotated column pairs (x~0 - x~1, x~0 + x~1) or the
 // plain pairs (x~0, x~1), row stride n/2 words.
 __global__ __launch_bounds__(64) void xt_prep_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                       const uint32_t* __restrict__ sign_in, uint32_t* __restrict__ xt,
-                                                      int n, int M, int mode) {
+                                                      int n, int M, int mode, int paired_k) {
   const int lane = threadIdx.x, row = blockIdx.y;
   if (mode == 0) {
     uint32_t d0 = 0u, d1 = 0u;
@@ -78,8 +101,10 @@ __global__ __launch_bounds__(64) void xt_prep_kernel(const uint16_t* __restrict_
     uint16_t* xh = reinterpret_cast<uint16_t*>(xt);
     const size_t mpad = gridDim.y;
     const int c0 = blockIdx.x * kBlock + lane, c1 = c0 + 64;
-    xh[((size_t)(c0 >> 4) * mpad + row) * 16 + (c0 & 15)] = (uint16_t)d0;
-    xh[((size_t)(c1 >> 4) * mpad + row) * 16 + (c1 & 15)] = (uint16_t)d1;
+    const int p0 = paired_k ? paired_pos(paired_k, c0 & 15) : c0 & 15;
+    const int p1 = paired_k ? paired_pos(paired_k, c1 & 15) : c1 & 15;
+    xh[((size_t)(c0 >> 4) * mpad + row) * 16 + p0] = (uint16_t)d0;
+    xh[((size_t)(c1 >> 4) * mpad + row) * 16 + p1] = (uint16_t)d1;
   } else {
     uint32_t d = 0u;
     if (row < M)
@@ -95,7 +120,10 @@ struct MfmaGeom {
   static constexpr int STEP = CODE != 1 ? K : 2 * K;      // stream bits between a lane's 4 windows
   static constexpr int WPT = 8 * K;                       // code words per tile
   static constexpr int LW = SPAN * K;                     // code words a lane loads per step
-  static constexpr int NLW = 3 * STEP > 16 ? 3 : 2;       // staged words a lane reads per tile
+  // Multiply-only codes with K dividing 16 (and K > 1): the lane's four columns are two pairs 16/K
+  // apart, each pair's windows in one 32-bit span (paired_columns).
+  static constexpr bool PAIRED = (CODE == kCodeMcg || CODE == kCodeMul1) && (K == 2 || K == 4 || K == 8);
+  static constexpr int NLW = PAIRED || 3 * STEP > 16 ? 3 : 2;   // staged words a lane reads per tile
 };
 
 // Per-lane code words of one tile column step: lane l holds K words of tile
@@ -136,8 +164,10 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
   constexpr int NLW = G::NLW, WPT = G::WPT, LW = G::LW, SPAN = G::SPAN, STEP = G::STEP;
   const int lane = threadIdx.x & 63;
   const int jrow = lane & 15, g = lane >> 4;
-  // first stream bit of the lane's four windows, and the tile of the step they lie in
-  const int b0 = CODE != 1 ? K * (16 * jrow + 4 * g) : 2 * K * (8 * jrow + 4 * (g & 1));
+  // first stream bit of the lane's four windows (paired: of its first span), and the tile of the
+  // step they lie in
+  const int b0 = G::PAIRED ? K * (16 * jrow + paired_lead(K, g))
+                           : CODE != 1 ? K * (16 * jrow + 4 * g) : 2 * K * (8 * jrow + 4 * (g & 1));
   const int toff = CODE != 1 ? 0 : (g >> 1) * WPT;
   const int q0 = b0 & 31, j0 = b0 >> 5;
   int widx[NLW];
@@ -194,6 +224,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
   for (int p = 0; p < PF; ++p) issue(cw[p], xa[p]);
 
   const CodeRegs cr;
+  const MulReg mr;
   for (int i0 = 0; i0 < ncol; i0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
@@ -227,6 +258,24 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int ob, int col0, i
           const uint32_t r1 = alignbit(wv[t][0], wv[t][1], shift);
           uint32_t r2 = 0u;
           if constexpr (NLW == 3) r2 = alignbit(wv[t][1], wv[t][2], shift);
+          if constexpr (G::PAIRED) {
+            // spans at the lane's first two columns; each holds the window 16/K columns on in its
+            // low half. B word order: lead, lead + 1, lead + D, lead + D + 1.
+            const uint32_t sp[2] = {r1, alignbit(r1, r2, 32 - K)};
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const uint32_t ph = (sp[i] >> 16) * mr.m, pl = (sp[i] & 0xFFFFu) * mr.m;
+              if constexpr (CODE == kCodeMul1) {
+                bw[tt][i] = mul1_weight_word(ph & kByteMask);
+                bw[tt][2 + i] = mul1_weight_word(pl & kByteMask);
+              } else {
+                const uint32_t uh = (ph & cr.mask) | cr.xr, ul = (pl & cr.mask) | cr.xr;
+                bw[tt][i] = ROUND ? (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(uh)) : uh;
+                bw[tt][2 + i] = ROUND ? (uint32_t)__builtin_bit_cast(uint16_t, halves_sum_rne(ul)) : ul;
+              }
+            }
+            continue;
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int P = STEP * e;
@@ -403,8 +452,10 @@ static hipError_t launch_code(const GemmArgs& a, int k_bits, bool round_weights,
 hipError_t launch_gemm_small(const GemmArgs& a, const uint16_t* X, int64_t ldx, const uint32_t* sign_in, int k_bits,
                              int code_id, bool round_weights, hipStream_t s) {
   const int mode = code_id == 1 ? (round_weights ? 2 : 1) : 0;
+  // the paired column order of the multiply-only codes (identity at K = 8)
+  const int paired_k = (code_id == kCodeMul1 || code_id == kCodeMcg) && (k_bits == 2 || k_bits == 4) ? k_bits : 0;
   hipLaunchKernelGGL(xt_prep_kernel, dim3(a.n / kBlock, a.mpad), dim3(64), 0, s, X, ldx, sign_in,
-                     const_cast<uint32_t*>(a.xt), a.n, a.M, mode);
+                     const_cast<uint32_t*>(a.xt), a.n, a.M, mode, paired_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (code_id == 2) return launch_code<2>(a, k_bits, false, s);

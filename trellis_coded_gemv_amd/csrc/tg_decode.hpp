@@ -49,18 +49,11 @@ __device__ __forceinline__ uint32_t lane_window(const uint32_t (&w)[2 * K], uint
   return ubfe(alignbit(wj, wj1, 16), 32 - q, 16);
 }
 
-// Multiply-only codes (mul1): with K dividing 16, the window 16 stream bits
-// after window tl is window tl + 16/K, so one 32-bit span holds two windows
-// (tl in its high half, tl + 16/K in its low half) and one v_alignbit serves
-// both. The multiplier sits in an SGPR, so each half feeds v_mul_u32_u24 through
-// an SDWA word select and needs no extract of its own.
-struct MulReg {
-  uint32_t m;
-  __device__ __forceinline__ MulReg() : m(kMul) {
-    asm volatile("" : "+s"(m));
-    m &= 0xFFFFFFu;   // known 24-bit: v_mul_u32_u24
-  }
-};
+// Multiply-only codes (MCG, mul1): with K dividing 16, the window 16 stream
+// bits after window tl is window tl + 16/K, so one 32-bit span holds two
+// windows (tl in its high half, tl + 16/K in its low half) and one v_alignbit
+// serves both. The multiplier sits in an SGPR (MulReg), so each half feeds
+// v_mul_u32_u24 through an SDWA word select and needs no extract of its own.
 
 // The 32 stream bits starting at window tl's first bit.
 template <int K>

@@ -46,6 +46,16 @@ __device__ __forceinline__ uint32_t code_halves(uint32_t state, const CodeRegs& 
   return (h & c.mask) | c.xr;
 }
 
+// The multiplier in an SGPR, known to fit 24 bits: a multiply-only code's v_mul_u32_u24 can then
+// take its state through an SDWA word select (SDWA operands take no literal).
+struct MulReg {
+  uint32_t m;
+  __device__ __forceinline__ MulReg() : m(kMul) {
+    asm volatile("" : "+s"(m));
+    m &= 0xFFFFFFu;
+  }
+};
+
 // MCG (code_id 3; "Trellis Quantization" lecture, Part eleven): the same
 // halves from the generator with its additive constant dropped (multiply only).
 __device__ __forceinline__ uint32_t mcg_halves(uint32_t state, const CodeRegs& c) {
@@ -234,6 +244,13 @@ __device__ __forceinline__ uint32_t mul1_biased_half(uint32_t state) {
 __device__ __forceinline__ uint16_t mul1_weight_bits(uint32_t state) {
   const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)mul1_biased_half(state));
   return __builtin_bit_cast(uint16_t, (_Float16)(h - (_Float16)48.0f));
+}
+
+// The same from the masked product bytes (state * multiplier & 0x3F3F3F3F), as the word (w, 0).
+__device__ __forceinline__ uint32_t mul1_weight_word(uint32_t bytes) {
+  const uint32_t biased = __builtin_amdgcn_udot4(bytes, kByteOnes, kMul1Magic - (uint32_t)kMul1Offset, false);
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)biased);
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(h - (_Float16)48.0f));
 }
 
 // Two weights as one packed word (a in the low half): one packed binary16 subtract.
