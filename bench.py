@@ -753,7 +753,7 @@ def main(argv=None):
         if w == args.workload:
             continue
         log("context workload", w)
-        _, _, r, _, _, _ = measure(w, args.code, min(steps, 50), 5, not args.no_graph, hot=False)
+        _, _, r, _, _, _ = measure(w, args.code, steps, args.warmup, not args.no_graph, hot=False)
         others.append(r)
     config["other_workloads"] = others
     codes = []
@@ -762,7 +762,7 @@ def main(argv=None):
         saved = LAYER_FLAGS["int8"]
         LAYER_FLAGS["int8"] = i8
         try:
-            _, _, r, _, _, _ = measure(args.workload, cid, min(steps, 50), 5, not args.no_graph, hot=False)
+            _, _, r, _, _, _ = measure(args.workload, cid, steps, args.warmup, not args.no_graph, hot=False)
         finally:
             LAYER_FLAGS["int8"] = saved
         codes.append(r)
