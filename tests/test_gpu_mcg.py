@@ -226,3 +226,20 @@ def test_multiply_only_codes_gemm_small_config4(code_id):
     assert np.isfinite(Y).all()
     for r in range(X.shape[0]):
         assert rel_err(Y[r, rows], ref[r]) <= REL_TOL, r
+
+
+@pytest.mark.parametrize("k", [4, 6, 8])
+def test_mcg_encode_high_rates_consistent(k):
+    """Wider steps (the oracle's search is too slow here): each stored stream decodes, through the
+    oracle's walk and code, to the error the encoder reports, and the error falls with the rate."""
+    dev = device()
+    import torch
+    tgt = np.random.default_rng(9450 + k).standard_normal((3, 256)).astype(np.float32)
+    say("mcg encode", k)
+    codes, err = tg.trellis_encode(torch.from_numpy(tgt).to(dev), k, MCG, 0.75)
+    torch.cuda.synchronize()
+    codes, err = codes.cpu().numpy().view(np.uint32), err.cpu().numpy()
+    for i in range(3):
+        recomputed = ov.tile_errors(codes[i], tgt[i], k, MCG, 0.75)
+        assert abs(recomputed - float(err[i])) <= 1e-4 * max(recomputed, 1e-3), i
+    assert float(err.mean()) / 256 < {4: 0.012, 6: 0.004, 8: 0.003}[k]

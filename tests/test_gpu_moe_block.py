@@ -59,3 +59,22 @@ def test_moe_block_pair_code_and_invalid_ids():
         ref = moe.moe_block(gu, dn, [4, 0], [0.4, 0.2], x)
         assert np.isfinite(y.cpu().numpy()).all()
         assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("code_id", [2, 3])
+def test_moe_block_multiply_only_codes(code_id):
+    """mul1 and MCG experts, each tensor with K drawn from {1, 2, 3} (paired windows at K = 1 and 2,
+    the per-window form at K = 3)."""
+    dev = device()
+    import torch
+    wl = inputs.MoEWorkload(experts=8, tokens=2)
+    gu, gut, dn, dnt = _tables(dev, wl, code_id=code_id)
+    sel = wl.routing()[1][:4].astype(np.int32)
+    w = np.array([0.1, 0.2, 0.3, 0.4], np.float32)
+    x = inputs.make_x(wl.hidden, 78 + code_id)
+    say("moe block code", code_id, list(sel))
+    y = tg.trellis_moe_block(gut, dnt, torch.from_numpy(sel).to(dev), torch.from_numpy(w).to(dev),
+                             tg.fp16_tensor(x, dev))
+    torch.cuda.synchronize()
+    ref = moe.moe_block(gu, dn, sel, w, x)
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
