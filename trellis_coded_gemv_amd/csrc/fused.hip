@@ -147,22 +147,39 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   const X16 raw1 = load_x16(a.x, a.L[lay1].sign_in, xfirst);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Code prefetch ring over the run's units; units past the run read a dummy line.
+  // Code prefetch ring over the run's units; units past the run read a dummy line. Units are
+  // issued in order, so the issue position (layer il, output block iob, step ist) advances by one
+  // per issue in registers: no division and no search of the layer table per unit (each was a
+  // chain of scalar loads and a division sequence in front of every prefetch).
   uint32_t buf[PF][NW];
   const uint32_t* __restrict__ dummy = a.L[lay0].codes;
-  auto issue = [&](int u, uint32_t(&dst)[NW]) {
+  int iu = u0, il = lay0, iob, ist;
+  {
+    const int rel = u0 - a.L[lay0].unit0;
+    iob = rel / spr;
+    ist = rel - iob * spr;
+  }
+  const uint32_t* __restrict__ icodes = a.L[il].codes;
+  int inext = il + 1 < kFusedMaxLayers ? a.L[il + 1].unit0 : INT32_MAX;   // first unit of the next layer
+  auto issue = [&](uint32_t(&dst)[NW]) {
     const uint32_t* p = dummy;
-    if (u < u1) {
-      const int l = fused_layer_of(a, u);
-      const int rel = u - a.L[l].unit0;
-      const int ob = rel / spr, st = rel - ob * spr;
-      if (st * 16 + jslot < n16)
-        p = a.L[l].codes + ((size_t)(ob * 8 + wave) * n16 + (size_t)st * 16) * (8 * K) + (size_t)lane * NW;
-    }
+    if (iu < u1 && ist * 16 + jslot < n16)
+      p = icodes + ((size_t)(iob * 8 + wave) * n16 + (size_t)ist * 16) * (8 * K) + (size_t)lane * NW;
     load_lane_words<K>(p, dst);
+    ++iu;
+    if (++ist == spr) {   // next output block, or the next layer's first
+      ist = 0;
+      ++iob;
+      if (iu == inext) {
+        ++il;
+        iob = 0;
+        icodes = a.L[il].codes;
+        inext = il + 1 < kFusedMaxLayers ? a.L[il + 1].unit0 : INT32_MAX;
+      }
+    }
   };
 #pragma unroll
-  for (int p = 0; p < PF; ++p) issue(u0 + p, buf[p]);
+  for (int p = 0; p < PF; ++p) issue(buf[p]);
 
   fused_transform<CODE, ROUND>(a.x, a.L[lay0].sign_in, nb, nbp, raw0, xx0, xbias0, xfac0);
   if (lay1 != lay0) fused_transform<CODE, ROUND>(a.x, a.L[lay1].sign_in, nb, nbp, raw1, xx1, xbias1, xfac1);
@@ -260,7 +277,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
         else if constexpr (CODE == kCodeMul1) decode_dot_mul1_64<K>(buf[p], nbw, xv, acc);
         else decode_dot_mul1_i8_64<K>(buf[p], nbw, xv, xbias[tile], xfac[tile >> 3], acc);
       }
-      issue(u + PF, buf[p]);     // refill after use; past the run: the dummy line
+      issue(buf[p]);     // refill after use with unit u + PF; past the run: the dummy line
       if (live && u + 1 == seg_end) {
         finish_segment();
         if (u + 1 < u1) {
