@@ -151,31 +151,40 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   // issued in order, so the issue position (layer il, output block iob, step ist) advances by one
   // per issue in registers: no division and no search of the layer table per unit (each was a
   // chain of scalar loads and a division sequence in front of every prefetch).
+  // A run touches lay0 and at most lay1, so both layers' code pointers are read here, once; the
+  // issue pointer itself moves by one step (16 tiles) per issue and is recomputed only at a block
+  // boundary. Issues past the run read the dummy line whatever the position says.
   uint32_t buf[PF][NW];
   const uint32_t* __restrict__ dummy = a.L[lay0].codes;
-  int iu = u0, il = lay0, iob, ist;
+  const uint32_t* __restrict__ codes1 = a.L[lay1].codes;
+  int inext = lay1 != lay0 ? a.L[lay1].unit0 : INT32_MAX;   // where the run enters lay1
+  int iu = u0, iob, ist;
+  const uint32_t* __restrict__ icodes = a.L[lay0].codes;
   {
     const int rel = u0 - a.L[lay0].unit0;
     iob = rel / spr;
     ist = rel - iob * spr;
   }
-  const uint32_t* __restrict__ icodes = a.L[il].codes;
-  int inext = il + 1 < kFusedMaxLayers ? a.L[il + 1].unit0 : INT32_MAX;   // first unit of the next layer
+  constexpr size_t kStepWords = (size_t)16 * 8 * K;         // code words of one 16-tile step of a tile row
+  const uint32_t* __restrict__ ibase = icodes + ((size_t)(iob * 8 + wave) * n16 + (size_t)ist * 16) * (8 * K);
+  const uint32_t lane_bytes = (uint32_t)lane * NW * 4u;
   auto issue = [&](uint32_t(&dst)[NW]) {
-    const uint32_t* p = dummy;
-    if (iu < u1 && ist * 16 + jslot < n16)
-      p = icodes + ((size_t)(iob * 8 + wave) * n16 + (size_t)ist * 16) * (8 * K) + (size_t)lane * NW;
-    load_lane_words<K>(p, dst);
+    // past the run: the dummy line (a uniform choice); a lane past the last tile of a ragged step
+    // reads the step's first tile (its x~ is the zero padding block)
+    const char* base = reinterpret_cast<const char*>(iu < u1 ? ibase : dummy);
+    const uint32_t off = ist * 16 + jslot < n16 ? lane_bytes : 0u;
+    load_lane_words<K>(reinterpret_cast<const uint32_t*>(base + off), dst);
     ++iu;
-    if (++ist == spr) {   // next output block, or the next layer's first
+    ibase += kStepWords;
+    if (++ist == spr) {   // next output block, or the first of lay1
       ist = 0;
       ++iob;
       if (iu == inext) {
-        ++il;
         iob = 0;
-        icodes = a.L[il].codes;
-        inext = il + 1 < kFusedMaxLayers ? a.L[il + 1].unit0 : INT32_MAX;
+        icodes = codes1;
+        inext = INT32_MAX;
       }
+      ibase = icodes + (size_t)(iob * 8 + wave) * n16 * (8 * K);
     }
   };
 #pragma unroll
