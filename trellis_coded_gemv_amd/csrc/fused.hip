@@ -110,10 +110,13 @@ __device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, 
   }
 }
 
-__device__ __forceinline__ int fused_layer_of(const FusedArgs& a, int u) {
+// Layer of unit u: unit0 increases along the table and unused entries hold
+// INT32_MAX, so the layer is the number of later entries starting at or before
+// u (u0 of the table's unit0 column, read beforehand).
+__device__ __forceinline__ int fused_layer_of(const int (&uz)[kFusedMaxLayers], int u) {
   int l = 0;
-  for (int i = 1; i < a.n_layers; ++i)
-    if (u >= a.L[i].unit0) l = i;
+#pragma unroll
+  for (int i = 1; i < kFusedMaxLayers; ++i) l += u >= uz[i] ? 1 : 0;
   return l;
 }
 
@@ -125,12 +128,25 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63, wave = wave_id();   // wave = tile row within the block
   const int jslot = lane >> 2;
+  // The kernel arguments the start needs, the layer table's unit0 column included, are read in
+  // one batch of scalar loads (the empty asm wants them all at once): a search of the table
+  // indexed by the running layer was a chain of dependent loads ahead of the first input load.
+  // The batch also brings every table entry into the scalar cache for the reads below.
+  int uz[kFusedMaxLayers];
+#pragma unroll
+  for (int i = 0; i < kFusedMaxLayers; ++i) uz[i] = a.L[i].unit0;
+  const int upw = a.upw, total_units = a.total_units, n = a.n;
+  const uint16_t* __restrict__ xin = a.x;
+  asm volatile("" ::"s"(upw), "s"(total_units), "s"(n), "s"(xin), "s"(uz[1]), "s"(uz[2]), "s"(uz[3]), "s"(uz[4]),
+               "s"(uz[5]), "s"(uz[6]), "s"(uz[7]));
+  static_assert(kFusedMaxLayers == 8, "the batch above names every entry");
   const int w = blockIdx.x;
-  const int u0 = w * a.upw;
-  const int u1 = u0 + a.upw < a.total_units ? u0 + a.upw : a.total_units;
+  const int u0 = w * upw;
+  const int u1 = u0 + upw < total_units ? u0 + upw : total_units;
   if (u0 >= u1) return;
-  const int nb = a.n >> 7, nbp = (nb + 1) & ~1, n16 = a.n >> 4, spr = nbp >> 1;
-  const int lay0 = fused_layer_of(a, u0), lay1 = fused_layer_of(a, u1 - 1);
+  const int nb = n >> 7, nbp = (nb + 1) & ~1, n16 = n >> 4, spr = nbp >> 1;
+  const int lay0 = fused_layer_of(uz, u0), lay1 = fused_layer_of(uz, u1 - 1);
+  const int unit0_0 = a.L[lay0].unit0, unit0_1 = a.L[lay1].unit0;
   const size_t buf_words = (size_t)nbp * kBlock;                   // one layer's x~ area (fp32 exchange size)
   uint32_t* xx0 = lds;
   uint32_t* xx1 = lds + buf_words;
@@ -143,8 +159,8 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
 
   // Raw inputs of the first transform pass, before the code prefetch (loads complete in order).
   const int xfirst = ((8 * wave + (lane >> 3)) < nb ? (8 * wave + (lane >> 3)) : nb - 1) * kBlock + 16 * (lane & 7);
-  const X16 raw0 = load_x16(a.x, a.L[lay0].sign_in, xfirst);
-  const X16 raw1 = load_x16(a.x, a.L[lay1].sign_in, xfirst);
+  const X16 raw0 = load_x16(xin, a.L[lay0].sign_in, xfirst);
+  const X16 raw1 = load_x16(xin, a.L[lay1].sign_in, xfirst);
   __builtin_amdgcn_sched_barrier(0);
 
   // Code prefetch ring over the run's units; units past the run read a dummy line. Units are
@@ -157,11 +173,11 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   uint32_t buf[PF][NW];
   const uint32_t* __restrict__ dummy = a.L[lay0].codes;
   const uint32_t* __restrict__ codes1 = a.L[lay1].codes;
-  int inext = lay1 != lay0 ? a.L[lay1].unit0 : INT32_MAX;   // where the run enters lay1
+  int inext = lay1 != lay0 ? unit0_1 : INT32_MAX;   // where the run enters lay1
   int iu = u0, iob, ist;
   const uint32_t* __restrict__ icodes = a.L[lay0].codes;
   {
-    const int rel = u0 - a.L[lay0].unit0;
+    const int rel = u0 - unit0_0;
     iob = rel / spr;
     ist = rel - iob * spr;
   }
@@ -190,8 +206,8 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(buf[p]);
 
-  fused_transform<CODE, ROUND>(a.x, a.L[lay0].sign_in, nb, nbp, raw0, xx0, xbias0, xfac0);
-  if (lay1 != lay0) fused_transform<CODE, ROUND>(a.x, a.L[lay1].sign_in, nb, nbp, raw1, xx1, xbias1, xfac1);
+  fused_transform<CODE, ROUND>(xin, a.L[lay0].sign_in, nb, nbp, raw0, xx0, xbias0, xfac0);
+  if (lay1 != lay0) fused_transform<CODE, ROUND>(xin, a.L[lay1].sign_in, nb, nbp, raw1, xx1, xbias1, xfac1);
 
   const CodeRegs cr;
   // The current block segment: layer l, output block ob, units [seg_u0, seg_end).
@@ -200,15 +216,16 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   const int32_t* xbias = xbias0;
   const float* xfac = xfac0;
   auto start_segment = [&](int u) {
-    l = fused_layer_of(a, u);
-    ob = (u - a.L[l].unit0) / spr;
-    seg_u0 = a.L[l].unit0 + ob * spr;
+    l = u >= unit0_1 ? lay1 : lay0;   // the run enters lay1 at its first unit
+    const int lu0 = l == lay0 ? unit0_0 : unit0_1;
+    ob = (u - lu0) / spr;
+    seg_u0 = lu0 + ob * spr;
     const int e = seg_u0 + spr;
     seg_end = e < u1 ? e : u1;
     xx = l == lay0 ? xx0 : xx1;
     xbias = l == lay0 ? xbias0 : xbias1;
     xfac = l == lay0 ? xfac0 : xfac1;
-    count = (seg_u0 + spr - 1) / a.upw - seg_u0 / a.upw + 1;       // workgroups contributing to the block
+    count = (seg_u0 + spr - 1) / upw - seg_u0 / upw + 1;       // workgroups contributing to the block
   };
   start_segment(u0);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -219,7 +236,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
     const FusedLayer& Ld = a.L[l];
     const float d = reduce_slots(acc, lane);
     const int orow = wave * 16 + reduced_row(lane);
-    const int first_wg = seg_u0 / a.upw;
+    const int first_wg = seg_u0 / upw;
     __syncthreads();                                                   // ybuf is free (previous segment done)
     if (lane < 16) ybuf[orow] = d;
     if (count == 1) {

@@ -67,8 +67,9 @@ __device__ __forceinline__ void gemv_workgroup(const GemvArgs& a, int ob, int sp
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int rw = wave & 7, kp = wave >> 3;     // tile row within the block, step phase
   const int nb128 = a.n >> 7;
-  const int blk0 = (int)((int64_t)split * nb128 / a.splits);
-  const int blk1 = (int)((int64_t)(split + 1) * nb128 / a.splits);
+  // n <= 2^22, so split * nb128 <= 2^30 and 32-bit division suffices
+  const int blk0 = split * nb128 / a.splits;
+  const int blk1 = (split + 1) * nb128 / a.splits;
   const int cb = blk1 - blk0;             // 128-blocks in this chunk
   const int ntiles = cb * 8;              // tiles of the chunk in one tile row
   const int nsteps = (cb + 1) >> 1;       // 16 tiles per step
@@ -331,6 +332,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 template <int K, int CODE, bool ROUND, int PF, int P>
 __global__ __launch_bounds__(64 * 8 * P) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t lds[];
+  // Every argument the kernel reads goes out in one batch of scalar loads (the empty asm wants
+  // them all here); loaded where first used, the pointers came a round trip after the sizes,
+  // ahead of the input load.
+  asm volatile("" ::"s"(a.codes), "s"(a.scales), "s"(a.sign_in), "s"(a.sign_out), "s"(a.x), "s"(a.y), "s"(a.slots),
+               "s"(a.counters), "s"(a.status), "s"(a.m), "s"(a.n), "s"(a.splits));
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int ob = bid / a.splits;
   gemv_workgroup<K, CODE, ROUND, PF, P>(a, ob, bid - ob * a.splits, lds);
