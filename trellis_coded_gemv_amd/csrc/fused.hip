@@ -260,25 +260,46 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
     const uint32_t tag = flag[1];
     if (lane < 16) put_slot(slots + (size_t)me * kBlock + orow, d, tag);
     if (flag[0] == 0u || wave != 0) return;
-    // the last contributor: every other one has published; sum in contributor order
+    // The last contributor: every other one has published. Up to J contributors' slots are read
+    // together (one memory round trip, not one per contributor), the ones not yet holding this
+    // call's partial re-read together until all do (bounded), and the partials summed in
+    // contributor order.
+    constexpr int J = 4;
     float v0 = 0.f, v1 = 0.f;
     bool late = false;
-    for (int i = 0; i < count; ++i) {
-      if (i == me) {
-        v0 += ybuf[lane];
-        v1 += ybuf[lane + 64];
-        continue;
+    for (int i0 = 0; i0 < count; i0 += J) {
+      uint64_t s0[J], s1[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int i = i0 + j;
+        s0[j] = s1[j] = (uint64_t)tag << 32;   // contributors past the count, and this one, count as ready
+        if (i < count && i != me) {
+          s0[j] = peek_slot(slots + (size_t)i * kBlock + lane);
+          s1[j] = peek_slot(slots + (size_t)i * kBlock + lane + 64);
+        }
       }
-      uint64_t s0 = peek_slot(slots + (size_t)i * kBlock + lane);
-      uint64_t s1 = peek_slot(slots + (size_t)i * kBlock + lane + 64);
-      for (uint32_t it = 0; it < kSlotPolls && (!slot_ready(s0, tag) || !slot_ready(s1, tag)); ++it) {
+      bool empty = true;
+      for (uint32_t it = 0; it < kSlotPolls; ++it) {
+        empty = false;
+#pragma unroll
+        for (int j = 0; j < J; ++j) empty |= !slot_ready(s0[j], tag) || !slot_ready(s1[j], tag);
+        if (!empty) break;
         __builtin_amdgcn_s_sleep(1);
-        if (!slot_ready(s0, tag)) s0 = peek_slot(slots + (size_t)i * kBlock + lane);
-        if (!slot_ready(s1, tag)) s1 = peek_slot(slots + (size_t)i * kBlock + lane + 64);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int i = i0 + j;
+          if (!slot_ready(s0[j], tag)) s0[j] = peek_slot(slots + (size_t)i * kBlock + lane);
+          if (!slot_ready(s1[j], tag)) s1[j] = peek_slot(slots + (size_t)i * kBlock + lane + 64);
+        }
       }
-      late |= !slot_ready(s0, tag) || !slot_ready(s1, tag);
-      v0 += slot_value(s0, tag);
-      v1 += slot_value(s1, tag);
+      late |= empty;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int i = i0 + j;
+        if (i >= count) break;
+        v0 += i == me ? ybuf[lane] : slot_value(s0[j], tag);
+        v1 += i == me ? ybuf[lane + 64] : slot_value(s1[j], tag);
+      }
     }
     if (late) report_status(a.status, kStatusSplitkTimeout);
     rht_out_block(v0, v1, Ld.scales, Ld.sign_out, Ld.y, ob * kBlock, lane);
