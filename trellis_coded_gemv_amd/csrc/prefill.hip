@@ -8,6 +8,8 @@
 //   rows_rht_kernel      X~ = H diag(s_in) X / sqrt(128), fp16, in 32-column slabs
 //   prefill_mfma_kernel  Y = diag(s_out) H (g * (X~ W^T)) / sqrt(128): decode into
 //                        LDS, v_mfma_f32_16x16x32_f16, output transform in the epilogue
+#include <type_traits>
+
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
@@ -141,11 +143,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_mfma_kernel(const uint3
   }
   const uint32_t slab = (uint32_t)M * 32u;   // halves per 32-column slab
 
-  uint32_t cw[NRAW];
-  auto load = [&](int c, uint32_t(&wd)[NRAW], u32x4(&xa)[4]) {
+  auto load_codes = [&](int c, uint32_t(&wd)[NRAW]) {
     const uint32_t* t = tp + (size_t)c * 2 * WPT;
 #pragma unroll
     for (int i = 0; i < NRAW; ++i) wd[i] = t[widx[i]];
+  };
+  auto load_a = [&](int c, u32x4(&xa)[4]) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) xa[a] = *reinterpret_cast<const u32x4*>(Xt + (aoff[a] + (uint32_t)c * slab));
   };
@@ -157,21 +160,35 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_mfma_kernel(const uint3
     for (int t = 0; t < 8; ++t) acc[a][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   const CodeRegs cr;
-  u32x4 av[4], avn[4];
-  load(0, cw, av);
-  bsh[0][wave][lane] = pf_decode<K, CODE>(cw, shift, cr);
-  load(nchunks > 1 ? 1 : 0, cw, avn);
+  // Operands in flight in two register sets used alternately: the A operands of chunk c in
+  // set c % 2 (loaded two chunks ahead), the code words of chunk c in set c % 2 (loaded three
+  // chunks ahead, decoded one chunk ahead into LDS). The loop runs two chunks per trip, so the
+  // sets never rotate through copies. (Rotating a single pair, av = next, compiled to register
+  // copies after the next loads, and so to a wait, once per chunk, for loads just issued.)
+  const int last = nchunks - 1;
+  uint32_t cw0[NRAW], cw1[NRAW];
+  u32x4 av0[4], av1[4];
+  load_codes(0, cw0);
+  load_a(0, av0);
+  load_codes(last < 1 ? last : 1, cw1);
+  load_a(last < 1 ? last : 1, av1);
+  bsh[0][wave][lane] = pf_decode<K, CODE>(cw0, shift, cr);
+  load_codes(last < 2 ? last : 2, cw0);
   __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
+  // One chunk: B operands of chunk c from LDS, the next chunk's B decoded from its code words
+  // while the matrix cores run (waves with activation rows; the others only decode), then the
+  // loads of chunk c + 3's code words and chunk c + 2's A operands into the sets just used. No
+  // branch inside: the chunk count is even (n is a multiple of 128) and the store of a B past
+  // the last chunk goes to the buffer no wave reads any more.
+  auto chunk = [&](int c, u32x4(&av)[4], uint32_t(&cwn)[NRAW], auto mm) {
     u32x4 bo[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) bo[t] = bsh[c & 1][t][lane];
-    // The next chunk's B operand is decoded in the same block as this chunk's
-    // MFMAs, interleaved with them (one MFMA, then two VALU instructions), so
-    // the decode runs while the matrix core works.
-    u32x4 nb;
-    if (rows) {
-      nb = pf_decode<K, CODE>(cw, shift, cr);
+    const u32x4 nb = pf_decode<K, CODE>(cwn, shift, cr);
+    if constexpr (decltype(mm)::value) {
+      // The next chunk's B operand is decoded in the same block as this chunk's
+      // MFMAs, interleaved with them (one MFMA, then two VALU instructions), so
+      // the decode runs while the matrix core works.
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -183,14 +200,22 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_mfma_kernel(const uint3
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
       }
-    } else {
-      nb = pf_decode<K, CODE>(cw, shift, cr);
     }
-    if (c + 1 < nchunks) bsh[(c + 1) & 1][wave][lane] = nb;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) av[a] = avn[a];
-    load(c + 2 < nchunks ? c + 2 : nchunks - 1, cw, avn);
+    bsh[(c + 1) & 1][wave][lane] = nb;
+    load_codes(c + 3 < last ? c + 3 : last, cwn);
+    load_a(c + 2 < last ? c + 2 : last, av);
     __syncthreads();
+  };
+  if (rows) {
+    for (int c = 0; c < nchunks; c += 2) {
+      chunk(c, av0, cw1, std::true_type{});
+      chunk(c + 1, av1, cw0, std::true_type{});
+    }
+  } else {
+    for (int c = 0; c < nchunks; c += 2) {
+      chunk(c, av0, cw1, std::false_type{});
+      chunk(c + 1, av1, cw0, std::false_type{});
+    }
   }
 
   // acc[a][t][v] = Y~[row0 + 16a + 4g + v][128 ob + 16t + j]. The output side
