@@ -201,8 +201,8 @@ def test_trellis_linear_dispatch():
     from trellis_coded_gemv_amd.binding import TrellisLinear
     assert TrellisLinear.path_for_rows(1) == "gemv"
     assert TrellisLinear.path_for_rows(2) == "small" and TrellisLinear.path_for_rows(64) == "small"
-    assert TrellisLinear.path_for_rows(65) == "small_chunked" and TrellisLinear.path_for_rows(191) == "small_chunked"
-    assert TrellisLinear.path_for_rows(192) == "prefill" and TrellisLinear.path_for_rows(4096) == "prefill"
+    assert TrellisLinear.path_for_rows(65) == "small_chunked" and TrellisLinear.path_for_rows(127) == "small_chunked"
+    assert TrellisLinear.path_for_rows(128) == "prefill" and TrellisLinear.path_for_rows(4096) == "prefill"
     assert TrellisLinear.path_for_rows(100, prefill_min_rows=65) == "prefill"
     with pytest.raises(ValueError):
         TrellisLinear.path_for_rows(0)

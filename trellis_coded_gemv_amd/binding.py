@@ -398,21 +398,21 @@ class TrellisLinear:
       R <= 64                -> trellis_gemm_small
       R <  prefill_min_rows  -> trellis_gemm_small on row chunks of 64
       otherwise              -> trellis_gemm_prefill (decode once per 512 rows into MFMA operands)
-    The default threshold (192 rows) sits past the measured crossover of the last two on
-    the 8192 -> 28672 gate shape. Workspaces are allocated on first use of each path and kept
+    The default threshold (128 rows) sits at the measured crossover of the last two on the
+    8192 -> 28672 gate shape (96 rows: chunked small batch faster; 128: prefill faster). Workspaces are allocated on first use of each path and kept
     (the prefill one grows with the largest row count seen); calls are ordered on one stream.
     """
 
     SMALL_MAX_ROWS = 64
 
-    def __init__(self, layer: DeviceLayer, prefill_min_rows: int = 192):
+    def __init__(self, layer: DeviceLayer, prefill_min_rows: int = 128):
         self.layer = layer
         self.prefill_min_rows = int(prefill_min_rows)
         self._ws = None
         self._prefill_ws, self._prefill_rows = None, 0
 
     @classmethod
-    def path_for_rows(cls, rows: int, prefill_min_rows: int = 192) -> str:
+    def path_for_rows(cls, rows: int, prefill_min_rows: int = 128) -> str:
         if rows < 1:
             raise ValueError("no rows")
         if rows == 1:
