@@ -77,3 +77,49 @@ def test_random_tables_and_forced_counts():
         n = 128 * int(rng.integers(1, 129))
         ms = [128 * int(rng.integers(1, 65)) for _ in range(int(rng.integers(1, 9)))]
         replay(ms, n, target=int(rng.integers(1, 700)))
+
+
+def issue_replay(ms, n, K, target=None, pf=2):
+    """The fused kernel's code prefetch, replayed: the issue position (output block, step) advances
+    by one unit per issue with a block wrap and one switch of code pointer where the run enters its
+    second layer, and every issue inside the run must address the code words the unit's own
+    (layer, block, step) names, for every tile row (wave) of the block."""
+    spr, unit0, total, upw, grid, _ = geometry(ms, n, target)
+    n16 = n // 16
+    step_words = 16 * 8 * K
+    layer_of = lambda u: int(np.searchsorted(unit0, u, side="right") - 1)
+    for w in range(grid):
+        u0, u1 = w * upw, min((w + 1) * upw, total)
+        lay0, lay1 = layer_of(u0), layer_of(u1 - 1)
+        for wave in range(8):
+            inext = unit0[lay1] if lay1 != lay0 else 1 << 62
+            iu, icodes = u0, lay0
+            rel = u0 - unit0[lay0]
+            iob, ist = rel // spr, rel % spr
+            ibase = ((iob * 8 + wave) * n16 + ist * 16) * (8 * K)
+            for _ in range(u1 - u0 + pf):
+                if iu < u1:
+                    l = layer_of(iu)
+                    r = iu - unit0[l]
+                    want = (l, ((r // spr * 8 + wave) * n16 + (r % spr) * 16) * (8 * K))
+                    assert (icodes, ibase) == want, (ms, n, K, w, wave, iu)
+                    assert ist == r % spr                     # the ragged-step test uses ist
+                iu += 1
+                ibase += step_words
+                ist += 1
+                if ist == spr:
+                    ist = 0
+                    iob += 1
+                    if iu == inext:
+                        iob, icodes, inext = 0, lay1, 1 << 62
+                    ibase = (iob * 8 + wave) * n16 * (8 * K)
+
+
+def test_prefetch_position_replay():
+    issue_replay([8192, 1024, 1024], 8192, 2)
+    issue_replay([28672, 28672], 8192, 2)
+    rng = np.random.default_rng(5)
+    for _ in range(60):
+        n = 128 * int(rng.integers(1, 40))
+        ms = [128 * int(rng.integers(1, 12)) for _ in range(int(rng.integers(1, 5)))]
+        issue_replay(ms, n, int(rng.integers(1, 9)), target=int(rng.integers(1, 300)))
