@@ -123,3 +123,37 @@ def test_prefetch_position_replay():
         n = 128 * int(rng.integers(1, 40))
         ms = [128 * int(rng.integers(1, 12)) for _ in range(int(rng.integers(1, 5)))]
         issue_replay(ms, n, int(rng.integers(1, 9)), target=int(rng.integers(1, 300)))
+
+
+def needed_blocks_replay(ms, n, target=None):
+    """The fused kernel transforms only the input blocks its run reads: in its first layer the
+    nn0 blocks from 2 * (first unit's step) on, in the second the nn1 blocks from 0 on (modulo
+    the padded block count). Every block a unit of the run reads (two per step) must be among
+    them."""
+    spr, unit0, total, upw, grid, _ = geometry(ms, n, target)
+    nbp = 2 * spr
+    layer_of = lambda u: int(np.searchsorted(unit0, u, side="right") - 1)
+    for w in range(grid):
+        u0, u1 = w * upw, min((w + 1) * upw, total)
+        lay0, lay1 = layer_of(u0), layer_of(u1 - 1)
+        end0 = unit0[lay1] if lay1 != lay0 else u1
+        step0 = (u0 - unit0[lay0]) % spr
+        nn0 = min(nbp, 2 * (end0 - u0))
+        nn1 = min(nbp, 2 * (u1 - unit0[lay1]))
+        done = {lay0: {(2 * step0 + i) % nbp for i in range(nn0)}}
+        if lay1 != lay0:
+            done[lay1] = {i % nbp for i in range(nn1)}
+        for u in range(u0, u1):
+            l = layer_of(u)
+            s = (u - unit0[l]) % spr
+            assert {2 * s, 2 * s + 1} <= done[l], (ms, n, w, u)
+
+
+def test_needed_input_blocks():
+    needed_blocks_replay([8192, 1024, 1024], 8192)
+    needed_blocks_replay([28672, 28672], 8192)
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        n = 128 * int(rng.integers(1, 129))
+        ms = [128 * int(rng.integers(1, 65)) for _ in range(int(rng.integers(1, 9)))]
+        needed_blocks_replay(ms, n, target=int(rng.integers(1, 700)))

@@ -31,23 +31,36 @@ namespace tg {
 #define TG_FUSED_PF 2
 #endif
 
-// Input transform of one layer's x~ into LDS: blocks [0, nbp) (the padding
-// block of an odd block count is zero), 8 lanes per block, 64 blocks per pass
-// of the workgroup's 512 threads. `raw` holds this lane's raw inputs of the
-// first pass (loaded early by the caller); later passes load their own.
+// Input transform of one layer's x~ into LDS: the nn blocks fb, fb + 1, ... (modulo
+// nbp) that the workgroup's units of this layer read -- two per 16-tile step -- of
+// the nbp blocks (the padding block of an odd block count is zero), 8 lanes per
+// block, 64 blocks per pass of the workgroup's 512 threads. `raw` holds this
+// lane's raw inputs of the first pass (loaded early by the caller); later passes
+// load their own. Transforming only those blocks leaves the other waves idle and
+// the SIMDs to the ones that work (a short run reads 20 of 64 blocks).
 // The int8 form (mul1 with int8 activations) also writes each tile column's
 // bias (xbias) and each block's factor (xfac).
+// Block of the idx-th of the nn needed ones: fb + idx modulo nbp (fb < nbp, nn <= nbp); a
+// thread past them (idx >= nn, it writes nothing) takes block fb, so every address it forms
+// stays inside the layer's area.
+__device__ __forceinline__ int fused_block(int fb, int idx, int nn, int nbp) {
+  const int b = fb + (idx < nn ? idx : 0);
+  return b >= nbp ? b - nbp : b;
+}
+
 template <int CODE, bool ROUND>
 __device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
-                                                int nb, int nbp, X16 raw, uint32_t* xx, int32_t* xbias, float* xfac) {
+                                                int nb, int nbp, int fb, int nn, X16 raw, uint32_t* xx, int32_t* xbias,
+                                                float* xfac) {
   constexpr int XB = (CODE == 1 ? 8 : 16) * 8;   // input words per 128-block
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int xs = lane & 7;
-  for (int pass = 0; pass * 64 < nbp; ++pass) {
-    const int xb = pass * 64 + 8 * wave + (lane >> 3);
+  for (int pass = 0; pass * 64 < nn; ++pass) {
+    const int idx = pass * 64 + 8 * wave + (lane >> 3);
+    const int xb = fused_block(fb, idx, nn, nbp);
     const int first = (xb < nb ? xb : nb - 1) * kBlock + 16 * xs;
     if (pass > 0) raw = load_x16(x, sign_in, first);
-    const bool active = xb < nbp, live = xb < nb;
+    const bool active = idx < nn, live = xb < nb;
     if constexpr (CODE == kCodeMul1I8) {
       int32_t qe[8], qo[8];
       int e;
@@ -157,10 +170,16 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   float* xfac0 = reinterpret_cast<float*>(xbias1 + nbp * 8);       // int8 form: [nbp] per layer
   float* xfac1 = xfac0 + nbp;
 
+  // The input blocks the run reads: in lay0 from the step of its first unit on, one step per
+  // unit (wrapping into the next output block), in lay1 from step 0 on.
+  const int end0 = lay1 != lay0 ? unit0_1 : u1;
+  const int step0 = (u0 - unit0_0) % spr;
+  const int fb0 = 2 * step0, nn0 = 2 * (end0 - u0) < nbp ? 2 * (end0 - u0) : nbp;
+  const int nn1 = 2 * (u1 - unit0_1) < nbp ? 2 * (u1 - unit0_1) : nbp;
   // Raw inputs of the first transform pass, before the code prefetch (loads complete in order).
-  const int xfirst = ((8 * wave + (lane >> 3)) < nb ? (8 * wave + (lane >> 3)) : nb - 1) * kBlock + 16 * (lane & 7);
-  const X16 raw0 = load_x16(xin, a.L[lay0].sign_in, xfirst);
-  const X16 raw1 = load_x16(xin, a.L[lay1].sign_in, xfirst);
+  const int xb0 = fused_block(fb0, 8 * wave + (lane >> 3), nn0, nbp), xb1 = fused_block(0, 8 * wave + (lane >> 3), nn1, nbp);
+  const X16 raw0 = load_x16(xin, a.L[lay0].sign_in, (xb0 < nb ? xb0 : nb - 1) * kBlock + 16 * (lane & 7));
+  const X16 raw1 = load_x16(xin, a.L[lay1].sign_in, (xb1 < nb ? xb1 : nb - 1) * kBlock + 16 * (lane & 7));
   __builtin_amdgcn_sched_barrier(0);
 
   // Code prefetch ring over the run's units; units past the run read a dummy line. Units are
@@ -206,8 +225,9 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(buf[p]);
 
-  fused_transform<CODE, ROUND>(xin, a.L[lay0].sign_in, nb, nbp, raw0, xx0, xbias0, xfac0);
-  if (lay1 != lay0) fused_transform<CODE, ROUND>(xin, a.L[lay1].sign_in, nb, nbp, raw1, xx1, xbias1, xfac1);
+  fused_transform<CODE, ROUND>(xin, a.L[lay0].sign_in, nb, nbp, fb0, nn0, raw0, xx0, xbias0, xfac0);
+  if (lay1 != lay0)
+    fused_transform<CODE, ROUND>(xin, a.L[lay1].sign_in, nb, nbp, 0, nn1, raw1, xx1, xbias1, xfac1);
 
   const CodeRegs cr;
   // The current block segment: layer l, output block ob, units [seg_u0, seg_end).
