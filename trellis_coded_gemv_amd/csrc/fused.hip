@@ -31,15 +31,26 @@ namespace tg {
 #define TG_FUSED_PF 2
 #endif
 
-// Input transform of one layer's x~ into LDS: the nn blocks fb, fb + 1, ... (modulo
-// nbp) that the workgroup's units of this layer read -- two per 16-tile step -- of
-// the nbp blocks (the padding block of an odd block count is zero), 8 lanes per
-// block, 64 blocks per pass of the workgroup's 512 threads. `raw` holds this
-// lane's raw inputs of the first pass (loaded early by the caller); later passes
-// load their own. Transforming only those blocks leaves the other waves idle and
-// the SIMDs to the ones that work (a short run reads 20 of 64 blocks).
+// Input transform of the run's x~ into LDS: for each layer the run touches (one or
+// two, each with its own input signs and LDS area), the nn blocks fb, fb + 1, ...
+// (modulo nbp) that the run's units of that layer read -- two per 16-tile step --
+// of the nbp blocks (the padding block of an odd block count is zero). Both
+// layers' blocks are taken in one sequence, 8 lanes per block, 64 blocks per pass
+// of the workgroup's 512 threads: a run that crosses a layer boundary transforms
+// both in the time of one. `raw` holds this lane's raw inputs of the first pass
+// (loaded early by the caller); later passes load their own. Transforming only
+// the blocks read leaves the other waves idle and the SIMDs to the ones that work
+// (a short run reads 20 of 64 blocks).
 // The int8 form (mul1 with int8 activations) also writes each tile column's
 // bias (xbias) and each block's factor (xfac).
+struct TransformPart {
+  const uint32_t* sign_in;
+  uint32_t* xx;
+  int32_t* xbias;
+  float* xfac;
+  int fb, nn;
+};
+
 // Block of the idx-th of the nn needed ones: fb + idx modulo nbp (fb < nbp, nn <= nbp); a
 // thread past them (idx >= nn, it writes nothing) takes block fb, so every address it forms
 // stays inside the layer's area.
@@ -48,19 +59,31 @@ __device__ __forceinline__ int fused_block(int fb, int idx, int nn, int nbp) {
   return b >= nbp ? b - nbp : b;
 }
 
+// The layer part and block of sequence position idx (parts p0 then p1), and the first
+// input element of this lane's 16 (clamped to the last block for the padding block).
+__device__ __forceinline__ void fused_slot(const TransformPart& p0, const TransformPart& p1, int idx, int nb,
+                                           int nbp, bool& second, int& xb, int& first) {
+  second = idx >= p0.nn;
+  xb = second ? fused_block(p1.fb, idx - p0.nn, p1.nn, nbp) : fused_block(p0.fb, idx, p0.nn, nbp);
+  first = (xb < nb ? xb : nb - 1) * kBlock + 16 * (threadIdx.x & 7);
+}
+
 template <int CODE, bool ROUND>
-__device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, const uint32_t* __restrict__ sign_in,
-                                                int nb, int nbp, int fb, int nn, X16 raw, uint32_t* xx, int32_t* xbias,
-                                                float* xfac) {
+__device__ __forceinline__ void fused_transform(const uint16_t* __restrict__ x, int nb, int nbp,
+                                                const TransformPart& p0, const TransformPart& p1, int total, X16 raw) {
   constexpr int XB = (CODE == 1 ? 8 : 16) * 8;   // input words per 128-block
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int xs = lane & 7;
-  for (int pass = 0; pass * 64 < nn; ++pass) {
+  for (int pass = 0; pass * 64 < total; ++pass) {
     const int idx = pass * 64 + 8 * wave + (lane >> 3);
-    const int xb = fused_block(fb, idx, nn, nbp);
-    const int first = (xb < nb ? xb : nb - 1) * kBlock + 16 * xs;
-    if (pass > 0) raw = load_x16(x, sign_in, first);
-    const bool active = idx < nn, live = xb < nb;
+    bool second;
+    int xb, first;
+    fused_slot(p0, p1, idx, nb, nbp, second, xb, first);
+    uint32_t* xx = second ? p1.xx : p0.xx;
+    int32_t* xbias = second ? p1.xbias : p0.xbias;
+    float* xfac = second ? p1.xfac : p0.xfac;
+    if (pass > 0) raw = load_x16(x, second ? p1.sign_in : p0.sign_in, first);
+    const bool active = idx < total, live = xb < nb;
     if constexpr (CODE == kCodeMul1I8) {
       int32_t qe[8], qo[8];
       int e;
@@ -176,10 +199,17 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
   const int step0 = (u0 - unit0_0) % spr;
   const int fb0 = 2 * step0, nn0 = 2 * (end0 - u0) < nbp ? 2 * (end0 - u0) : nbp;
   const int nn1 = 2 * (u1 - unit0_1) < nbp ? 2 * (u1 - unit0_1) : nbp;
+  const TransformPart tp0{a.L[lay0].sign_in, xx0, xbias0, xfac0, fb0, nn0};
+  const TransformPart tp1{a.L[lay1].sign_in, xx1, xbias1, xfac1, 0, nn1};
+  const int ttotal = nn0 + (lay1 != lay0 ? nn1 : 0);
   // Raw inputs of the first transform pass, before the code prefetch (loads complete in order).
-  const int xb0 = fused_block(fb0, 8 * wave + (lane >> 3), nn0, nbp), xb1 = fused_block(0, 8 * wave + (lane >> 3), nn1, nbp);
-  const X16 raw0 = load_x16(xin, a.L[lay0].sign_in, (xb0 < nb ? xb0 : nb - 1) * kBlock + 16 * (lane & 7));
-  const X16 raw1 = load_x16(xin, a.L[lay1].sign_in, (xb1 < nb ? xb1 : nb - 1) * kBlock + 16 * (lane & 7));
+  X16 raw;
+  {
+    bool second;
+    int xb, first;
+    fused_slot(tp0, tp1, 8 * wave + (lane >> 3), nb, nbp, second, xb, first);
+    raw = load_x16(xin, second ? tp1.sign_in : tp0.sign_in, first);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // Code prefetch ring over the run's units; units past the run read a dummy line. Units are
@@ -225,9 +255,7 @@ __global__ __launch_bounds__(512) void fused_kernel(FusedArgs a) {
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(buf[p]);
 
-  fused_transform<CODE, ROUND>(xin, a.L[lay0].sign_in, nb, nbp, fb0, nn0, raw0, xx0, xbias0, xfac0);
-  if (lay1 != lay0)
-    fused_transform<CODE, ROUND>(xin, a.L[lay1].sign_in, nb, nbp, 0, nn1, raw1, xx1, xbias1, xfac1);
+  fused_transform<CODE, ROUND>(xin, nb, nbp, tp0, tp1, ttotal, raw);
 
   const CodeRegs cr;
   // The current block segment: layer l, output block ob, units [seg_u0, seg_end).
