@@ -63,8 +63,8 @@ int32_t check_layer(const tg_layer* L) {
 }
 
 // Number of input chunks (split-K) for a batch-1 GEMV. About 256 workgroups
-// (one 128-output block x one chunk each) measured best on 256 CUs for every
-// workload shape; chunks are kept equal and a whole number of 16-tile steps
+// (one 128-output block x one chunk each) measured best on 256 CUs for most
+// shapes, 1024 for long inputs (below); chunks are kept equal and a whole number of 16-tile steps
 // (two 128-blocks), since a half step costs the decode work of a full one.
 // The chunk also has to fit the LDS budget. A layer's `splits` field, when
 // positive, forces the count (a tuning aid; still clamped to what fits).
@@ -85,9 +85,13 @@ int gemv_splits(int m, int n, int forced) {
   int s = forced;
   if (s <= 0) {
     // chunks of a single step lose to two-step chunks: the split-K handoff
-    // costs more than the extra parallelism gains (1024 x 8192: 8.9 vs 7.3 us)
+    // costs more than the extra parallelism gains (1024 x 8192: 8.9 vs 7.3 us).
+    // A long input (192 blocks or more) aims at 1024 workgroups instead: four
+    // per compute unit hide the code loads better than one, and its chunks
+    // stay long (8192 x 28672: 16 chunks of 7 steps, 0.5 us faster per call)
     const int max_s = nb / 4 > 1 ? nb / 4 : 1;
-    const int target = (256 + ob / 2) / ob;
+    const int wgs = nb >= 192 ? 1024 : 256;
+    const int target = (wgs + ob / 2) / ob;
     s = split_for_target(nb, target < max_s ? target : max_s);
   }
   const int cap = kSlotPairs / ob;               // (block, split) pairs the slot area holds
